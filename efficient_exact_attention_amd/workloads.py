@@ -1,0 +1,159 @@
+"""Seeded synthetic workloads shared by the tests, the bench and the oracle checks.
+
+This module only draws and rounds numbers; it holds none of the attention
+arithmetic. Both the HIP path and the CPU oracle take their inputs from here.
+
+Recipe (stated once, used everywhere):
+  * Each of Q, K, V is drawn head by head. Stream ``t*B*H + b*H + h`` of
+    ``numpy.random.SeedSequence(seed).spawn(3*B*H)`` (t = 0, 1, 2 for Q, K, V)
+    feeds ``default_rng(...).standard_normal((N, d), float32)``, multiplied by
+    ``sigma``. Any one head can therefore be regenerated on its own.
+  * For bf16 workloads every value is rounded once to bf16 with
+    round-to-nearest-even; the same 16-bit patterns go to the GPU and, upcast
+    exactly, to the oracle.
+
+The shapes and mask arguments are the five workloads of the exact-attention
+pages (causal, Mistral-style sliding window, long-context causal,
+Longformer/BigBird-style local+global) plus the causal N=32768 d=128 shape the
+throughput target is quoted on.
+"""
+from __future__ import annotations
+
+import os
+from concurrent.futures import ThreadPoolExecutor
+from dataclasses import dataclass, field
+
+import numpy as np
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    N: int
+    d: int
+    dtype: str          # "bf16" or "f32"
+    sigma: float
+    causal: int
+    win_left: int
+    win_right: int
+    global_idx: tuple = field(default_factory=tuple)
+    seed: int = 0
+    desc: str = ""
+
+    @property
+    def n_global(self) -> int:
+        return len(self.global_idx)
+
+    def mask_args(self) -> dict:
+        return dict(causal=self.causal, win_left=self.win_left,
+                    win_right=self.win_right, global_idx=tuple(self.global_idx))
+
+    def with_(self, **kw) -> "Workload":
+        d = dict(self.__dict__)
+        d.update(kw)
+        return Workload(**d)
+
+
+def every_2048th(N: int) -> tuple:
+    """Global tokens {0, 1} plus every multiple of 2048 below N (0 listed once)."""
+    return tuple(sorted({0, 1} | set(range(0, N, 2048))))
+
+
+WORKLOADS = {
+    "c1": Workload("c1", 1, 1, 256, 64, "f32", 1.0, 1, -1, -1, (), 101,
+                   "single-head causal, fp32 inputs"),
+    "c2": Workload("c2", 4, 32, 4096, 128, "bf16", 1.0, 1, -1, -1, (), 102,
+                   "full causal"),
+    "c3": Workload("c3", 1, 32, 32768, 128, "bf16", 1.0, 1, 4095, 0, (), 103,
+                   "sliding-window causal, w=4096 (row i sees i-4095..i)"),
+    "c4": Workload("c4", 1, 8, 131072, 128, "bf16", 0.5, 1, -1, -1, (), 104,
+                   "long-context causal, sigma 0.5"),
+    "c5": Workload("c5", 2, 12, 16384, 64, "bf16", 1.0, 0, 256, 256,
+                   every_2048th(16384), 105,
+                   "non-causal band +-256 plus 9 global tokens"),
+    "tgt": Workload("tgt", 1, 32, 32768, 128, "bf16", 1.0, 1, -1, -1, (), 106,
+                    "full causal, throughput target shape"),
+}
+
+
+def round_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bf16 bit patterns (uint16), round to nearest, ties to even."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    r = (u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)
+    return r.astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def _streams(seed: int, B: int, H: int):
+    return np.random.SeedSequence(seed).spawn(3 * B * H)
+
+
+def head_values(w: Workload, t: int, b: int, h: int, streams=None) -> np.ndarray:
+    """One head of tensor t (0=Q, 1=K, 2=V) as float32 values exactly as the
+    GPU sees them (already rounded to bf16 for bf16 workloads)."""
+    ss = (streams or _streams(w.seed, w.B, w.H))[t * w.B * w.H + b * w.H + h]
+    x = np.random.default_rng(ss).standard_normal((w.N, w.d), dtype=np.float32)
+    if w.sigma != 1.0:
+        x *= np.float32(w.sigma)
+    if w.dtype == "bf16":
+        x = bf16_bits_to_f32(round_to_bf16_bits(x))
+    return x
+
+
+def make_tensor(w: Workload, t: int, threads: int | None = None) -> np.ndarray:
+    """Full [B][H][N][d] tensor t. bf16 workloads return uint16 bit patterns,
+    f32 workloads return float32."""
+    streams = _streams(w.seed, w.B, w.H)
+    dt = np.uint16 if w.dtype == "bf16" else np.float32
+    out = np.empty((w.B, w.H, w.N, w.d), dtype=dt)
+
+    def fill(bh):
+        b, h = divmod(bh, w.H)
+        x = np.random.default_rng(streams[t * w.B * w.H + bh]).standard_normal(
+            (w.N, w.d), dtype=np.float32)
+        if w.sigma != 1.0:
+            x *= np.float32(w.sigma)
+        out[b, h] = round_to_bf16_bits(x) if w.dtype == "bf16" else x
+
+    n = threads or min(16, len(os.sched_getaffinity(0)))
+    with ThreadPoolExecutor(n) as ex:
+        list(ex.map(fill, range(w.B * w.H)))
+    return out
+
+
+def make_qkv(w: Workload):
+    return tuple(make_tensor(w, t) for t in range(3))
+
+
+def as_f64(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact upcast of stored inputs (bf16 bits or float32) to float64."""
+    if dtype == "bf16":
+        return bf16_bits_to_f32(x).astype(np.float64)
+    return x.astype(np.float64)
+
+
+def sample_rows(w: Workload, per_head: int, bm: int = 128, seed_offset: int = 7) -> np.ndarray:
+    """Seeded query-row subset used where the oracle cannot cover every row:
+    fixed edge rows (tile boundaries, the middle, the end) plus seeded random
+    rows, sorted and unique."""
+    N = w.N
+    edge = {0, 1, bm - 1, bm, 2 * bm - 1, 2 * bm, N // 2, N - 2, N - 1}
+    edge |= set(int(g) for g in w.global_idx)
+    edge = {r for r in edge if 0 <= r < N}
+    rng = np.random.default_rng(w.seed + seed_offset)
+    extra = max(0, per_head - len(edge))
+    rnd = rng.choice(N, size=min(extra, N), replace=False) if extra else []
+    return np.array(sorted(edge | set(int(r) for r in rnd)), dtype=np.int64)
+
+
+def random_workload(name: str, B: int, H: int, N: int, d: int, *, dtype="bf16",
+                    sigma=1.0, causal=1, win_left=-1, win_right=-1,
+                    global_idx=(), seed=0) -> Workload:
+    return Workload(name, B, H, N, d, dtype, sigma, causal, win_left, win_right,
+                    tuple(global_idx), seed, "ad-hoc")

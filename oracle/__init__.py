@@ -1,0 +1,10 @@
+"""CPU fp64 oracle for exact masked attention (test infrastructure only).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package. It shares no code with the HIP path.
+"""
+from .masked_attention import (attention, probabilities, online_softmax_rows, visible,
+                        mask_rows, visible_pairs_bruteforce, useful_flops)
+
+__all__ = ["attention", "probabilities", "online_softmax_rows", "visible",
+           "mask_rows", "visible_pairs_bruteforce", "useful_flops"]

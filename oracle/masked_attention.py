@@ -1,0 +1,196 @@
+"""CPU fp64 oracle for exact scaled dot-product attention with sparse masks.
+
+TEST INFRASTRUCTURE. Only the tests, ``__graft_entry__.smoke()`` and the CPU
+baseline leg of ``bench.py`` may import or call this module. The product path
+never does, and this module imports nothing from the product package.
+
+What it computes (plain definition, no tiling, no fusion):
+
+* Attention: each output row is the softmax-weighted sum of value rows, the
+  weights being the softmax over keys of the query-key dot products divided by
+  the square root of the head size. Sources: "Week 17 lecture notes on
+  efficient attention" (neelsoumya.github.io), opening recap of scaled
+  dot-product attention and its cost table; "Module 9 - Quadratic cost and
+  efficient attention", section "Where the n^2 hides".
+* Masking: invisible pairs get a score of minus infinity before the softmax,
+  as in the masked naive attention of "Efficient Transformers: Sparse
+  Attention, Linear Attention and FlashAttention" (section "Family 3") and the
+  sliding-window mask code of the week-17 notes.
+* Mask sets:
+    - local window, row i sees i-wl .. i+wr clipped to the sequence (week-17
+      notes, local-window passage; "Module 9", table in "Sparse and windowed
+      attention");
+    - Mistral-style causal sliding window (week-17 notes, Mistral passage;
+      "Sparse & sub-quadratic attention", section "Escape 1");
+    - global tokens that see every position and are seen by every position
+      (week-17 notes, global-token passage; "Efficient Transformers",
+      "Family 1"; "Sparse & sub-quadratic attention", "Escape 1").
+  Readings used where the pages leave a choice open:
+    - ``win_left``/``win_right`` count keys strictly left/right of the
+      diagonal; -1 means unbounded on that side;
+    - ``causal`` is combined with everything else by AND;
+    - a pair is visible if it is in the window band OR its row is global OR
+      its column is global (each pair counted once);
+    - LSE is the natural log of the sum over visible keys of exp(scaled
+      score), one value per query row;
+    - a row with no visible key (impossible under the argument rules, since
+      the diagonal is always visible) yields output 0 and LSE -inf.
+
+``online_softmax_rows`` restates the block recurrence of the week-17 notes
+(FlashAttention section, online-softmax pseudocode), read row by row, so that
+the algebra the GPU kernel relies on is itself checked against the two-pass
+definition above.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+
+def visible(i: int, j: int, N: int, causal: int, win_left: int, win_right: int,
+            global_set) -> bool:
+    """Scalar visibility predicate: may query row i attend to key j?"""
+    if not (0 <= i < N and 0 <= j < N):
+        return False
+    if causal and j > i:
+        return False
+    in_band = (win_left < 0 or j >= i - win_left) and (win_right < 0 or j <= i + win_right)
+    return bool(in_band or (i in global_set) or (j in global_set))
+
+
+def mask_rows(rows, N: int, causal: int, win_left: int, win_right: int,
+              global_idx=()) -> np.ndarray:
+    """Boolean visibility matrix [len(rows), N]: the predicate of `visible`
+    evaluated for every (row, key) pair."""
+    i = np.asarray(rows, dtype=np.int64)[:, None]
+    j = np.arange(N, dtype=np.int64)[None, :]
+    band = np.ones((i.shape[0], N), dtype=bool)
+    if win_left >= 0:
+        band &= j >= i - win_left
+    if win_right >= 0:
+        band &= j <= i + win_right
+    is_global = np.zeros(N, dtype=bool)
+    if len(global_idx):
+        is_global[np.asarray(global_idx, dtype=np.int64)] = True
+    vis = band | is_global[i] | is_global[j]
+    if causal:
+        vis &= j <= i
+    return vis
+
+
+def attention(q, k, v, *, causal: int, win_left: int = -1, win_right: int = -1,
+              global_idx=(), rows=None, scale: float | None = None,
+              row_block: int = 256):
+    """Masked softmax attention in fp64.
+
+    q, k, v: [B, H, N, d] arrays (any real dtype; upcast to float64).
+    rows:    optional 1-D array of query rows to compute (default: all).
+    Returns (O [B, H, R, d] float64, LSE [B, H, R] float64).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    rows = np.arange(N) if rows is None else np.asarray(rows, dtype=np.int64)
+    R = rows.shape[0]
+    out = np.zeros((B, H, R, v.shape[-1]), dtype=np.float64)
+    lse = np.full((B, H, R), -np.inf, dtype=np.float64)
+    for r0 in range(0, R, row_block):
+        rb = rows[r0:r0 + row_block]
+        vis = mask_rows(rb, N, causal, win_left, win_right, global_idx)
+        any_vis = vis.any(axis=1)
+        for b in range(B):
+            for h in range(H):
+                s = (q[b, h, rb] @ k[b, h].T) * scale          # full score rows
+                s = np.where(vis, s, -np.inf)
+                m = s.max(axis=1, keepdims=True)
+                m = np.where(np.isfinite(m), m, 0.0)
+                p = np.exp(s - m)                              # masked -> 0
+                l = p.sum(axis=1, keepdims=True)
+                safe_l = np.where(l > 0, l, 1.0)
+                out[b, h, r0:r0 + len(rb)] = np.where(any_vis[:, None], (p @ v[b, h]) / safe_l, 0.0)
+                lse[b, h, r0:r0 + len(rb)] = np.where(any_vis, m[:, 0] + np.log(safe_l[:, 0]), -np.inf)
+    return out, lse
+
+
+def probabilities(q, k, *, causal: int, win_left: int = -1, win_right: int = -1,
+                  global_idx=(), rows=None, scale: float | None = None):
+    """Softmax weights [B, H, R, N] (fp64) of the same definition; used to
+    check that visible weights sum to one and masked weights are zero."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    rows = np.arange(N) if rows is None else np.asarray(rows, dtype=np.int64)
+    vis = mask_rows(rows, N, causal, win_left, win_right, global_idx)
+    s = np.einsum("bhrd,bhnd->bhrn", q[:, :, rows], k) * scale
+    s = np.where(vis[None, None], s, -np.inf)
+    m = s.max(axis=-1, keepdims=True)
+    m = np.where(np.isfinite(m), m, 0.0)
+    p = np.exp(s - m)
+    l = p.sum(axis=-1, keepdims=True)
+    return p / np.where(l > 0, l, 1.0)
+
+
+def online_softmax_rows(q_rows, k, v, vis, block: int, scale: float | None = None):
+    """The block recurrence of the week-17 notes' online-softmax pseudocode,
+    applied to each query row separately (the running max is per row).
+
+    State per row: running max m, running normaliser ("denominator") l and a
+    running output o that is renormalised after every block:
+        m_new = max(m, max of this block's scores)
+        l_new = exp(m - m_new) * l + sum(exp(s - m_new))
+        o     = (exp(m - m_new) * l * o + exp(s - m_new) @ V_block) / l_new
+    q_rows: [R, d]; k, v: [N, d]; vis: bool [R, N]. Returns (O [R, d], LSE [R]).
+    """
+    q_rows = np.asarray(q_rows, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    R, d = q_rows.shape
+    N = k.shape[0]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    O = np.zeros((R, v.shape[1]))
+    LSE = np.full(R, -np.inf)
+    for r in range(R):
+        m, l = -np.inf, 0.0
+        o = np.zeros(v.shape[1])
+        for j0 in range(0, N, block):
+            j1 = min(N, j0 + block)
+            s = (k[j0:j1] @ q_rows[r]) * scale
+            s = np.where(vis[r, j0:j1], s, -np.inf)
+            bmax = s.max()
+            m_new = max(m, bmax)
+            if m_new == -np.inf:          # nothing visible yet: state unchanged
+                continue
+            e = np.exp(s - m_new)
+            carry = math.exp(m - m_new) if m != -np.inf else 0.0
+            l_new = carry * l + e.sum()
+            o = (carry * l * o + e @ v[j0:j1]) / l_new
+            m, l = m_new, l_new
+        O[r] = o
+        LSE[r] = m + math.log(l) if l > 0 else -np.inf
+    return O, LSE
+
+
+# ---- visible-pair counting -------------------------------------------------
+
+def visible_pairs_bruteforce(N: int, causal: int, win_left: int, win_right: int,
+                             global_idx=(), row_block: int = 4096) -> int:
+    """Count of visible (i, j) pairs of one head by evaluating the mask."""
+    total = 0
+    for r0 in range(0, N, row_block):
+        rows = np.arange(r0, min(N, r0 + row_block))
+        total += int(mask_rows(rows, N, causal, win_left, win_right, global_idx).sum())
+    return total
+
+
+def useful_flops(B: int, H: int, d: int, pairs_per_head: int) -> int:
+    """Useful FLOPs of one forward call: 2*d for the score of each visible
+    pair plus 2*d for its contribution to the output (cost table of the
+    week-17 notes: QK^T and weights-times-V each O(n^2 d))."""
+    return 4 * d * pairs_per_head * B * H
