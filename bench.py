@@ -1,0 +1,232 @@
+#!/usr/bin/env python3
+"""Throughput of the exact-attention forward on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--config tgt|c1|c2|c3|c4|c5]
+
+One step = one attn_fwd call (every pass the mask needs) over one batch of
+seeded synthetic inputs already resident in HBM. The default workload is
+causal attention at B=1, H=32, N=32768, d=128 in bf16, the shape the
+throughput target is quoted on. Useful FLOPs count visible pairs only:
+4*d per visible (query, key) pair (QK^T and PV, two flops per multiply-add).
+
+Prints one JSON line with the metric, a roofline object for the forward
+kernel (HIP events on the launch stream) and the CPU oracle timed on a bounded
+sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+# MI355X dense bf16 MFMA peak: 256 CUs x 2.4 GHz x 4096 flop/clk/CU = 2516.6
+# TFLOP/s (AMD's published 2.5 PFLOP/s); dense fp32 MFMA: 157.3 TFLOP/s.
+PEAK_BF16 = 2516.6
+PEAK_F32 = 157.3
+METRIC = "fwd attention TFLOP/s (unmasked FLOPs only) + % of bf16 MFMA peak"
+KERNEL_SRC = os.path.join(ROOT, "efficient_exact_attention_amd", "csrc", "attn_fwd.hip")
+
+
+def mask_name(w):
+    if w.global_idx:
+        return f"band -{w.win_left}/+{w.win_right} + {len(w.global_idx)} global tokens"
+    if w.causal and w.win_left >= 0:
+        return f"causal sliding window {w.win_left + 1}"
+    return "causal" if w.causal else "full"
+
+
+def source_hash():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def traffic_for(config):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if the
+    kernel source has not changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{config}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_sha256") != source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i["num_threads"] for i in threadpool_info() if i.get("user_api") == "blas"]
+        if n:
+            return int(max(n))
+    except Exception:
+        pass
+    return len(os.sched_getaffinity(0))
+
+
+def cpu_baseline(w, budget_s, gpu_out=None, gpu_lse=None):
+    """Time the oracle on a bounded, seeded sample of query rows of the same
+    workload (same input values as the GPU run)."""
+    import numpy as np
+    import oracle
+    from efficient_exact_attention_amd import workloads as W
+
+    rng = np.random.default_rng(w.seed + 1000)
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    order = [heads[i] for i in rng.permutation(len(heads))]
+    t_used = 0.0
+    flops = 0
+    nrows = 0
+    nheads = 0
+    max_err = 0.0
+    rows_per_head = 64
+    for (b, h) in order:
+        q, k, v = (W.head_values(w, t, b, h).astype(np.float64) for t in range(3))
+        rows = np.sort(rng.choice(w.N, size=min(rows_per_head, w.N), replace=False))
+        t0 = time.perf_counter()
+        O, L = oracle.attention(q[None, None], k[None, None], v[None, None], causal=w.causal,
+                                win_left=w.win_left, win_right=w.win_right,
+                                global_idx=w.global_idx, rows=rows)
+        dt = time.perf_counter() - t0
+        t_used += dt
+        vis = oracle.mask_rows(rows, w.N, w.causal, w.win_left, w.win_right, w.global_idx)
+        flops += 4 * w.d * int(vis.sum())
+        nrows += len(rows)
+        nheads += 1
+        if gpu_out is not None:
+            go = gpu_out[b, h, rows].float().cpu().numpy().astype(np.float64)
+            max_err = max(max_err, float(np.max(np.abs(go - O[0, 0]))))
+        if t_used >= budget_s:
+            break
+        # scale the next heads' row count towards the budget
+        per_row = t_used / nrows
+        rows_per_head = int(min(w.N, max(16, (budget_s - t_used) / per_row / 2)))
+    return dict(value=flops / t_used / 1e12, unit="TFLOP/s", cores=blas_threads(), kind="oracle",
+                sample=f"{nrows} seeded query rows over {nheads} head(s) of the same workload, "
+                       f"numpy fp64 full masked score rows, {t_used:.1f} s",
+                seconds=round(t_used, 2)), max_err
+
+
+def main():
+    from efficient_exact_attention_amd import workloads as W
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="tgt", choices=sorted(W.WORKLOADS))
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures a single GPU: the attention forward of one GPU's share "
+              "(heads are independent) is what this library runs; --gpus must be 1.",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    import efficient_exact_attention_amd as ea
+    ea.lib()
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        return 1
+
+    w = W.WORKLOADS[args.config]
+    print(f"[bench] generating {w.name}: B={w.B} H={w.H} N={w.N} d={w.d} {w.dtype}", file=sys.stderr,
+          flush=True)
+    qkv = W.make_qkv(w)
+
+    def dev(x):
+        if w.dtype == "bf16":
+            return torch.from_numpy(x.view("int16")).view(torch.bfloat16).cuda()
+        return torch.from_numpy(x).cuda()
+    q, k, v = (dev(x) for x in qkv)
+    del qkv
+    out = torch.empty_like(q)
+    lse = torch.empty(w.B, w.H, w.N, dtype=torch.float32, device="cuda")
+    pairs = ea.attn_plan_stats(w.N, w.causal, w.win_left, w.win_right, w.global_idx, 128, 64)[0]
+    flops = 4 * w.d * pairs * w.B * w.H
+    ws = None
+    if w.global_idx:
+        ws = torch.empty(ea.attn_workspace_bytes(w.B, w.H, w.N, w.d, len(w.global_idx)),
+                         dtype=torch.uint8, device="cuda")
+
+    stream = torch.cuda.current_stream()
+
+    def step():
+        ea.fwd(q, k, v, causal=w.causal, win_left=w.win_left, win_right=w.win_right,
+               global_idx=w.global_idx or None, out=out, lse=lse, workspace=ws, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup}), timing {args.steps} steps", file=sys.stderr, flush=True)
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for s, e in ev:
+        s.record(stream)
+        step()
+        e.record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+    launch_ms = sorted(s.elapsed_time(e) for s, e in ev)
+    avg_launch_ms = sum(launch_ms) / len(launch_ms)
+    value = flops / (ms_step * 1e-3) / 1e12
+    achieved = flops / (avg_launch_ms * 1e-3) / 1e12
+    peak = PEAK_F32 if w.dtype == "f32" else PEAK_BF16
+    print(f"[bench] {ms_step:.3f} ms/step, {value:.1f} TFLOP/s, launch avg {avg_launch_ms:.3f} ms "
+          f"(min {launch_ms[0]:.3f}, max {launch_ms[-1]:.3f}), wall {wall:.2f} s", file=sys.stderr,
+          flush=True)
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{mask_name(w)} attention forward B={w.B} H={w.H} N={w.N} d={w.d}",
+                   "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
+                   "win_left": w.win_left, "win_right": w.win_right,
+                   "n_global": len(w.global_idx), "seed": w.seed,
+                   "inputs": f"{w.dtype} ~N(0,{w.sigma}^2)", "useful_flop_per_step": flops},
+        "pct_bf16_peak": round(100.0 * value / PEAK_BF16, 2),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": traffic_for(args.config),
+                     "kernel": "attn_fwd (band pass)" if not w.global_idx
+                     else "attn_fwd call (band pass + global rows + merge)"},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        print(f"[bench] timing the CPU oracle for ~{args.cpu_seconds:.0f} s", file=sys.stderr, flush=True)
+        cb, err = cpu_baseline(w, args.cpu_seconds, out, lse)
+        result["cpu_baseline"] = cb
+        result["sample_max_abs_err_vs_oracle"] = err
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,163 @@
+"""Python binding of the gfx950 exact-attention library (include/attn.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``libattn.so``. PyTorch supplies device memory and the stream.
+If the library has not been built, every entry point raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = ["AttnError", "attn_fwd", "attn_fwd_ex", "attn_workspace_bytes", "attn_plan_stats",
+           "attn_tile_shape", "attn_last_error", "attn_version", "fwd", "library_path",
+           "ATTN_OK", "ATTN_ERR_INVALID_ARG", "ATTN_ERR_UNSUPPORTED", "ATTN_ERR_DEVICE",
+           "ATTN_BF16", "ATTN_F32"]
+
+ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_DEVICE = 0, 1, 2, 3
+ATTN_BF16, ATTN_F32 = 0, 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libattn.so")
+_lib = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"attn status {status}: {message}")
+        self.status = status
+        self.message = message
+
+
+class _Opts(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int), ("scale", ctypes.c_float), ("stream", ctypes.c_void_p),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def lib():
+    """Load libattn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is missing: build it with "
+                           "`python -m efficient_exact_attention_amd.build`")
+    L = ctypes.CDLL(_LIB_PATH)
+    vp, ci = ctypes.c_void_p, ctypes.c_int
+    fwd_args = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, ctypes.POINTER(ci), ci]
+    L.attn_fwd.argtypes = fwd_args
+    L.attn_fwd.restype = ci
+    L.attn_fwd_ex.argtypes = fwd_args + [ctypes.POINTER(_Opts)]
+    L.attn_fwd_ex.restype = ci
+    L.attn_workspace_bytes.argtypes = [ci, ci, ci, ci, ci]
+    L.attn_workspace_bytes.restype = ctypes.c_size_t
+    ll = ctypes.POINTER(ctypes.c_longlong)
+    L.attn_plan_stats.argtypes = [ci, ci, ci, ci, ctypes.POINTER(ci), ci, ci, ci, ll, ll, ll]
+    L.attn_plan_stats.restype = ci
+    L.attn_tile_shape.argtypes = [ci, ci, ctypes.POINTER(ci), ctypes.POINTER(ci)]
+    L.attn_tile_shape.restype = ci
+    L.attn_last_error.argtypes = []
+    L.attn_last_error.restype = ctypes.c_char_p
+    L.attn_version.argtypes = []
+    L.attn_version.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def attn_last_error() -> str:
+    return lib().attn_last_error().decode()
+
+
+def attn_version() -> str:
+    return lib().attn_version().decode()
+
+
+def _check(status: int):
+    if status != ATTN_OK:
+        raise AttnError(status, attn_last_error())
+
+
+def _gidx(global_idx):
+    if global_idx is None or len(global_idx) == 0:
+        return None, 0
+    arr = (ctypes.c_int * len(global_idx))(*[int(g) for g in global_idx])
+    return arr, len(global_idx)
+
+
+def attn_fwd(q, k, v, out, lse, B, H, N, d, causal, win_left, win_right, global_idx=None):
+    """Raw entry point: q, k, v, out, lse are integer device addresses."""
+    g, ng = _gidx(global_idx)
+    _check(lib().attn_fwd(q, k, v, out, lse, B, H, N, d, causal, win_left, win_right, g, ng))
+
+
+def attn_fwd_ex(q, k, v, out, lse, B, H, N, d, causal, win_left, win_right, global_idx=None,
+                *, dtype=ATTN_BF16, scale=0.0, stream=None, workspace=None, workspace_bytes=0):
+    """Raw entry point with options: pointers and stream are integers."""
+    g, ng = _gidx(global_idx)
+    opts = _Opts(dtype, float(scale), stream, workspace, workspace_bytes)
+    _check(lib().attn_fwd_ex(q, k, v, out, lse, B, H, N, d, causal, win_left, win_right, g, ng,
+                             ctypes.byref(opts)))
+
+
+def attn_workspace_bytes(B, H, N, d, n_global) -> int:
+    return int(lib().attn_workspace_bytes(B, H, N, d, n_global))
+
+
+def attn_plan_stats(N, causal, win_left, win_right, global_idx, bm, bn):
+    """(visible_pairs, tiles_full, tiles_edge) of one head."""
+    g, ng = _gidx(global_idx)
+    a, b, c = ctypes.c_longlong(), ctypes.c_longlong(), ctypes.c_longlong()
+    _check(lib().attn_plan_stats(N, causal, win_left, win_right, g, ng, bm, bn,
+                                 ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)))
+    return a.value, b.value, c.value
+
+
+def attn_tile_shape(d, dtype=ATTN_BF16):
+    bm, bn = ctypes.c_int(), ctypes.c_int()
+    _check(lib().attn_tile_shape(d, dtype, ctypes.byref(bm), ctypes.byref(bn)))
+    return bm.value, bn.value
+
+
+def fwd(q, k, v, *, causal=False, win_left=-1, win_right=-1, global_idx=None, scale=None,
+        out=None, lse=None, workspace=None, stream=None):
+    """Attention forward on torch CUDA tensors [B, H, N, d] (bf16 or fp32).
+
+    Allocates ``out`` (input dtype) and ``lse`` (fp32 [B, H, N]) with torch
+    unless given, enqueues the kernels on torch's current stream (or
+    ``stream``) and returns (out, lse) without synchronising.
+    """
+    import torch
+    if q.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype != q.dtype or t.shape != q.shape:
+            raise ValueError(f"{name} must match q in dtype and shape")
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    if q.dim() != 4:
+        raise ValueError("tensors must be [B, H, N, d]")
+    B, H, N, d = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor shaped and typed like q")
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous fp32 tensor [B, H, N]")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    ws, wsb = (workspace.data_ptr(), workspace.numel() * workspace.element_size()) \
+        if workspace is not None else (None, 0)
+    attn_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                B, H, N, d, int(bool(causal)), int(win_left), int(win_right), global_idx,
+                dtype=ATTN_F32 if q.dtype == torch.float32 else ATTN_BF16,
+                scale=0.0 if scale is None else float(scale), stream=stream,
+                workspace=ws, workspace_bytes=wsb)
+    return out, lse

@@ -1,0 +1,282 @@
+// attn_api.cpp - the C ABI of include/attn.h: argument validation, error
+// reporting, workspace handling and the host-side tile planner.
+//
+// Every argument is checked before the first HIP call, so every error path
+// can be exercised on a machine without a GPU.
+#include "attn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <climits>
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "attn_internal.h"
+#include "attn_plan.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+struct DeviceSlot {
+    int arch_checked = 0;
+    int arch_ok = 0;
+    void *scratch = nullptr;
+    size_t scratch_bytes = 0;
+};
+std::mutex g_mu;
+std::vector<DeviceSlot> g_dev;
+
+DeviceSlot &slot(int dev) {
+    if ((int)g_dev.size() <= dev) g_dev.resize(dev + 1);
+    return g_dev[dev];
+}
+
+bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
+    uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + nb && y < x + na;
+}
+
+// Largest split-key workspace over both element types.
+size_t workspace_for(int BH, int N, int d, int ng) {
+    size_t best = 0;
+    for (int f32 = 0; f32 < 2; ++f32) {
+        int ct = 0;
+        int chunks = eea::global_chunks(BH, N, d, f32, &ct);
+        size_t b = (size_t)BH * ng * chunks * (d + 2) * sizeof(float);
+        best = std::max(best, b);
+    }
+    return best;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *attn_version(void) { return "efficient_exact_attention_amd 0.1.0 (gfx950)"; }
+
+const char *attn_last_error(void) { return g_err.c_str(); }
+
+int attn_tile_shape(int d, int dtype, int *bm, int *bn) {
+    if (d != 64 && d != 128) return fail(ATTN_ERR_UNSUPPORTED, "head size d=%d is not supported (64 or 128)", d);
+    if (dtype != ATTN_BF16 && dtype != ATTN_F32) return fail(ATTN_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+    if (bm) *bm = eea::tile_bm(d, dtype == ATTN_F32);
+    if (bn) *bn = eea::tile_bn(d, dtype == ATTN_F32);
+    return ATTN_OK;
+}
+
+size_t attn_workspace_bytes(int B, int H, int N, int d, int n_global) {
+    if (B <= 0 || H <= 0 || N <= 0 || n_global <= 0 || n_global > eea::kMaxGlobal) return 0;
+    if (d != 64 && d != 128) return 0;
+    if ((long long)B * H > INT_MAX) return 0;
+    return workspace_for(B * H, N, d, n_global);
+}
+
+static int check_globals(const int *global_idx, int n_global, int N, std::vector<int> &sorted) {
+    if (n_global < 0) return fail(ATTN_ERR_INVALID_ARG, "n_global=%d is negative", n_global);
+    if (n_global > eea::kMaxGlobal)
+        return fail(ATTN_ERR_UNSUPPORTED, "n_global=%d exceeds the supported maximum of %d", n_global,
+                    eea::kMaxGlobal);
+    if (n_global > 0 && !global_idx) return fail(ATTN_ERR_INVALID_ARG, "global_idx is NULL with n_global=%d", n_global);
+    sorted.assign(global_idx, global_idx + n_global);
+    std::sort(sorted.begin(), sorted.end());
+    for (int t = 0; t < n_global; ++t) {
+        if (sorted[t] < 0 || sorted[t] >= N)
+            return fail(ATTN_ERR_INVALID_ARG, "global index %d is outside [0, %d)", sorted[t], N);
+        if (t > 0 && sorted[t] == sorted[t - 1])
+            return fail(ATTN_ERR_INVALID_ARG, "global index %d is listed twice", sorted[t]);
+    }
+    return ATTN_OK;
+}
+
+int attn_plan_stats(int N, int causal, int win_left, int win_right, const int *global_idx, int n_global,
+                    int bm, int bn, long long *visible_pairs, long long *tiles_full, long long *tiles_edge) {
+    g_err.clear();
+    if (N <= 0) return fail(ATTN_ERR_INVALID_ARG, "N=%d must be positive", N);
+    if (bm <= 0 || bn <= 0) return fail(ATTN_ERR_INVALID_ARG, "tile shape %dx%d must be positive", bm, bn);
+    if (causal != 0 && causal != 1) return fail(ATTN_ERR_INVALID_ARG, "causal=%d must be 0 or 1", causal);
+    if (win_left < -1 || win_right < -1)
+        return fail(ATTN_ERR_INVALID_ARG, "window (%d, %d) must be >= -1", win_left, win_right);
+    std::vector<int> G;
+    int rc = check_globals(global_idx, n_global, N, G);
+    if (rc != ATTN_OK) return rc;
+
+    const eea::Band band = eea::make_band(N, causal, win_left, win_right);
+    const bool use_g = n_global > 0 && !eea::band_is_everything(band, causal);
+    std::vector<char> is_g(N, 0);
+    if (use_g)
+        for (int g : G) is_g[g] = 1;
+
+    long long pairs = 0, full = 0, edge = 0;
+    for (int i = 0; i < N; ++i) {
+        const int lo = eea::row_lo(band, i), hi = eea::row_hi(band, i);
+        if (use_g && is_g[i]) {
+            pairs += causal ? (long long)i + 1 : (long long)N;
+            continue;
+        }
+        pairs += hi - lo + 1;
+        if (use_g)
+            for (int g : G)
+                if ((g < lo || g > hi) && (!causal || g <= i)) ++pairs;
+    }
+    const int nqt = (N + bm - 1) / bm;
+    for (int qt = 0; qt < nqt; ++qt) {
+        const int r0 = qt * bm, r1 = std::min(N - 1, r0 + bm - 1);
+        int klo, khi;
+        eea::key_tile_range(band, r0, r1, bn, &klo, &khi);
+        for (int kt = klo; kt <= khi; ++kt) {
+            const int cl = eea::classify(band, r0, r1, kt * bn, kt * bn + bn - 1);
+            if (cl == eea::TILE_FULL) ++full;
+            else if (cl == eea::TILE_EDGE) ++edge;
+        }
+        if (use_g) ++edge;   // gathered tile of global columns
+    }
+    if (use_g)
+        for (int g : G) {
+            const long long keys = causal ? (long long)g + 1 : (long long)N;
+            edge += (keys + bn - 1) / bn;
+        }
+    if (visible_pairs) *visible_pairs = pairs;
+    if (tiles_full) *tiles_full = full;
+    if (tiles_edge) *tiles_edge = edge;
+    return ATTN_OK;
+}
+
+int attn_fwd_ex(const void *q, const void *k, const void *v, void *out, float *lse, int B, int H, int N, int d,
+                int causal, int win_left, int win_right, const int *global_idx, int n_global,
+                const attn_opts *opts) {
+    g_err.clear();
+    const int dtype = opts ? opts->dtype : ATTN_BF16;
+    if (!q || !k || !v || !out || !lse) return fail(ATTN_ERR_INVALID_ARG, "a tensor pointer is NULL");
+    if (B <= 0 || H <= 0 || N <= 0)
+        return fail(ATTN_ERR_INVALID_ARG, "sizes B=%d H=%d N=%d must be positive", B, H, N);
+    if (dtype != ATTN_BF16 && dtype != ATTN_F32) return fail(ATTN_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+    if (causal != 0 && causal != 1) return fail(ATTN_ERR_INVALID_ARG, "causal=%d must be 0 or 1", causal);
+    if (win_left < -1 || win_right < -1)
+        return fail(ATTN_ERR_INVALID_ARG, "window (%d, %d) must be >= -1", win_left, win_right);
+    if (d != 64 && d != 128) return fail(ATTN_ERR_UNSUPPORTED, "head size d=%d is not supported (64 or 128)", d);
+    std::vector<int> G;
+    int rc = check_globals(global_idx, n_global, N, G);
+    if (rc != ATTN_OK) return rc;
+
+    const long long BH = (long long)B * H;
+    const int bm = eea::tile_bm(d, dtype == ATTN_F32);
+    const long long nqt = (N + (long long)bm - 1) / bm;
+    if (BH > INT_MAX || BH * nqt > INT_MAX)
+        return fail(ATTN_ERR_INVALID_ARG, "B*H=%lld with N=%d exceeds the launch grid", BH, N);
+    const size_t esize = dtype == ATTN_F32 ? 4 : 2;
+    const size_t tbytes = (size_t)BH * N * d * esize;   // < 2^31 * 2^31 * 128 * 4: fits in 64 bits
+    const size_t lbytes = (size_t)BH * N * sizeof(float);
+
+    if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out) & 15)
+        return fail(ATTN_ERR_INVALID_ARG, "q, k, v and out must be 16-byte aligned");
+    if ((uintptr_t)lse & 3) return fail(ATTN_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+    if (overlaps(out, tbytes, q, tbytes) || overlaps(out, tbytes, k, tbytes) || overlaps(out, tbytes, v, tbytes))
+        return fail(ATTN_ERR_INVALID_ARG, "out overlaps an input tensor");
+    if (overlaps(lse, lbytes, q, tbytes) || overlaps(lse, lbytes, k, tbytes) || overlaps(lse, lbytes, v, tbytes) ||
+        overlaps(lse, lbytes, out, tbytes))
+        return fail(ATTN_ERR_INVALID_ARG, "lse overlaps another tensor");
+
+    float scale = (opts && opts->scale != 0.f) ? opts->scale : 1.0f / std::sqrt((float)d);
+    if (!(scale > 0.f) || !std::isfinite(scale))
+        return fail(ATTN_ERR_INVALID_ARG, "scale must be positive and finite");
+
+    const eea::Band band = eea::make_band(N, causal, win_left, win_right);
+    const int ng = eea::band_is_everything(band, causal) ? 0 : n_global;
+
+    eea::FwdParams p;
+    std::memset(&p, 0, sizeof p);
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.out = out;
+    p.lse = lse;
+    p.head_stride = (long long)N * d;
+    p.BH = (int)BH;
+    p.N = N;
+    p.wl = band.wl;
+    p.wr = band.wr;
+    p.causal = causal;
+    p.n_global = ng;
+    p.num_qt = (int)nqt;
+    p.scale_log2 = scale * 1.4426950408889634f;
+    for (int t = 0; t < ng; ++t) p.gidx[t] = G[t];
+
+    size_t need = 0;
+    if (ng > 0) {
+        int ct = 0;
+        p.chunks = eea::global_chunks((int)BH, N, d, dtype == ATTN_F32, &ct);
+        p.chunk_tiles = ct;
+        need = (size_t)BH * ng * p.chunks * (d + 2) * sizeof(float);
+        if (opts && opts->workspace) {
+            if (opts->workspace_bytes < need)
+                return fail(ATTN_ERR_INVALID_ARG, "workspace of %zu bytes is smaller than the %zu needed",
+                            opts->workspace_bytes, need);
+            if ((uintptr_t)opts->workspace & 15)
+                return fail(ATTN_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+            p.part = static_cast<float *>(opts->workspace);
+        }
+    }
+
+    // ---- first HIP call
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(ATTN_ERR_DEVICE, "hipGetDevice: %s", hipGetErrorString(e));
+    {
+        std::lock_guard<std::mutex> lk(g_mu);
+        DeviceSlot &s = slot(dev);
+        if (!s.arch_checked) {
+            hipDeviceProp_t prop;
+            e = hipGetDeviceProperties(&prop, dev);
+            if (e != hipSuccess) return fail(ATTN_ERR_DEVICE, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+            s.arch_ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+            s.arch_checked = 1;
+        }
+        if (!s.arch_ok) return fail(ATTN_ERR_UNSUPPORTED, "device %d is not gfx950 (MI355X)", dev);
+        if (ng > 0 && !p.part) {
+            if (s.scratch_bytes < need) {
+                if (s.scratch) {
+                    e = hipFree(s.scratch);
+                    s.scratch = nullptr;
+                    s.scratch_bytes = 0;
+                    if (e != hipSuccess) return fail(ATTN_ERR_DEVICE, "hipFree: %s", hipGetErrorString(e));
+                }
+                e = hipMalloc(&s.scratch, need);
+                if (e != hipSuccess) {
+                    s.scratch = nullptr;
+                    return fail(ATTN_ERR_DEVICE, "hipMalloc(%zu): %s", need, hipGetErrorString(e));
+                }
+                s.scratch_bytes = need;
+            }
+            p.part = static_cast<float *>(s.scratch);
+        }
+    }
+    hipStream_t stream = opts ? static_cast<hipStream_t>(opts->stream) : nullptr;
+    e = eea::launch_forward(p, d, dtype == ATTN_F32, stream);
+    if (e != hipSuccess) return fail(ATTN_ERR_DEVICE, "kernel launch: %s", hipGetErrorString(e));
+    return ATTN_OK;
+}
+
+int attn_fwd(const void *q, const void *k, const void *v, void *out, float *lse, int B, int H, int N, int d,
+             int causal, int win_left, int win_right, const int *global_idx, int n_global) {
+    return attn_fwd_ex(q, k, v, out, lse, B, H, N, d, causal, win_left, win_right, global_idx, n_global, nullptr);
+}
+
+}  // extern "C"

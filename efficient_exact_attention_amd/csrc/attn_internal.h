@@ -1,0 +1,46 @@
+// attn_internal.h - parameter block and launcher entry points shared between
+// the C ABI (attn_api.cpp) and the HIP kernels (attn_fwd.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace eea {
+
+constexpr int kMaxGlobal = 64;       // one gathered key tile holds every global column
+
+// Kernel arguments. Offsets are 64-bit throughout: one head at N=131072, d=128
+// is 2^24 elements and B*H*N*d can exceed 2^31.
+struct FwdParams {
+    const void *q;
+    const void *k;
+    const void *v;
+    void *out;
+    float *lse;
+    float *part;          // global-row partials [B*H][n_global][chunks][d + 2]
+    long long head_stride;  // N * d elements
+    int BH;               // B * H
+    int N;
+    int wl, wr;           // normalised band (see attn_plan.h)
+    int causal;
+    int n_global;         // 0 when the band already covers every visible key
+    int num_qt;           // query tiles per head
+    int chunks;           // key chunks per global row (split-key pass)
+    int chunk_tiles;      // key tiles per chunk
+    int xcd_remap;        // 1: group consecutive work items on one XCD
+    float scale_log2;     // score scale * log2(e)
+    int gidx[kMaxGlobal]; // sorted global positions
+};
+
+// Tile shapes chosen per (d, dtype).
+int tile_bm(int d, int f32);
+int tile_bn(int d, int f32);
+
+// Enqueue the band pass (every query tile), then, when n_global > 0, the
+// split-key pass over global rows and the merge. Returns a hipError_t.
+hipError_t launch_forward(const FwdParams &p, int d, int f32, hipStream_t stream);
+
+// Number of key chunks the split-key pass uses for these sizes.
+int global_chunks(int BH, int N, int d, int f32, int *chunk_tiles);
+
+}  // namespace eea

@@ -1,0 +1,141 @@
+/*
+ * attn.h - C ABI of the MI355X (gfx950) exact-attention forward library.
+ *
+ * The operation is exact scaled dot-product attention,
+ *     out_i = sum_j softmax_j(q_i . k_j / sqrt(d)) v_j      (visible j only),
+ * computed tile by tile with an online softmax so the N x N score matrix is
+ * never stored ("Efficient Transformers: Sparse Attention, Linear Attention and
+ * FlashAttention", sections "Family 3: exact attention, computed smarter" and
+ * "The online softmax trick"; week-17 lecture notes on efficient attention,
+ * FlashAttention tiling and online-softmax passages). Sparse masks follow the
+ * week-17 notes (local window, Mistral sliding window, global tokens),
+ * "Sparse & sub-quadratic attention" ("Escape 1") and "Module 9 - Quadratic
+ * cost and efficient attention" ("Sparse and windowed attention").
+ *
+ * Conventions shared by every entry point:
+ *   - Tensors q, k, v, out are dense row-major [B][H][N][d] (head-major, one
+ *     row of d elements per token), element type bf16 (default) or fp32.
+ *     lse is dense [B][H][N] fp32.
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller; the library
+ *     never frees or retains it. Pointers must be 16-byte aligned (lse: 4).
+ *     q, k and v may alias one another; out and lse must not overlap any input
+ *     or each other.
+ *   - global_idx is a HOST array of n_global int32 token positions, unique,
+ *     each in [0, N), any order. It is copied before the call returns.
+ *   - All device work is enqueued asynchronously on the chosen stream; the
+ *     call does not synchronise. Execution errors surface at the caller's
+ *     next synchronisation on that stream.
+ *   - Every argument is validated before any HIP call. Functions return an
+ *     attn_status; no exception crosses the ABI and the library never aborts.
+ *     attn_last_error() gives a message for the last non-OK status of the
+ *     calling thread.
+ */
+#ifndef EEA_ATTN_H
+#define EEA_ATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    ATTN_OK = 0,
+    ATTN_ERR_INVALID_ARG = 1,   /* bad pointer, size, index, alignment or overlap */
+    ATTN_ERR_UNSUPPORTED = 2,   /* valid request this build does not implement */
+    ATTN_ERR_DEVICE = 3         /* HIP runtime error; message in attn_last_error() */
+} attn_status;
+
+typedef enum { ATTN_BF16 = 0, ATTN_F32 = 1 } attn_dtype;
+
+typedef struct attn_opts {
+    int dtype;              /* attn_dtype of q, k, v and out */
+    float scale;            /* score scale; 0 selects 1/sqrt(d) */
+    void *stream;           /* hipStream_t to enqueue on; NULL = default stream */
+    void *workspace;        /* device scratch for global-row partial results, or
+                               NULL to use a library-owned buffer (see below) */
+    size_t workspace_bytes; /* size of workspace; must be >= attn_workspace_bytes() */
+} attn_opts;
+
+/*
+ * attn_fwd - masked exact attention forward, bf16 in/out, scale 1/sqrt(d),
+ * default stream. Equivalent to attn_fwd_ex(..., NULL).
+ *
+ *   q, k, v     [B][H][N][d] bf16 inputs.
+ *   out         [B][H][N][d] bf16 output: softmax-weighted sum of value rows.
+ *   lse         [B][H][N] fp32 output: natural log of the sum over visible
+ *               keys of exp(scaled score), the per-row log-sum-exp that a
+ *               recomputing backward pass needs.
+ *   B, H, N     batch, heads, tokens (each >= 1).
+ *   d           head size, 64 or 128 (others: ATTN_ERR_UNSUPPORTED).
+ *   causal      1: key j is visible from row i only if j <= i. 0: no such limit.
+ *   win_left    keys strictly left of the diagonal that row i may see:
+ *               j >= i - win_left. -1 = unbounded. A Mistral window of w
+ *               tokens ending at i is win_left = w - 1.
+ *   win_right   keys strictly right of the diagonal: j <= i + win_right.
+ *               -1 = unbounded. Ignored (taken as 0) when causal = 1.
+ *   global_idx  host array of global token positions (may be NULL when
+ *               n_global = 0). A global row sees every key and a global
+ *               column is seen by every row, the causal limit still applying.
+ *   n_global    0..64 (more: ATTN_ERR_UNSUPPORTED).
+ *
+ * Visible(i, j) = [causal => j <= i] AND ( in_window(i, j) OR i in G OR j in G ).
+ * Every row sees at least its diagonal key, so no row is empty.
+ */
+int attn_fwd(const void *q, const void *k, const void *v, void *out, float *lse,
+             int B, int H, int N, int d, int causal, int win_left, int win_right,
+             const int *global_idx, int n_global);
+
+/*
+ * attn_fwd_ex - as attn_fwd with options (opts may be NULL for defaults).
+ * With opts->dtype = ATTN_F32, q, k, v and out are fp32 and both products run
+ * in fp32 on the matrix cores. When n_global > 0 and the window does not
+ * already cover every key, the global query rows are computed by a separate
+ * split-key pass that needs attn_workspace_bytes() of device scratch: taken
+ * from opts->workspace if given, else from a buffer the library allocates
+ * once per device (guarded by a mutex, grown on demand, never freed).
+ */
+int attn_fwd_ex(const void *q, const void *k, const void *v, void *out, float *lse,
+                int B, int H, int N, int d, int causal, int win_left, int win_right,
+                const int *global_idx, int n_global, const attn_opts *opts);
+
+/*
+ * attn_workspace_bytes - device scratch a call with these sizes needs for the
+ * global-row partial results; 0 when n_global = 0. It grows with
+ * B*H*n_global*d and a chunk count bounded by N/64, never with N*N.
+ * Returns 0 for invalid sizes.
+ */
+size_t attn_workspace_bytes(int B, int H, int N, int d, int n_global);
+
+/*
+ * attn_plan_stats - host-only description of the work the tile scheduler
+ * does for one head at a tile shape of bm query rows by bn keys: the number
+ * of visible (i, j) pairs, and the number of band key tiles visited that need
+ * no mask (tiles_full) or need one (tiles_edge), summed over the query tiles.
+ * Tiles with no visible pair are never visited and not counted. Global
+ * columns add one gathered tile per query tile (counted in tiles_edge);
+ * global rows are counted as ceil(keys / bn) edge tiles each. Output
+ * pointers are host pointers; any may be NULL. Makes no HIP call.
+ */
+int attn_plan_stats(int N, int causal, int win_left, int win_right,
+                    const int *global_idx, int n_global, int bm, int bn,
+                    long long *visible_pairs, long long *tiles_full,
+                    long long *tiles_edge);
+
+/*
+ * attn_tile_shape - the tile shape (query rows, keys) the forward kernel uses
+ * for head size d and element type dtype. Host-only, no HIP call.
+ */
+int attn_tile_shape(int d, int dtype, int *bm, int *bn);
+
+/* attn_last_error - message for the calling thread's last non-OK status ("" if none). */
+const char *attn_last_error(void);
+
+/* attn_version - library version string. */
+const char *attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EEA_ATTN_H */

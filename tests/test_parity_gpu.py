@@ -1,0 +1,244 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle,
+element by element on seeded inputs."""
+import numpy as np
+import pytest
+
+import oracle
+from efficient_exact_attention_amd import workloads as W
+from gpu_common import (all_heads, check, errors, host_f64, oracle_heads, run_gpu, say,
+                        some_heads, to_device)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import efficient_exact_attention_amd as ea
+    ea.lib()   # loud failure if the library is missing
+
+
+SMALL_MASKS = {
+    "full": dict(causal=0, win_left=-1, win_right=-1, global_idx=()),
+    "causal": dict(causal=1, win_left=-1, win_right=-1, global_idx=()),
+    "swa100": dict(causal=1, win_left=100, win_right=0, global_idx=()),
+    "band50": dict(causal=0, win_left=50, win_right=50, global_idx=()),
+    "band7_g": dict(causal=0, win_left=7, win_right=7, global_idx=(0, 1, 130, 999)),
+    "swa33_g": dict(causal=1, win_left=33, win_right=0, global_idx=(2, 64, 500)),
+    "asym": dict(causal=0, win_left=3, win_right=90, global_idx=()),
+}
+
+
+def _mk(name, B, H, N, d, dtype, mask, seed, sigma=1.0):
+    g = tuple(x for x in mask["global_idx"] if x < N)
+    return W.random_workload(name, B, H, N, d, dtype=dtype, sigma=sigma, causal=mask["causal"],
+                             win_left=mask["win_left"], win_right=mask["win_right"],
+                             global_idx=g, seed=seed)
+
+
+# ---- small shapes: several tiles and ragged tails, every row checked --------------------
+
+@pytest.mark.parametrize("mask", list(SMALL_MASKS))
+@pytest.mark.parametrize("N", [1, 37, 128, 200, 1000])
+@pytest.mark.parametrize("d", [64, 128])
+def test_small_bf16(mask, N, d):
+    w = _mk(f"small-{mask}-{N}-{d}", 2, 3, N, d, "bf16", SMALL_MASKS[mask], seed=N * 7 + d)
+    qkv = W.make_qkv(w)
+    o, l = run_gpu(w, qkv)
+    check(w, o, l, all_heads(w), np.arange(N), qkv)
+
+
+@pytest.mark.parametrize("mask", ["full", "causal", "swa100", "band7_g"])
+@pytest.mark.parametrize("N,d", [(1, 64), (77, 64), (300, 128)])
+def test_small_fp32(mask, N, d):
+    w = _mk(f"f32-{mask}-{N}-{d}", 1, 2, N, d, "f32", SMALL_MASKS[mask], seed=N + d)
+    qkv = W.make_qkv(w)
+    o, l = run_gpu(w, qkv)
+    # fp32 products on the matrix cores: far inside the contract tolerance
+    check(w, o, l, all_heads(w), np.arange(N), qkv, tol=(1e-4, 1e-5, 1e-4))
+
+
+def test_many_globals():
+    g = tuple(range(0, 2000, 33))[:64]
+    w = W.random_workload("g64", 1, 2, 2000, 64, causal=0, win_left=20, win_right=20,
+                          global_idx=g, seed=5)
+    qkv = W.make_qkv(w)
+    o, l = run_gpu(w, qkv)
+    check(w, o, l, all_heads(w), np.arange(2000), qkv)
+
+
+def test_causal_globals_bf16_d128():
+    w = W.random_workload("cg", 2, 2, 3000, 128, causal=1, win_left=200, win_right=0,
+                          global_idx=(0, 1, 1024, 2999), seed=6)
+    qkv = W.make_qkv(w)
+    o, l = run_gpu(w, qkv)
+    check(w, o, l, all_heads(w), np.arange(3000), qkv)
+
+
+# ---- the benchmark workloads at full size ---------------------------------------------
+
+def test_c1_fp32_all_rows():
+    w = W.WORKLOADS["c1"]
+    qkv = W.make_qkv(w)
+    o, l = run_gpu(w, qkv)
+    check(w, o, l, all_heads(w), np.arange(w.N), qkv)
+
+
+def test_c2_full_causal():
+    w = W.WORKLOADS["c2"]
+    o, l = run_gpu(w)
+    check(w, o, l, some_heads(w, 16), W.sample_rows(w, 96))
+
+
+def test_c3_sliding_window():
+    w = W.WORKLOADS["c3"]
+    o, l = run_gpu(w)
+    rows = np.union1d(W.sample_rows(w, 48), np.array([4094, 4095, 4096, 4097, 8191, 8192]))
+    check(w, o, l, some_heads(w, 8), rows)
+
+
+def test_c4_long_context():
+    w = W.WORKLOADS["c4"]
+    o, l = run_gpu(w)
+    check(w, o, l, all_heads(w), W.sample_rows(w, 40))
+
+
+def test_c5_local_global():
+    w = W.WORKLOADS["c5"]
+    o, l = run_gpu(w)
+    rows = np.union1d(W.sample_rows(w, 64),
+                      np.array([2, 255, 256, 257, 2047, 2049, 2304, 2305, 16127, 16128, 16383]))
+    check(w, o, l, some_heads(w, 8), rows)
+
+
+def test_target_causal_32k():
+    w = W.WORKLOADS["tgt"]
+    o, l = run_gpu(w)
+    check(w, o, l, some_heads(w, 6), W.sample_rows(w, 48))
+
+
+def test_c5_alternative_global_reading():
+    """Globals counted from 1 ({0, 1, 2047, 4095, ...}): any index set works."""
+    g = tuple(sorted({0, 1} | set(range(2047, 16384, 2048))))
+    w = W.WORKLOADS["c5"].with_(name="c5alt", global_idx=g, B=1, H=4)
+    o, l = run_gpu(w)
+    check(w, o, l, all_heads(w), W.sample_rows(w, 64))
+
+
+# ---- invariants on the GPU ------------------------------------------------------------
+
+def test_constant_v():
+    w = W.random_workload("constv", 1, 4, 700, 128, causal=1, win_left=60, seed=3)
+    q, k, v = W.make_qkv(w)
+    c = W.round_to_bf16_bits(np.linspace(-2, 2, 128).astype(np.float32))
+    v = np.broadcast_to(c, v.shape).copy()
+    o, _ = run_gpu(w, (q, k, v))
+    want = W.bf16_bits_to_f32(c).astype(np.float64)
+    assert np.max(np.abs(host_f64(o) - want)) <= 1e-2
+
+
+def test_identical_keys():
+    w = W.random_workload("samek", 1, 2, 300, 64, causal=0, win_left=20, win_right=5,
+                          global_idx=(7,), seed=4)
+    q, k, v = W.make_qkv(w)
+    k = np.broadcast_to(k[:, :, :1], k.shape).copy()
+    o, l = run_gpu(w, (q, k, v))
+    check(w, o, l, all_heads(w), np.arange(300), (q, k, v))
+
+
+def test_window_covering_sequence_is_bitwise_causal():
+    base = W.random_workload("wcov", 1, 4, 1500, 128, causal=1, seed=8)
+    qkv = W.make_qkv(base)
+    o1, l1 = run_gpu(base, qkv)
+    for wl in (1499, 4096):
+        o2, l2 = run_gpu(base.with_(win_left=wl, win_right=0), qkv)
+        assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_deterministic():
+    w = W.random_workload("det", 2, 4, 2100, 64, causal=0, win_left=100, win_right=100,
+                          global_idx=(0, 1000), seed=9)
+    qkv = W.make_qkv(w)
+    o1, l1 = run_gpu(w, qkv)
+    o2, l2 = run_gpu(w, qkv)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_qkv_same_tensor():
+    """q = k = v passed as one device buffer (peaked diagonal)."""
+    w = W.random_workload("qkv", 1, 8, 1024, 64, causal=1, seed=10)
+    qkv = W.make_qkv(w)
+    o, l = run_gpu(w, qkv, same_tensor=True)
+    check(w, o, l, all_heads(w), np.arange(1024), (qkv[0], qkv[0], qkv[0]))
+
+
+def test_large_key_shift():
+    """Scores far beyond exp's fp32 range: the running max keeps them finite."""
+    w = W.random_workload("shift", 1, 2, 400, 64, causal=1, seed=11)
+    q, k, v = W.make_qkv(w)
+    kf = W.bf16_bits_to_f32(k) + np.float32(40.0)
+    k2 = W.round_to_bf16_bits(kf)
+    o, l = run_gpu(w, (q, k2, v))
+    check(w, o, l, all_heads(w), np.arange(400), (q, k2, v))
+
+
+# ---- boundary behaviour ------------------------------------------------------------------
+
+def test_stream_and_workspace():
+    import efficient_exact_attention_amd as ea
+    w = W.random_workload("ws", 2, 3, 1100, 128, causal=0, win_left=40, win_right=40,
+                          global_idx=(0, 500, 1099), seed=12)
+    qkv = W.make_qkv(w)
+    o1, l1 = run_gpu(w, qkv)
+    nbytes = ea.attn_workspace_bytes(w.B, w.H, w.N, w.d, len(w.global_idx))
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        o2, l2 = run_gpu(w, qkv, workspace=ws, stream=s)
+    s.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_errors_raise_before_launch():
+    import efficient_exact_attention_amd as ea
+    x = torch.zeros(1, 1, 64, 96, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ea.AttnError) as ei:
+        ea.fwd(x, x, x)
+    assert ei.value.status == ea.ATTN_ERR_UNSUPPORTED
+    y = torch.zeros(1, 1, 64, 64, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ea.AttnError):
+        ea.fwd(y, y, y, global_idx=[3, 3], win_left=2)
+    with pytest.raises(ea.AttnError):
+        ea.fwd(y, y, y, out=y)
+
+
+def test_long_context_memory_is_linear():
+    """c4 with free device memory cut to a few GiB: an N x N score buffer
+    (68.7 GB per head in fp32) could not be allocated, yet the call succeeds
+    and leaves free memory unchanged."""
+    import efficient_exact_attention_amd as ea
+    w = W.WORKLOADS["c4"]
+    assert ea.attn_workspace_bytes(w.B, w.H, w.N, w.d, 0) == 0
+    qkv = W.make_qkv(w)
+    q, k, v = (to_device(x, w.dtype) for x in qkv)
+    out = torch.empty_like(q)
+    lse = torch.empty(w.B, w.H, w.N, dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    free, total = torch.cuda.mem_get_info()
+    hog = torch.empty(max(0, free - (6 << 30)), dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    free0, _ = torch.cuda.mem_get_info()
+    say(f"  free device memory during the call: {free0 / 2**30:.2f} GiB of {total / 2**30:.0f}")
+    assert free0 < 8 << 30
+    ea.fwd(q, k, v, causal=1, out=out, lse=lse)
+    torch.cuda.synchronize()
+    free1, _ = torch.cuda.mem_get_info()
+    del hog
+    assert abs(free1 - free0) < (64 << 20)
+    rows = np.array([0, 1, 65535, w.N - 1])
+    ref_o, ref_l = oracle_heads(w, [(0, 3)], rows)
+    e = errors(host_f64(out[0, 3, rows])[None], host_f64(lse[0, 3, rows])[None], ref_o, ref_l)
+    assert e[0] <= 1e-2 and e[2] <= 1e-3
