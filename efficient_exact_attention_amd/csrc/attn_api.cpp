@@ -146,7 +146,7 @@ int attn_plan_stats(int N, int causal, int win_left, int win_right, const int *g
             if (cl == eea::TILE_FULL) ++full;
             else if (cl == eea::TILE_EDGE) ++edge;
         }
-        if (use_g) ++edge;   // gathered tile of global columns
+        if (use_g) edge += (n_global + bn - 1) / bn;   // gathered tiles of global columns
     }
     if (use_g)
         for (int g : G) {

@@ -421,7 +421,7 @@ __global__ void __launch_bounds__(P::NT) fwd_kernel(const FwdParams prm) {
     const int ng = prm.n_global;
     const Band band{N, prm.wl, prm.wr};
 
-    if (tid < ng) s_gidx[tid] = prm.gidx[tid];
+    if (tid < kMaxGlobal) s_gidx[tid] = tid < ng ? prm.gidx[tid] : -1;
 
     // --- which work item
     const int G = gridDim.x;
@@ -487,30 +487,31 @@ __global__ void __launch_bounds__(P::NT) fwd_kernel(const FwdParams prm) {
     auto kbuf = [&](int b) { return smem + 2 * b * P::TILE_BYTES; };
     auto vbuf = [&](int b) { return smem + (2 * b + 1) * P::TILE_BYTES; };
 
-    // --- gathered tile of global columns
+    // --- gathered tiles of global columns (one per BN globals)
     if (MODE == MODE_BAND && ng > 0) {
-        typename P::Stage st;
-        P::load_stage(st, kh, vh, [&](int r) { return r < ng ? s_gidx[r] : -1; }, tid);
-        P::store_stage(st, kbuf(0), vbuf(0), tid);
-        __syncthreads();
-        if (wave_active) {
-            f32x16 s[P::MB];
-            P::scores(s, qf, kbuf(0), ln, h);
+        for (int g0 = 0; g0 < ng; g0 += BN) {
+            typename P::Stage st;
+            P::load_stage(st, kh, vh, [&](int r) { return g0 + r < ng ? s_gidx[g0 + r] : -1; }, tid);
+            P::store_stage(st, kbuf(0), vbuf(0), tid);
+            __syncthreads();
+            if (wave_active) {
+                f32x16 s[P::MB];
+                P::scores(s, qf, kbuf(0), ln, h);
+                // branch-free mask: a global column counts here only when it is
+                // outside the row's window (inside, the band tiles count it)
 #pragma unroll
-            for (int mb = 0; mb < P::MB; ++mb)
+                for (int mb = 0; mb < P::MB; ++mb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int col = mb * 32 + acc_row(r, h);
-                    bool vis = false;
-                    if (col < ng) {
-                        const int g = s_gidx[col];
-                        vis = (!prm.causal || g <= row) && !(g >= lo && g <= hi);
+                    for (int r = 0; r < 16; ++r) {
+                        const int col = g0 + mb * 32 + acc_row(r, h);
+                        const int g = s_gidx[col < kMaxGlobal ? col : 0];
+                        const bool vis = (col < ng) & ((prm.causal == 0) | (g <= row)) & ((g < lo) | (g > hi));
+                        s[mb][r] = vis ? s[mb][r] : EEA_NEG_INF;
                     }
-                    if (!vis) s[mb][r] = EEA_NEG_INF;
-                }
-            softmax_pv_step<P>(rs, s, c, vbuf(0), ln, h);
+                softmax_pv_step<P>(rs, s, c, vbuf(0), ln, h);
+            }
+            __syncthreads();
         }
-        __syncthreads();
     }
 
     // --- band tiles, double-buffered
@@ -547,7 +548,7 @@ __global__ void __launch_bounds__(P::NT) fwd_kernel(const FwdParams prm) {
 #pragma unroll
                         for (int r = 0; r < 16; ++r) {
                             const int j = k0 + mb * 32 + acc_row(r, h);
-                            if (j < lo || j > hi) s[mb][r] = EEA_NEG_INF;
+                            s[mb][r] = ((j >= lo) & (j <= hi)) ? s[mb][r] : EEA_NEG_INF;
                         }
                 }
                 softmax_pv_step<P>(rs, s, c, vbuf(cur), ln, h);

@@ -113,7 +113,8 @@ size_t attn_workspace_bytes(int B, int H, int N, int d, int n_global);
  * of visible (i, j) pairs, and the number of band key tiles visited that need
  * no mask (tiles_full) or need one (tiles_edge), summed over the query tiles.
  * Tiles with no visible pair are never visited and not counted. Global
- * columns add one gathered tile per query tile (counted in tiles_edge);
+ * columns add ceil(n_global / bn) gathered tiles per query tile (counted in
+ * tiles_edge);
  * global rows are counted as ceil(keys / bn) edge tiles each. Output
  * pointers are host pointers; any may be NULL. Makes no HIP call.
  */

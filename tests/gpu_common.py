@@ -12,6 +12,10 @@ from efficient_exact_attention_amd import workloads as W
 
 # Pass criteria (all configurations): max-abs and relative L2 over every checked
 # output element, max-abs over checked LSE values; compared in fp64.
+# A bf16 output cannot hold a value of magnitude >= 2.56 to within 1e-2 (half
+# an ulp there exceeds 1e-2: 1.56e-2 in [4, 8)), so for bf16 outputs each
+# element's max-abs bound is 1e-2 plus half a bf16 ulp of the exact value
+# (at most |O| * 2^-8). Only peaked rows with large outputs ever use it.
 TOL_MAXABS = 1e-2
 TOL_RELL2 = 5e-3
 TOL_LSE = 1e-3
@@ -72,9 +76,12 @@ def oracle_heads(w: W.Workload, heads, rows, qkv=None):
     return np.stack(outs), np.stack(lses)
 
 
-def errors(got_o, got_l, ref_o, ref_l):
+def errors(got_o, got_l, ref_o, ref_l, bf16_out=False):
+    """(max-abs excess over the bf16 output's own rounding, rel-L2, LSE max-abs).
+    For fp32 outputs the first value is the plain max-abs error."""
     diff = got_o - ref_o
-    maxabs = float(np.max(np.abs(diff)))
+    widen = np.abs(ref_o) * 2.0 ** -8 if bf16_out else 0.0
+    maxabs = float(np.max(np.abs(diff) - widen))
     rel = float(np.linalg.norm(diff) / max(np.linalg.norm(ref_o), 1e-300))
     lse = float(np.max(np.abs(got_l - ref_l)))
     return maxabs, rel, lse
@@ -85,9 +92,10 @@ def check(w: W.Workload, o, l, heads, rows, qkv=None, tol=(TOL_MAXABS, TOL_RELL2
     go = np.stack([host_f64(o[b, h, rows]) for (b, h) in heads])
     gl = np.stack([host_f64(l[b, h, rows]) for (b, h) in heads])
     assert np.all(np.isfinite(go)) and np.all(np.isfinite(gl)), "non-finite output"
-    e = errors(go, gl, ref_o, ref_l)
-    say(f"    {w.name}: max-abs {e[0]:.3e}  rel-L2 {e[1]:.3e}  lse {e[2]:.3e}  "
-        f"({len(heads)} heads x {len(rows)} rows)")
+    e = errors(go, gl, ref_o, ref_l, bf16_out=w.dtype == "bf16")
+    raw = float(np.max(np.abs(go - ref_o)))
+    say(f"    {w.name}: max-abs {raw:.3e} (beyond bf16 output rounding {e[0]:.3e})  "
+        f"rel-L2 {e[1]:.3e}  lse {e[2]:.3e}  ({len(heads)} heads x {len(rows)} rows)")
     assert e[0] <= tol[0], e
     assert e[1] <= tol[1], e
     assert e[2] <= tol[2], e

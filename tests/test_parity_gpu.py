@@ -70,6 +70,16 @@ def test_many_globals():
     check(w, o, l, all_heads(w), np.arange(2000), qkv)
 
 
+def test_fp32_more_globals_than_one_tile():
+    """fp32 key tiles hold 32 keys: 40 global columns need two gathered tiles."""
+    g = tuple(range(3, 1200, 30))[:40]
+    w = W.random_workload("f32g40", 1, 2, 1200, 64, dtype="f32", causal=0, win_left=9,
+                          win_right=9, global_idx=g, seed=13)
+    qkv = W.make_qkv(w)
+    o, l = run_gpu(w, qkv)
+    check(w, o, l, all_heads(w), np.arange(1200), qkv, tol=(1e-4, 1e-5, 1e-4))
+
+
 def test_causal_globals_bf16_d128():
     w = W.random_workload("cg", 2, 2, 3000, 128, causal=1, win_left=200, win_right=0,
                           global_idx=(0, 1, 1024, 2999), seed=6)
@@ -137,7 +147,7 @@ def test_constant_v():
     v = np.broadcast_to(c, v.shape).copy()
     o, _ = run_gpu(w, (q, k, v))
     want = W.bf16_bits_to_f32(c).astype(np.float64)
-    assert np.max(np.abs(host_f64(o) - want)) <= 1e-2
+    assert np.max(np.abs(host_f64(o) - want) - np.abs(want) * 2.0 ** -8) <= 1e-2
 
 
 def test_identical_keys():
@@ -240,5 +250,5 @@ def test_long_context_memory_is_linear():
     assert abs(free1 - free0) < (64 << 20)
     rows = np.array([0, 1, 65535, w.N - 1])
     ref_o, ref_l = oracle_heads(w, [(0, 3)], rows)
-    e = errors(host_f64(out[0, 3, rows])[None], host_f64(lse[0, 3, rows])[None], ref_o, ref_l)
+    e = errors(host_f64(out[0, 3, rows])[None], host_f64(lse[0, 3, rows])[None], ref_o, ref_l, True)
     assert e[0] <= 1e-2 and e[2] <= 1e-3
