@@ -10,23 +10,25 @@
 // are paid for, and block patterns map onto tiles).
 //
 // Layout of the work on gfx950 (our design, not the pages'):
-//  * One workgroup = 4 wave64s = 128 query rows; each wave owns 32 rows.
+//  * bf16: one workgroup = 8 wave64s = 256 query rows (two waves per SIMD, so
+//    one wave's softmax arithmetic overlaps the other's matrix-core work);
+//    each wave owns 32 rows.
 //  * Scores are computed transposed, S^T = K Q^T, with
 //    v_mfma_f32_32x32x16_bf16: K rows are the A operand (from LDS), the
 //    wave's 32 queries are the B operand (kept in registers for the whole
 //    kernel). In the 32x32 accumulator layout a lane then holds ONE query and
 //    16 keys, so the row max and row sum are in-lane reductions plus a single
-//    exchange between the two half-waves.
+//    exchange between the two half-waves (v_permlane32_swap).
 //  * The output is accumulated transposed, O^T += V^T P^T, so the fp32
 //    accumulators of a lane also belong to its one query: the online-softmax
 //    rescale is a per-lane scalar multiply. The exponentiated scores, rounded
-//    to bf16, are already in the B-operand layout of this product; the key
-//    order inside each 16-key step is permuted to match, and V^T is stored in
-//    LDS in that permuted order.
-//  * K and V^T tiles are double-buffered in LDS: the next tile's global loads
-//    are issued before the current tile's matrix work and written to the
-//    other buffer after it, one barrier per tile. 16-byte LDS chunks are XOR
-//    swizzled so the MFMA operand reads are free of bank conflicts.
+//    to bf16, are already in the B-operand layout of this product.
+//  * K and V tiles go straight from HBM into LDS (global_load_lds_dwordx4,
+//    no register staging), double-buffered, one barrier per tile. Each lane
+//    fetches the 16-byte chunk that lands at its LDS slot, so the XOR
+//    swizzle of chunks within a row is applied on the global side. K is read
+//    with ds_read_b128; V^T operands are produced by the LDS transpose read
+//    ds_read_b64_tr_b16 straight from row-major V.
 //  * Softmax runs in the exp2 domain with scale*log2(e) folded into one FMA.
 //    The running max is only moved (and the accumulators rescaled) when it
 //    grows by more than 2^8; otherwise the stale max keeps every weight below
@@ -34,13 +36,14 @@
 //  * Work items are ordered heaviest-first for causal masks, and consecutive
 //    work items are grouped onto one XCD so the workgroups that share a
 //    head's K/V stream share that XCD's L2.
-//  * fp32 inputs use v_mfma_f32_32x32x2_f32 with the same transposed scheme.
+//  * fp32 inputs use v_mfma_f32_32x32x2_f32 with the same transposed scheme
+//    and register-staged tile loads.
 //
-// Global tokens: global COLUMNS are gathered into one extra key tile per
-// query tile (masked where the column already lies in the row's window);
-// global ROWS see every key, so they are computed by a split-key pass that
-// writes partial (o, m, l) per key chunk and a merge kernel that combines
-// them with the same rescaling identity the online softmax uses.
+// Global tokens: global COLUMNS are gathered into extra key tiles per query
+// tile (masked where the column already lies in the row's window); global
+// ROWS see every key, so they are computed by a split-key pass that writes
+// partial (o, m, l) per key chunk and a merge kernel that combines them with
+// the same rescaling identity the online softmax uses.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -50,18 +53,21 @@
 namespace eea {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((ext_vector_type(8))) short s16x8;
 typedef __attribute__((ext_vector_type(8))) float f32x8;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
-typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
+
+#define EEA_LDS __attribute__((address_space(3)))
 
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleLog2 = 8.0f;
 #define EEA_NEG_INF (-__builtin_huge_valf())
 
 enum { MODE_BAND = 0, MODE_GROWS = 1 };
-enum { KIND_FULL = 0, KIND_EDGE = 1, KIND_GATHER = 2 };
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -69,37 +75,82 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // half-wave h, for the 32x32 MFMA output layout.
 __device__ __forceinline__ int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
 
+// s_waitcnt with vmcnt(0) and the other counters left alone (gfx9 encoding:
+// vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt_hi[15:14]).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Source rows of one key tile: keys k0.. for a band tile, or the global
+// positions g[k0..] for a gathered tile. Returns -1 for a row with no key.
+struct TileSrc {
+    int k0;
+    int gather;     // 0: band tile at key k0; 1: gathered tile from global slot k0
+    int N;
+    int ng;
+    const int *g;   // LDS copy of the sorted global positions
+    __device__ __forceinline__ int key(int r) const {
+        if (gather) return k0 + r < ng ? g[k0 + r] : -1;
+        return k0 + r < N ? k0 + r : -1;
+    }
+};
+
 // ---------------------------------------------------------------------------
-// bf16 inputs: QK^T and PV on v_mfma_f32_32x32x16_bf16.
+// bf16 inputs: QK^T and PV on v_mfma_f32_32x32x16_bf16; tiles loaded
+// global -> LDS directly, V operands through the LDS transpose read.
 // ---------------------------------------------------------------------------
-template <int D_, int BN_, int NT_>
+template <int D_, int NT_>
 struct Bf16Path {
-    static constexpr int D = D_, BN = BN_, NT = NT_;
+    static constexpr int D = D_, BN = 64, NT = NT_, NW = NT / 64;
     static constexpr bool F32 = false;
     static constexpr int KS = D / 16;     // k-steps of QK^T
     static constexpr int MB = BN / 32;    // 32-key blocks per tile
     static constexpr int DB = D / 32;     // 32-wide blocks of d in O^T
     static constexpr int PVS = BN / 16;   // 16-key steps of PV
-    static constexpr int KROW = D * 2;    // bytes per K row in LDS
-    static constexpr int VROW = BN * 2;   // bytes per V^T row in LDS
-    static constexpr int TILE_BYTES = BN * D * 2;
-    static constexpr int K_CHUNKS = BN * D / 8;
-    static constexpr int K_PER_T = (K_CHUNKS + NT - 1) / NT;
-    static constexpr int V_BLOCKS = (BN / 4) * (D / 8);   // 4 keys x 8 d
-    static constexpr int V_PER_T = (V_BLOCKS + NT - 1) / NT;
-    static constexpr int LDS_BYTES = 4 * TILE_BYTES;     // K, V^T, two buffers each
-    static_assert(D % 64 == 0 && BN % 64 == 0, "tile shape");
+    static constexpr int ROWB = D * 2;    // bytes per K or V row
+    static constexpr int TILE_BYTES = BN * ROWB;
+    static constexpr int SEGS = TILE_BYTES / 1024;   // one wave-wide 16-byte load = 1 KiB
+    static constexpr int SPW = SEGS / NW;            // loads per wave per tile (each of K, V)
+    static constexpr int LDS_BYTES = 4 * TILE_BYTES; // K and V, two buffers each
+    static_assert(SEGS % NW == 0, "tile loads must split evenly over the waves");
+    static_assert(D == 64 || D == 128, "head size");
 
     typedef uint16_t elem_t;
     struct QFrag { bf16x8 x[KS]; };
-    struct Stage { u32x4 k[K_PER_T]; u32x4 v[V_PER_T][4]; };
     struct PFrag { bf16x8 x[PVS]; };
+    struct Stage {};
 
-    static __device__ __forceinline__ int k_off(int row, int chunk) {
-        return row * KROW + ((chunk ^ (row & 7)) << 4);
-    }
-    static __device__ __forceinline__ int v_off(int d, int chunk) {
-        return d * VROW + ((chunk ^ ((d ^ (d >> 3)) & 7)) << 4);
+    // Per-lane constants, computed once.
+    struct Lane {
+        int krd[4];        // K operand: byte offset in a K tile for (mb=0, ks&3)
+        int vrd[2];        // V operand: byte offset in a V tile for (st=0, db&1)
+        int ldrow[SPW];    // tile row this lane fetches in load i
+        int ldcol[SPW];    // element offset of its 16-byte chunk within that row
+        int ldlds[SPW];    // LDS byte offset (within a tile) of this wave's load i
+    };
+
+    static __device__ __forceinline__ void init_lane(Lane &L, int lane, int wave) {
+        const int ln = lane & 31, h = lane >> 5, x = ln & 7;
+        // K row ln, logical chunk 2ks + h, stored at chunk (2ks + h) ^ (ln & 7)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            L.krd[q] = ln * ROWB + 16 * (2 * (q ^ (x >> 1)) + (h ^ (x & 1)));
+        // transpose read: lane j of 16-lane group g loads 4 elements of key
+        // row 4h + j/4 at d = 16(g&1) + 4(j&3); lane i of the group then holds
+        // d = 16(g&1) + i for the keys 4h + e, e = 0..3
+        const int g = lane >> 4, j = lane & 15;
+        const int krow = 4 * h + (j >> 2);
+        const int y = krow & 7;
+        const int t = 2 * (g & 1) + ((j >> 1) & 1);
+#pragma unroll
+        for (int p = 0; p < 2; ++p)
+            L.vrd[p] = krow * ROWB + 16 * ((4 * p + t) ^ y) + 8 * (j & 1);
+#pragma unroll
+        for (int i = 0; i < SPW; ++i) {
+            const int o = (wave * SPW + i) * 1024 + lane * 16;
+            const int row = o / ROWB, phys = (o % ROWB) / 16;
+            L.ldrow[i] = row;
+            L.ldcol[i] = (phys ^ (row & 7)) * 8;
+            L.ldlds[i] = (wave * SPW + i) * 1024;
+        }
     }
 
     static __device__ __forceinline__ void load_q(QFrag &qf, const elem_t *qh, int row, bool valid, int h) {
@@ -111,86 +162,31 @@ struct Bf16Path {
         }
     }
 
-    // Global -> registers for one key tile. key_of(row) gives the source key
-    // of tile row `row`, or -1 for a zero row.
-    template <class KeyOf>
-    static __device__ __forceinline__ void load_stage(Stage &st, const elem_t *kh, const elem_t *vh,
-                                                      KeyOf key_of, int tid) {
+    // Start the global -> LDS copy of one K tile and one V tile. Rows with no
+    // key fetch row `fallback` (a valid row); the caller masks them.
+    static __device__ __forceinline__ void issue(Stage &, const Lane &L, const elem_t *kh, const elem_t *vh,
+                                                 char *kbuf, char *vbuf, const TileSrc &src, int fallback) {
 #pragma unroll
-        for (int i = 0; i < K_PER_T; ++i) {
-            int c = tid + i * NT;
-            st.k[i] = u32x4{0, 0, 0, 0};
-            if (c < K_CHUNKS) {
-                int row = c / (D / 8), ch = c % (D / 8);
-                int key = key_of(row);
-                if (key >= 0)
-                    st.k[i] = *reinterpret_cast<const u32x4 *>(kh + (long long)key * D + ch * 8);
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < V_PER_T; ++i) {
-            int b = tid + i * NT;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) st.v[i][r] = u32x4{0, 0, 0, 0};
-            if (b < V_BLOCKS) {
-                int kg = b / (D / 8), dc = b % (D / 8);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    int key = key_of(4 * kg + r);
-                    if (key >= 0)
-                        st.v[i][r] = *reinterpret_cast<const u32x4 *>(vh + (long long)key * D + dc * 8);
-                }
-            }
+        for (int i = 0; i < SPW; ++i) {
+            int key = src.key(L.ldrow[i]);
+            key = key < 0 ? fallback : key;
+            const long long off = (long long)key * D + L.ldcol[i];
+            __builtin_amdgcn_global_load_lds(kh + off, (EEA_LDS void *)(kbuf + L.ldlds[i]), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(vh + off, (EEA_LDS void *)(vbuf + L.ldlds[i]), 16, 0, 0);
         }
     }
 
-    // Registers -> LDS. K rows go in as they are (swizzled 16-byte chunks);
-    // each 4-key x 8-d block of V is transposed in registers and written as
-    // eight 8-byte runs of V^T, in the permuted key order of the PV operand.
-    static __device__ __forceinline__ void store_stage(const Stage &st, char *kbuf, char *vbuf, int tid) {
-#pragma unroll
-        for (int i = 0; i < K_PER_T; ++i) {
-            int c = tid + i * NT;
-            if (c < K_CHUNKS) {
-                int row = c / (D / 8), ch = c % (D / 8);
-                *reinterpret_cast<u32x4 *>(kbuf + k_off(row, ch)) = st.k[i];
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < V_PER_T; ++i) {
-            int b = tid + i * NT;
-            if (b < V_BLOCKS) {
-                int kg = b / (D / 8), dc = b % (D / 8);
-                int ko = 4 * kg;
-                int in16 = ko & 15;
-                int pos = (ko & ~15) | ((in16 & 4) << 1) | ((in16 & 8) >> 1);
-                int chunk = pos >> 3, within = (pos & 7) * 2;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    int p = e >> 1;
-                    unsigned w0, w1;
-                    if (e & 1) {
-                        w0 = (st.v[i][0][p] >> 16) | (st.v[i][1][p] & 0xffff0000u);
-                        w1 = (st.v[i][2][p] >> 16) | (st.v[i][3][p] & 0xffff0000u);
-                    } else {
-                        w0 = (st.v[i][0][p] & 0xffffu) | (st.v[i][1][p] << 16);
-                        w1 = (st.v[i][2][p] & 0xffffu) | (st.v[i][3][p] << 16);
-                    }
-                    int d = dc * 8 + e;
-                    *reinterpret_cast<u32x2 *>(vbuf + v_off(d, chunk) + within) = u32x2{w0, w1};
-                }
-            }
-        }
-    }
+    static __device__ __forceinline__ void finish(Stage &, char *, char *, int) { wait_vmem(); }
 
-    static __device__ __forceinline__ void scores(f32x16 (&s)[MB], const QFrag &qf, const char *kbuf,
-                                                  int ln, int h) {
+    static __device__ __forceinline__ void scores(f32x16 (&s)[MB], const QFrag &qf, const Lane &L,
+                                                  const char *kbuf) {
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
             f32x16 acc = {};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                bf16x8 a = *reinterpret_cast<const bf16x8 *>(kbuf + k_off(mb * 32 + ln, 2 * ks + h));
+                const char *p = kbuf + L.krd[ks & 3] + mb * 32 * ROWB + 128 * (ks >> 2);
+                bf16x8 a = *reinterpret_cast<const bf16x8 *>(p);
                 acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf.x[ks], acc, 0, 0, 0);
             }
             s[mb] = acc;
@@ -207,13 +203,21 @@ struct Bf16Path {
         }
     }
 
-    static __device__ __forceinline__ void pv(f32x16 (&o)[DB], const PFrag &pf, const char *vbuf,
-                                              int ln, int h) {
+    static __device__ __forceinline__ bf16x8 v_operand(const Lane &L, const char *vbuf, int db, int st) {
+        const char *p = vbuf + L.vrd[db & 1] + 128 * (db >> 1) + 16 * st * ROWB;
+        s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((EEA_LDS s16x4 *)(p));
+        s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((EEA_LDS s16x4 *)(p + 8 * ROWB));
+        s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        return __builtin_bit_cast(bf16x8, v);
+    }
+
+    static __device__ __forceinline__ void pv(f32x16 (&o)[DB], const PFrag &pf, const Lane &L,
+                                              const char *vbuf) {
 #pragma unroll
         for (int st = 0; st < PVS; ++st) {
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
-                bf16x8 a = *reinterpret_cast<const bf16x8 *>(vbuf + v_off(db * 32 + ln, 2 * st + h));
+                bf16x8 a = v_operand(L, vbuf, db, st);
                 o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf.x[st], o[db], 0, 0, 0);
             }
         }
@@ -228,7 +232,6 @@ struct Bf16Path {
             for (int g = 0; g < 4; ++g) {
                 f32x4 x = {o[db][4 * g + 0] * inv, o[db][4 * g + 1] * inv,
                            o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv};
-                typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
                 bf16x4 y = __builtin_convertvector(x, bf16x4);
                 *reinterpret_cast<bf16x4 *>(dst + db * 32 + 8 * g + 4 * h) = y;
             }
@@ -239,10 +242,12 @@ struct Bf16Path {
 // ---------------------------------------------------------------------------
 // fp32 inputs: both products on v_mfma_f32_32x32x2_f32 (true fp32 products).
 // The contraction index of QK^T is split between half-waves as d = h*D/2 + s.
+// Tiles are staged through registers (global loads issued before the
+// current tile's work, written to LDS after it).
 // ---------------------------------------------------------------------------
-template <int D_, int BN_, int NT_>
+template <int D_, int NT_>
 struct F32Path {
-    static constexpr int D = D_, BN = BN_, NT = NT_;
+    static constexpr int D = D_, BN = 32, NT = NT_;
     static constexpr bool F32 = true;
     static constexpr int KS = D / 2;
     static constexpr int MB = BN / 32;
@@ -253,12 +258,18 @@ struct F32Path {
     static constexpr int CHUNKS = BN * CH;
     static constexpr int PER_T = (CHUNKS + NT - 1) / NT;
     static constexpr int LDS_BYTES = 4 * TILE_BYTES;
-    static_assert(D % 32 == 0 && BN % 32 == 0, "tile shape");
 
     typedef float elem_t;
     struct QFrag { float x[KS]; };
     struct Stage { u32x4 k[PER_T]; u32x4 v[PER_T]; };
     struct PFrag { float x[MB][16]; };
+    struct Lane { int ln, h, tid; };
+
+    static __device__ __forceinline__ void init_lane(Lane &L, int lane, int wave) {
+        L.ln = lane & 31;
+        L.h = lane >> 5;
+        L.tid = wave * 64 + lane;
+    }
 
     static __device__ __forceinline__ int k_off(int row, int chunk) {
         return row * ROW + ((chunk ^ (row & 7)) << 4);
@@ -274,17 +285,16 @@ struct F32Path {
         }
     }
 
-    template <class KeyOf>
-    static __device__ __forceinline__ void load_stage(Stage &st, const elem_t *kh, const elem_t *vh,
-                                                      KeyOf key_of, int tid) {
+    static __device__ __forceinline__ void issue(Stage &st, const Lane &L, const elem_t *kh, const elem_t *vh,
+                                                 char *, char *, const TileSrc &src, int) {
 #pragma unroll
         for (int i = 0; i < PER_T; ++i) {
-            int c = tid + i * NT;
+            int c = L.tid + i * NT;
             st.k[i] = u32x4{0, 0, 0, 0};
             st.v[i] = u32x4{0, 0, 0, 0};
             if (c < CHUNKS) {
                 int row = c / CH, ch = c % CH;
-                int key = key_of(row);
+                int key = src.key(row);
                 if (key >= 0) {
                     st.k[i] = *reinterpret_cast<const u32x4 *>(kh + (long long)key * D + ch * 4);
                     st.v[i] = *reinterpret_cast<const u32x4 *>(vh + (long long)key * D + ch * 4);
@@ -293,7 +303,7 @@ struct F32Path {
         }
     }
 
-    static __device__ __forceinline__ void store_stage(const Stage &st, char *kbuf, char *vbuf, int tid) {
+    static __device__ __forceinline__ void finish(const Stage &st, char *kbuf, char *vbuf, int tid) {
 #pragma unroll
         for (int i = 0; i < PER_T; ++i) {
             int c = tid + i * NT;
@@ -305,14 +315,14 @@ struct F32Path {
         }
     }
 
-    static __device__ __forceinline__ void scores(f32x16 (&s)[MB], const QFrag &qf, const char *kbuf,
-                                                  int ln, int h) {
+    static __device__ __forceinline__ void scores(f32x16 (&s)[MB], const QFrag &qf, const Lane &L,
+                                                  const char *kbuf) {
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
             f32x16 acc = {};
 #pragma unroll
             for (int c = 0; c < D / 8; ++c) {
-                f32x4 a = *reinterpret_cast<const f32x4 *>(kbuf + k_off(mb * 32 + ln, h * (D / 8) + c));
+                f32x4 a = *reinterpret_cast<const f32x4 *>(kbuf + k_off(mb * 32 + L.ln, L.h * (D / 8) + c));
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
                     acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[e], qf.x[4 * c + e], acc, 0, 0, 0);
@@ -328,16 +338,16 @@ struct F32Path {
             for (int r = 0; r < 16; ++r) pf.x[mb][r] = s[mb][r];
     }
 
-    static __device__ __forceinline__ void pv(f32x16 (&o)[DB], const PFrag &pf, const char *vbuf,
-                                              int ln, int h) {
+    static __device__ __forceinline__ void pv(f32x16 (&o)[DB], const PFrag &pf, const Lane &L,
+                                              const char *vbuf) {
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int key = mb * 32 + acc_row(r, h);
+                const int key = mb * 32 + acc_row(r, L.h);
 #pragma unroll
                 for (int db = 0; db < DB; ++db) {
-                    float a = *reinterpret_cast<const float *>(vbuf + key * ROW + (db * 32 + ln) * 4);
+                    float a = *reinterpret_cast<const float *>(vbuf + key * ROW + (db * 32 + L.ln) * 4);
                     o[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, pf.x[mb][r], o[db], 0, 0, 0);
                 }
             }
@@ -367,15 +377,26 @@ struct RowState {
     f32x16 o[P::DB];
 };
 
+// Lane l and lane l^32 hold the same query row: combine their values.
+__device__ __forceinline__ float max_across_halves(float x) {
+    auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+}
+
+__device__ __forceinline__ float sum_across_halves(float x) {
+    auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+}
+
 template <class P>
 __device__ __forceinline__ void softmax_pv_step(RowState<P> &rs, f32x16 (&s)[P::MB], float c,
-                                                const char *vbuf, int ln, int h) {
+                                                const typename P::Lane &L, const char *vbuf) {
     float mx = EEA_NEG_INF;
 #pragma unroll
     for (int mb = 0; mb < P::MB; ++mb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mb][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    mx = max_across_halves(mx);
     const float mnew = fmaxf(rs.m, mx * c);
     const bool need = mnew > rs.m + kRescaleLog2;
     if (__any(need)) {
@@ -398,7 +419,7 @@ __device__ __forceinline__ void softmax_pv_step(RowState<P> &rs, f32x16 (&s)[P::
     rs.lpart += sum;
     typename P::PFrag pf;
     P::pack_p(pf, s);
-    P::pv(rs.o, pf, vbuf, ln, h);
+    P::pv(rs.o, pf, L, vbuf);
 }
 
 // ---------------------------------------------------------------------------
@@ -412,7 +433,10 @@ __global__ void __launch_bounds__(P::NT) fwd_kernel(const FwdParams prm) {
     constexpr int BM = 32 * (NT / 64);
     typedef typename P::elem_t elem_t;
 
-    __shared__ __attribute__((aligned(16))) char smem[P::LDS_BYTES];
+    // Two LDS buffers (K tile then V tile each) as distinct objects, so that
+    // reads of one are never made to wait for the DMA into the other.
+    __shared__ __attribute__((aligned(1024))) char smem0[P::LDS_BYTES / 2];
+    __shared__ __attribute__((aligned(1024))) char smem1[P::LDS_BYTES / 2];
     __shared__ int s_gidx[kMaxGlobal];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -426,24 +450,27 @@ __global__ void __launch_bounds__(P::NT) fwd_kernel(const FwdParams prm) {
     // --- which work item
     const int G = gridDim.x;
     const int bid = blockIdx.x;
-    const int L = prm.xcd_remap ? (bid & 7) * (G >> 3) + (bid >> 3) : bid;
+    const int Lw = prm.xcd_remap ? (bid & 7) * (G >> 3) + (bid >> 3) : bid;
     int bh, unit;
     if (MODE == MODE_BAND) {
-        bh = L / prm.num_qt;
-        const int qi = L - bh * prm.num_qt;
+        bh = Lw / prm.num_qt;
+        const int qi = Lw - bh * prm.num_qt;
         unit = prm.causal ? prm.num_qt - 1 - qi : qi;
     } else {
-        bh = L / prm.chunks;
-        unit = L - bh * prm.chunks;
+        bh = Lw / prm.chunks;
+        unit = Lw - bh * prm.chunks;
     }
     const elem_t *qh = static_cast<const elem_t *>(prm.q) + (long long)bh * prm.head_stride;
     const elem_t *kh = static_cast<const elem_t *>(prm.k) + (long long)bh * prm.head_stride;
     const elem_t *vh = static_cast<const elem_t *>(prm.v) + (long long)bh * prm.head_stride;
 
+    typename P::Lane L;
+    P::init_lane(L, lane, wave);
+
     __syncthreads();   // s_gidx visible
 
     // --- this lane's query row and its visible key interval [lo, hi]
-    int row, lo, hi, kt_lo, kt_hi, wave_lo, wave_hi;
+    int row, lo, hi, kt_lo, kt_hi, wave_hi;
     bool valid, wave_active;
     int wr0 = 0, wr1 = 0;
     if (MODE == MODE_BAND) {
@@ -456,8 +483,7 @@ __global__ void __launch_bounds__(P::NT) fwd_kernel(const FwdParams prm) {
         wr1 = imin(N - 1, wr0 + 31);
         wave_active = wr0 < N;
         key_tile_range(band, q0, imin(N - 1, q0 + BM - 1), BN, &kt_lo, &kt_hi);
-        wave_lo = row_lo(band, wr0);
-        wave_hi = row_hi(band, wr1);
+        wave_hi = 0;
     } else {
         const int t = wave * 32 + ln;
         valid = t < ng;
@@ -469,7 +495,6 @@ __global__ void __launch_bounds__(P::NT) fwd_kernel(const FwdParams prm) {
         kt_lo = unit * prm.chunk_tiles;
         kt_hi = imin(num_kt - 1, kt_lo + prm.chunk_tiles - 1);
         if (prm.causal) kt_hi = imin(kt_hi, s_gidx[ng - 1] / BN);
-        wave_lo = 0;
         wave_hi = wave_active ? (prm.causal ? s_gidx[imin(ng - 1, wave * 32 + 31)] : N - 1) : -1;
     }
 
@@ -483,20 +508,20 @@ __global__ void __launch_bounds__(P::NT) fwd_kernel(const FwdParams prm) {
     for (int db = 0; db < P::DB; ++db) rs.o[db] = f32x16{};
 
     const float c = prm.scale_log2;
-    // buffer b: K at smem + 2*b*TILE, V^T right after it
-    auto kbuf = [&](int b) { return smem + 2 * b * P::TILE_BYTES; };
-    auto vbuf = [&](int b) { return smem + (2 * b + 1) * P::TILE_BYTES; };
+    char *const k0buf = smem0, *const v0buf = smem0 + P::TILE_BYTES;
+    char *const k1buf = smem1, *const v1buf = smem1 + P::TILE_BYTES;
 
     // --- gathered tiles of global columns (one per BN globals)
     if (MODE == MODE_BAND && ng > 0) {
         for (int g0 = 0; g0 < ng; g0 += BN) {
             typename P::Stage st;
-            P::load_stage(st, kh, vh, [&](int r) { return g0 + r < ng ? s_gidx[g0 + r] : -1; }, tid);
-            P::store_stage(st, kbuf(0), vbuf(0), tid);
+            const TileSrc src{g0, 1, N, ng, s_gidx};
+            P::issue(st, L, kh, vh, k0buf, v0buf, src, s_gidx[0]);
+            P::finish(st, k0buf, v0buf, tid);
             __syncthreads();
             if (wave_active) {
                 f32x16 s[P::MB];
-                P::scores(s, qf, kbuf(0), ln, h);
+                P::scores(s, qf, L, k0buf);
                 // branch-free mask: a global column counts here only when it is
                 // outside the row's window (inside, the band tiles count it)
 #pragma unroll
@@ -508,60 +533,64 @@ __global__ void __launch_bounds__(P::NT) fwd_kernel(const FwdParams prm) {
                         const bool vis = (col < ng) & ((prm.causal == 0) | (g <= row)) & ((g < lo) | (g > hi));
                         s[mb][r] = vis ? s[mb][r] : EEA_NEG_INF;
                     }
-                softmax_pv_step<P>(rs, s, c, vbuf(0), ln, h);
+                softmax_pv_step<P>(rs, s, c, L, v0buf);
             }
             __syncthreads();
         }
     }
 
-    // --- band tiles, double-buffered
+    // --- band tiles, double-buffered; the loop is unrolled by two so that
+    // each step reads one named buffer while the next tile streams into the
+    // other one.
+    auto step = [&](int kt, char *kr, char *vr, char *kw, char *vw) {
+        const bool more = kt < kt_hi;
+        typename P::Stage st;
+        if (more) {
+            const TileSrc src{(kt + 1) * BN, 0, N, ng, s_gidx};
+            P::issue(st, L, kh, vh, kw, vw, src, N - 1);
+        }
+        const int k0 = kt * BN;
+        int kind;   // -1 skip, 0 full, 1 edge
+        if (MODE == MODE_BAND) {
+            const int cl = classify(band, wr0, wr1, k0, k0 + BN - 1);
+            kind = (cl == TILE_SKIP || !wave_active) ? -1 : (cl == TILE_FULL ? 0 : 1);
+        } else {
+            kind = (!wave_active || k0 > wave_hi) ? -1 : 1;
+        }
+        if (kind >= 0) {
+            f32x16 s[P::MB];
+            P::scores(s, qf, L, kr);
+            if (kind == 1) {
+#pragma unroll
+                for (int mb = 0; mb < P::MB; ++mb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int j = k0 + mb * 32 + acc_row(r, h);
+                        s[mb][r] = ((j >= lo) & (j <= hi)) ? s[mb][r] : EEA_NEG_INF;
+                    }
+            }
+            softmax_pv_step<P>(rs, s, c, L, vr);
+        }
+        if (more) P::finish(st, kw, vw, tid);
+        __syncthreads();
+    };
     if (kt_lo <= kt_hi) {
         {
             typename P::Stage st;
-            const int k0 = kt_lo * BN;
-            P::load_stage(st, kh, vh, [&](int r) { return k0 + r < N ? k0 + r : -1; }, tid);
-            P::store_stage(st, kbuf(0), vbuf(0), tid);
+            const TileSrc src{kt_lo * BN, 0, N, ng, s_gidx};
+            P::issue(st, L, kh, vh, k0buf, v0buf, src, N - 1);
+            P::finish(st, k0buf, v0buf, tid);
         }
         __syncthreads();
-        int cur = 0;
-        for (int kt = kt_lo; kt <= kt_hi; ++kt) {
-            const bool more = kt < kt_hi;
-            typename P::Stage st;
-            if (more) {
-                const int k1 = (kt + 1) * BN;
-                P::load_stage(st, kh, vh, [&](int r) { return k1 + r < N ? k1 + r : -1; }, tid);
-            }
-            const int k0 = kt * BN;
-            int kind;
-            if (MODE == MODE_BAND) {
-                const int cl = classify(band, wr0, wr1, k0, k0 + BN - 1);
-                kind = (cl == TILE_SKIP || !wave_active) ? -1 : (cl == TILE_FULL ? KIND_FULL : KIND_EDGE);
-            } else {
-                kind = (!wave_active || k0 > wave_hi) ? -1 : KIND_EDGE;
-            }
-            if (kind >= 0) {
-                f32x16 s[P::MB];
-                P::scores(s, qf, kbuf(cur), ln, h);
-                if (kind == KIND_EDGE) {
-#pragma unroll
-                    for (int mb = 0; mb < P::MB; ++mb)
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const int j = k0 + mb * 32 + acc_row(r, h);
-                            s[mb][r] = ((j >= lo) & (j <= hi)) ? s[mb][r] : EEA_NEG_INF;
-                        }
-                }
-                softmax_pv_step<P>(rs, s, c, vbuf(cur), ln, h);
-            }
-            if (more) P::store_stage(st, kbuf(cur ^ 1), vbuf(cur ^ 1), tid);
-            __syncthreads();
-            cur ^= 1;
+        for (int kt = kt_lo; kt <= kt_hi; kt += 2) {
+            step(kt, k0buf, v0buf, k1buf, v1buf);
+            if (kt + 1 > kt_hi) break;
+            step(kt + 1, k1buf, v1buf, k0buf, v0buf);
         }
     }
-    (void)wave_lo;
 
     // --- epilogue
-    const float l = rs.lpart + __shfl_xor(rs.lpart, 32, 64);
+    const float l = sum_across_halves(rs.lpart);
     if (MODE == MODE_BAND) {
         if (!valid) return;
         if (ng > 0) {
@@ -581,9 +610,11 @@ __global__ void __launch_bounds__(P::NT) fwd_kernel(const FwdParams prm) {
         for (int db = 0; db < P::DB; ++db)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                f32x4 x = {rs.o[db][4 * g + 0], rs.o[db][4 * g + 1], rs.o[db][4 * g + 2], rs.o[db][4 * g + 3]};
                 float *p = dst + db * 32 + 8 * g + 4 * h;
-                p[0] = x[0]; p[1] = x[1]; p[2] = x[2]; p[3] = x[3];
+                p[0] = rs.o[db][4 * g + 0];
+                p[1] = rs.o[db][4 * g + 1];
+                p[2] = rs.o[db][4 * g + 2];
+                p[3] = rs.o[db][4 * g + 3];
             }
         if (h == 0) {
             dst[D] = rs.m;
@@ -631,10 +662,10 @@ __global__ void __launch_bounds__(64) merge_kernel(const FwdParams prm) {
 // ---------------------------------------------------------------------------
 // Host-side launch.
 // ---------------------------------------------------------------------------
-template <int D> using BandBf16 = Bf16Path<D, 64, 256>;
-template <int D> using BandF32 = F32Path<D, 32, 256>;
+constexpr int kBandThreadsBf16 = 512;   // 8 waves, 256 query rows
+constexpr int kBandThreadsF32 = 256;    // 4 waves, 128 query rows
 
-int tile_bm(int d, int f32) { (void)d; (void)f32; return 128; }
+int tile_bm(int d, int f32) { (void)d; return 32 * ((f32 ? kBandThreadsF32 : kBandThreadsBf16) / 64); }
 int tile_bn(int d, int f32) { (void)d; return f32 ? 32 : 64; }
 
 int global_chunks(int BH, int N, int d, int f32, int *chunk_tiles) {
@@ -672,11 +703,13 @@ static hipError_t launch_impl(const FwdParams &p0, hipStream_t stream) {
 
 hipError_t launch_forward(const FwdParams &p, int d, int f32, hipStream_t stream) {
     if (f32) {
-        if (d == 64) return launch_impl<F32Path<64, 32, 256>, F32Path<64, 32, 64>, F32Path<64, 32, 128>, 64, true>(p, stream);
-        return launch_impl<F32Path<128, 32, 256>, F32Path<128, 32, 64>, F32Path<128, 32, 128>, 128, true>(p, stream);
+        if (d == 64)
+            return launch_impl<F32Path<64, kBandThreadsF32>, F32Path<64, 64>, F32Path<64, 128>, 64, true>(p, stream);
+        return launch_impl<F32Path<128, kBandThreadsF32>, F32Path<128, 64>, F32Path<128, 128>, 128, true>(p, stream);
     }
-    if (d == 64) return launch_impl<Bf16Path<64, 64, 256>, Bf16Path<64, 64, 64>, Bf16Path<64, 64, 128>, 64, false>(p, stream);
-    return launch_impl<Bf16Path<128, 64, 256>, Bf16Path<128, 64, 64>, Bf16Path<128, 64, 128>, 128, false>(p, stream);
+    if (d == 64)
+        return launch_impl<Bf16Path<64, kBandThreadsBf16>, Bf16Path<64, 64>, Bf16Path<64, 128>, 64, false>(p, stream);
+    return launch_impl<Bf16Path<128, kBandThreadsBf16>, Bf16Path<128, 64>, Bf16Path<128, 128>, 128, false>(p, stream);
 }
 
 }  // namespace eea

@@ -102,8 +102,8 @@ def test_inputs_may_alias():
 
 
 def test_tile_shape():
-    assert ea.attn_tile_shape(128) == (128, 64)
-    assert ea.attn_tile_shape(64) == (128, 64)
+    assert ea.attn_tile_shape(128) == (256, 64)
+    assert ea.attn_tile_shape(64) == (256, 64)
     assert ea.attn_tile_shape(64, ea.ATTN_F32) == (128, 32)
     with pytest.raises(ea.AttnError):
         ea.attn_tile_shape(80)
