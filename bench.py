@@ -122,6 +122,9 @@ def main():
     ap.add_argument("--config", default="tgt", choices=sorted(W.WORKLOADS))
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="after timing, run one plain device copy of this many bytes "
+                         "(calibration dispatch for HBM byte counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -192,6 +195,15 @@ def main():
     print(f"[bench] {ms_step:.3f} ms/step, {value:.1f} TFLOP/s, launch avg {avg_launch_ms:.3f} ms "
           f"(min {launch_ms[0]:.3f}, max {launch_ms[-1]:.3f}), wall {wall:.2f} s", file=sys.stderr,
           flush=True)
+
+    if args.copy_bytes > 0:
+        src = torch.ones(args.copy_bytes, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[bench] calibration copy of {args.copy_bytes} bytes done", file=sys.stderr, flush=True)
+        del src, dst
 
     result = {
         "metric": METRIC,

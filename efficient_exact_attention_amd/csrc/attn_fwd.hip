@@ -118,37 +118,51 @@ struct Bf16Path {
     struct PFrag { bf16x8 x[PVS]; };
     struct Stage {};
 
+    // LDS layouts (gfx950 LDS serves 256 bytes per clock: 64 banks of 4 B).
+    // K rows: 16-byte chunk c of row r is stored at chunk c ^ kx(r). A
+    // ds_read_b128 serves 16 lanes per pass and the 16 lanes of a pass read
+    // the same logical chunk of 16 consecutive rows, so kx must map those
+    // rows onto 16 distinct 16-byte slots of the 256-byte bank window.
+    static __device__ __forceinline__ int kx(int r) {
+        return D == 128 ? (r & 15) : ((r >> 1) & 7);   // d=64: two rows per window
+    }
+    // V rows: the transpose read of a half-wave touches 4 consecutive key
+    // rows over one 64-byte d-block, so vx moves those 4 rows onto the 4
+    // distinct 64-byte quarters of the bank window.
+    static __device__ __forceinline__ int vx(int r) {
+        return D == 128 ? ((r & 3) << 2) : (((r >> 1) & 1) << 2);
+    }
+
     // Per-lane constants, computed once.
     struct Lane {
-        int krd[4];        // K operand: byte offset in a K tile for (mb=0, ks&3)
-        int vrd[2];        // V operand: byte offset in a V tile for (st=0, db&1)
+        int krd[KS];       // K operand: byte offset in a K tile for (mb=0, ks)
+        int vrd[DB];       // V operand: byte offset in a V tile for (st=0, db)
         int ldrow[SPW];    // tile row this lane fetches in load i
-        int ldcol[SPW];    // element offset of its 16-byte chunk within that row
+        int ldkcol[SPW];   // element offset of its K chunk within that row
+        int ldvcol[SPW];   // element offset of its V chunk within that row
         int ldlds[SPW];    // LDS byte offset (within a tile) of this wave's load i
     };
 
     static __device__ __forceinline__ void init_lane(Lane &L, int lane, int wave) {
-        const int ln = lane & 31, h = lane >> 5, x = ln & 7;
-        // K row ln, logical chunk 2ks + h, stored at chunk (2ks + h) ^ (ln & 7)
+        const int ln = lane & 31, h = lane >> 5;
+        // K row ln, logical chunk 2ks + h
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-            L.krd[q] = ln * ROWB + 16 * (2 * (q ^ (x >> 1)) + (h ^ (x & 1)));
+        for (int ks = 0; ks < KS; ++ks) L.krd[ks] = ln * ROWB + 16 * ((2 * ks + h) ^ kx(ln));
         // transpose read: lane j of 16-lane group g loads 4 elements of key
-        // row 4h + j/4 at d = 16(g&1) + 4(j&3); lane i of the group then holds
-        // d = 16(g&1) + i for the keys 4h + e, e = 0..3
+        // row 4h + j/4 at d = 32db + 16(g&1) + 4(j&3); lane i of the group then
+        // holds d = 32db + 16(g&1) + i for the keys 4h + e, e = 0..3
         const int g = lane >> 4, j = lane & 15;
         const int krow = 4 * h + (j >> 2);
-        const int y = krow & 7;
         const int t = 2 * (g & 1) + ((j >> 1) & 1);
 #pragma unroll
-        for (int p = 0; p < 2; ++p)
-            L.vrd[p] = krow * ROWB + 16 * ((4 * p + t) ^ y) + 8 * (j & 1);
+        for (int db = 0; db < DB; ++db) L.vrd[db] = krow * ROWB + 16 * ((4 * db + t) ^ vx(krow)) + 8 * (j & 1);
 #pragma unroll
         for (int i = 0; i < SPW; ++i) {
             const int o = (wave * SPW + i) * 1024 + lane * 16;
             const int row = o / ROWB, phys = (o % ROWB) / 16;
             L.ldrow[i] = row;
-            L.ldcol[i] = (phys ^ (row & 7)) * 8;
+            L.ldkcol[i] = (phys ^ kx(row)) * 8;
+            L.ldvcol[i] = (phys ^ vx(row)) * 8;
             L.ldlds[i] = (wave * SPW + i) * 1024;
         }
     }
@@ -170,9 +184,9 @@ struct Bf16Path {
         for (int i = 0; i < SPW; ++i) {
             int key = src.key(L.ldrow[i]);
             key = key < 0 ? fallback : key;
-            const long long off = (long long)key * D + L.ldcol[i];
-            __builtin_amdgcn_global_load_lds(kh + off, (EEA_LDS void *)(kbuf + L.ldlds[i]), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(vh + off, (EEA_LDS void *)(vbuf + L.ldlds[i]), 16, 0, 0);
+            const long long off = (long long)key * D;
+            __builtin_amdgcn_global_load_lds(kh + off + L.ldkcol[i], (EEA_LDS void *)(kbuf + L.ldlds[i]), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(vh + off + L.ldvcol[i], (EEA_LDS void *)(vbuf + L.ldlds[i]), 16, 0, 0);
         }
     }
 
@@ -185,7 +199,7 @@ struct Bf16Path {
             f32x16 acc = {};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                const char *p = kbuf + L.krd[ks & 3] + mb * 32 * ROWB + 128 * (ks >> 2);
+                const char *p = kbuf + L.krd[ks] + mb * 32 * ROWB;
                 bf16x8 a = *reinterpret_cast<const bf16x8 *>(p);
                 acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf.x[ks], acc, 0, 0, 0);
             }
@@ -204,7 +218,7 @@ struct Bf16Path {
     }
 
     static __device__ __forceinline__ bf16x8 v_operand(const Lane &L, const char *vbuf, int db, int st) {
-        const char *p = vbuf + L.vrd[db & 1] + 128 * (db >> 1) + 16 * st * ROWB;
+        const char *p = vbuf + L.vrd[db] + 16 * st * ROWB;
         s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((EEA_LDS s16x4 *)(p));
         s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((EEA_LDS s16x4 *)(p + 8 * ROWB));
         s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
