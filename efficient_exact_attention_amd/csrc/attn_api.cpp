@@ -182,6 +182,8 @@ int attn_fwd_ex(const void *q, const void *k, const void *v, void *out, float *l
     if (BH > INT_MAX || BH * nqt > INT_MAX)
         return fail(ATTN_ERR_INVALID_ARG, "B*H=%lld with N=%d exceeds the launch grid", BH, N);
     const size_t esize = dtype == ATTN_F32 ? 4 : 2;
+    if ((long long)N * d * (long long)esize > INT_MAX)
+        return fail(ATTN_ERR_UNSUPPORTED, "one head's K of N=%d x d=%d elements exceeds 2 GiB", N, d);
     const size_t tbytes = (size_t)BH * N * d * esize;   // < 2^31 * 2^31 * 128 * 4: fits in 64 bits
     const size_t lbytes = (size_t)BH * N * sizeof(float);
 

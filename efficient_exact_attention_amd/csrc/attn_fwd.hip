@@ -141,6 +141,8 @@ struct Bf16Path {
         int ldkcol[SPW];   // element offset of its K chunk within that row
         int ldvcol[SPW];   // element offset of its V chunk within that row
         int ldlds[SPW];    // LDS byte offset (within a tile) of this wave's load i
+        int ldk[SPW];      // byte offset of load i's K chunk from the tile's first row
+        int ldv[SPW];      // byte offset of load i's V chunk from the tile's first row
     };
 
     static __device__ __forceinline__ void init_lane(Lane &L, int lane, int wave) {
@@ -164,6 +166,8 @@ struct Bf16Path {
             L.ldkcol[i] = (phys ^ kx(row)) * 8;
             L.ldvcol[i] = (phys ^ vx(row)) * 8;
             L.ldlds[i] = (wave * SPW + i) * 1024;
+            L.ldk[i] = row * ROWB + 2 * L.ldkcol[i];
+            L.ldv[i] = row * ROWB + 2 * L.ldvcol[i];
         }
     }
 
@@ -178,33 +182,102 @@ struct Bf16Path {
 
     // Start the global -> LDS copy of one K tile and one V tile. Rows with no
     // key fetch row `fallback` (a valid row); the caller masks them.
+    //
+    // The copies are MUBUF buffer loads with the LDS-destination bit (one
+    // buffer resource per head, byte offsets below 2^31). Unlike the FLAT
+    // form of the same copy, a buffer load only counts on vmcnt, so the
+    // compiler can still wait for an exact number of the LDS reads that
+    // follow it while the copy is in flight.
+    static __device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const elem_t *base, int N) {
+        // dword3 0x00020000: raw 32-bit data format, the usual gfx9 setting
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<elem_t *>(base), 0, N * ROWB, 0x00020000);
+    }
     static __device__ __forceinline__ void issue(Stage &, const Lane &L, const elem_t *kh, const elem_t *vh,
                                                  char *kbuf, char *vbuf, const TileSrc &src, int fallback) {
+        const __amdgpu_buffer_rsrc_t kr = head_rsrc(kh, src.N), vr = head_rsrc(vh, src.N);
 #pragma unroll
         for (int i = 0; i < SPW; ++i) {
             int key = src.key(L.ldrow[i]);
             key = key < 0 ? fallback : key;
-            const long long off = (long long)key * D;
-            __builtin_amdgcn_global_load_lds(kh + off + L.ldkcol[i], (EEA_LDS void *)(kbuf + L.ldlds[i]), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(vh + off + L.ldvcol[i], (EEA_LDS void *)(vbuf + L.ldlds[i]), 16, 0, 0);
+            const unsigned off = (unsigned)key * ROWB;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (EEA_LDS void *)(kbuf + L.ldlds[i]), 16,
+                                                     off + 2 * L.ldkcol[i], 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (EEA_LDS void *)(vbuf + L.ldlds[i]), 16,
+                                                     off + 2 * L.ldvcol[i], 0, 0, 0);
         }
+    }
+
+    // Band tiles: the copy of the K (or V) tile whose first key is k0. Rows
+    // past the end of the sequence lie past the buffer's last record, so the
+    // copy fills them with zeros (finite values that the edge mask drops).
+    static __device__ __forceinline__ void issue_k(const Lane &L, const elem_t *kh, int N, char *kbuf, int k0) {
+        const __amdgpu_buffer_rsrc_t kr = head_rsrc(kh, N);
+        const unsigned base = (unsigned)k0 * ROWB;
+#pragma unroll
+        for (int i = 0; i < SPW; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (EEA_LDS void *)(kbuf + L.ldlds[i]), 16, base + L.ldk[i], 0,
+                                                     0, 0);
+    }
+    static __device__ __forceinline__ void issue_v(const Lane &L, const elem_t *vh, int N, char *vbuf, int k0) {
+        const __amdgpu_buffer_rsrc_t vr = head_rsrc(vh, N);
+        const unsigned base = (unsigned)k0 * ROWB;
+#pragma unroll
+        for (int i = 0; i < SPW; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (EEA_LDS void *)(vbuf + L.ldlds[i]), 16, base + L.ldv[i], 0,
+                                                     0, 0);
     }
 
     static __device__ __forceinline__ void finish(Stage &, char *, char *, int) { wait_vmem(); }
 
+    // Operand pipeline of one matrix phase. The LDS reads of batch b+1 (four
+    // operands) are issued before the four MFMAs of batch b, each group fenced
+    // by sched_barrier, so every MFMA finds its operand a whole batch after
+    // the read was issued instead of waiting out the LDS latency. Operands
+    // are taken in an order whose consecutive MFMAs write different
+    // accumulators. The recursion keeps every index a compile-time constant.
+    static constexpr int kBatch = 4, kSlots = 2 * kBatch;
+
+    template <int I>
+    static __device__ __forceinline__ void qk_fetch(bf16x8 (&op)[kSlots], const Lane &L, const char *kbuf) {
+        if constexpr (I < KS * MB) {
+            constexpr int ks = I / MB, mb = I % MB;
+            op[I % kSlots] = *reinterpret_cast<const bf16x8 *>(kbuf + L.krd[ks] + mb * 32 * ROWB);
+        }
+    }
+    template <int B>
+    static __device__ __forceinline__ void qk_run(f32x16 (&s)[MB], const QFrag &qf, const Lane &L,
+                                                  const char *kbuf, bf16x8 (&op)[kSlots]) {
+        constexpr int NB = KS * MB / kBatch;
+        if constexpr (B < NB) {
+            if constexpr (B + 1 < NB) {
+                qk_fetch<kBatch * (B + 1) + 0>(op, L, kbuf);
+                qk_fetch<kBatch * (B + 1) + 1>(op, L, kbuf);
+                qk_fetch<kBatch * (B + 1) + 2>(op, L, kbuf);
+                qk_fetch<kBatch * (B + 1) + 3>(op, L, kbuf);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                const int I = kBatch * B + u, ks = I / MB, mb = I % MB;
+                s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[I % kSlots], qf.x[ks], s[mb], 0, 0, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            qk_run<B + 1>(s, qf, L, kbuf, op);
+        }
+    }
+
     static __device__ __forceinline__ void scores(f32x16 (&s)[MB], const QFrag &qf, const Lane &L,
                                                   const char *kbuf) {
+        static_assert((KS * MB) % kBatch == 0, "whole batches");
+        bf16x8 op[kSlots];
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-            f32x16 acc = {};
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const char *p = kbuf + L.krd[ks] + mb * 32 * ROWB;
-                bf16x8 a = *reinterpret_cast<const bf16x8 *>(p);
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf.x[ks], acc, 0, 0, 0);
-            }
-            s[mb] = acc;
-        }
+        for (int mb = 0; mb < MB; ++mb) s[mb] = f32x16{};
+        qk_fetch<0>(op, L, kbuf);
+        qk_fetch<1>(op, L, kbuf);
+        qk_fetch<2>(op, L, kbuf);
+        qk_fetch<3>(op, L, kbuf);
+        __builtin_amdgcn_sched_barrier(0);
+        qk_run<0>(s, qf, L, kbuf, op);
     }
 
     static __device__ __forceinline__ void pack_p(PFrag &pf, const f32x16 (&s)[MB]) {
@@ -225,16 +298,42 @@ struct Bf16Path {
         return __builtin_bit_cast(bf16x8, v);
     }
 
+    template <int I>
+    static __device__ __forceinline__ void pv_fetch(bf16x8 (&op)[kSlots], const Lane &L, const char *vbuf) {
+        if constexpr (I < PVS * DB) op[I % kSlots] = v_operand(L, vbuf, I % DB, I / DB);
+    }
+    template <int B>
+    static __device__ __forceinline__ void pv_run(f32x16 (&o)[DB], const PFrag &pf, const Lane &L,
+                                                  const char *vbuf, bf16x8 (&op)[kSlots]) {
+        constexpr int NB = PVS * DB / kBatch;
+        if constexpr (B < NB) {
+            if constexpr (B + 1 < NB) {
+                pv_fetch<kBatch * (B + 1) + 0>(op, L, vbuf);
+                pv_fetch<kBatch * (B + 1) + 1>(op, L, vbuf);
+                pv_fetch<kBatch * (B + 1) + 2>(op, L, vbuf);
+                pv_fetch<kBatch * (B + 1) + 3>(op, L, vbuf);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                const int I = kBatch * B + u, st = I / DB, db = I % DB;
+                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[I % kSlots], pf.x[st], o[db], 0, 0, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            pv_run<B + 1>(o, pf, L, vbuf, op);
+        }
+    }
+
     static __device__ __forceinline__ void pv(f32x16 (&o)[DB], const PFrag &pf, const Lane &L,
                                               const char *vbuf) {
-#pragma unroll
-        for (int st = 0; st < PVS; ++st) {
-#pragma unroll
-            for (int db = 0; db < DB; ++db) {
-                bf16x8 a = v_operand(L, vbuf, db, st);
-                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf.x[st], o[db], 0, 0, 0);
-            }
-        }
+        static_assert((PVS * DB) % kBatch == 0, "whole batches");
+        bf16x8 op[kSlots];
+        pv_fetch<0>(op, L, vbuf);
+        pv_fetch<1>(op, L, vbuf);
+        pv_fetch<2>(op, L, vbuf);
+        pv_fetch<3>(op, L, vbuf);
+        __builtin_amdgcn_sched_barrier(0);
+        pv_run<0>(o, pf, L, vbuf, op);
     }
 
     static __device__ __forceinline__ void store_out(elem_t *oh, int row, const f32x16 (&o)[DB],
@@ -637,6 +736,356 @@ __global__ void __launch_bounds__(P::NT) fwd_kernel(const FwdParams prm) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 band pass, software-pipelined inside each wave.
+//
+// Iteration j of the key-tile loop gives the matrix cores and the vector ALU
+// of one wave independent work at the same time:
+//   region A: S(j+1) = K(j+1) Q^T on the matrix cores, while the vector ALU
+//             exponentiates S(j) against the running max and packs the
+//             weights to bf16;
+//   region B: O^T += V(j)^T P(j)^T on the matrix cores, while the vector ALU
+//             adds the fp32 weights of tile j to the normaliser and masks
+//             (edge tiles) and reduces the row max of S(j+1);
+//   then the running max moves, and O and the normaliser are rescaled, if
+//   S(j+1) raised it by more than 2^8.
+// K runs one tile ahead of V: iteration j reads K(j+1) and V(j) and copies
+// K(j+2) and V(j+1) into the buffers iteration j-1 finished reading.
+// Within a region, sched_group_barrier lays the stream out as one MFMA
+// followed by a share of the vector work, so the vector instructions issue
+// while the MFMA before them is still in the matrix pipe.
+// ---------------------------------------------------------------------------
+struct EdgeMask {
+    int k0, lo, hi, h;   // first key of the tile; the lane's row interval; half-wave
+};
+
+template <class P>
+struct BandPipe {
+    static constexpr int MB = P::MB, KS = P::KS, DB = P::DB, PVS = P::PVS;
+    static constexpr int NE = 16 * MB;                    // scores per lane per tile
+    static constexpr int kB = 4, kSlots = 8;              // MFMAs per batch; operand slots
+    static constexpr int BQK = KS * MB / kB, BPV = PVS * DB / kB;
+    static constexpr int EA = NE / BQK, EB = NE / BPV;    // scores handled per batch
+    static_assert(EA % 8 == 0 && EB % 2 == 0, "whole packed groups per batch");
+    typedef typename P::QFrag QF;
+    typedef typename P::PFrag PF;
+    typedef typename P::Lane LN;
+
+    template <int I>
+    static __device__ __forceinline__ void k_fetch(bf16x8 (&op)[kSlots], const LN &L, const char *kbuf) {
+        if constexpr (I < KS * MB) {
+            constexpr int ks = I / MB, mb = I % MB;
+            op[I % kSlots] = *reinterpret_cast<const bf16x8 *>(kbuf + L.krd[ks] + mb * 32 * P::ROWB);
+        }
+    }
+    template <int I>
+    static __device__ __forceinline__ void v_fetch(bf16x8 (&op)[kSlots], const LN &L, const char *vbuf) {
+        if constexpr (I < PVS * DB) op[I % kSlots] = P::v_operand(L, vbuf, I % DB, I / DB);
+    }
+
+    // Region A, batch B: the reads of batch B+1, four QK MFMAs, and the
+    // exponentials of scores [B*EA, (B+1)*EA) of the previous tile.
+    template <bool QK, bool EXP, int B>
+    static __device__ __forceinline__ void a_run(f32x16 (&sn)[MB], f32x16 (&s)[MB], PF &pf, const QF &qf,
+                                                 const LN &L, const char *kbuf, bf16x8 (&op)[kSlots], float c,
+                                                 float nmu) {
+        if constexpr (B < BQK) {
+            if constexpr (QK && B + 1 < BQK) {
+                k_fetch<kB * (B + 1) + 0>(op, L, kbuf);
+                k_fetch<kB * (B + 1) + 1>(op, L, kbuf);
+                k_fetch<kB * (B + 1) + 2>(op, L, kbuf);
+                k_fetch<kB * (B + 1) + 3>(op, L, kbuf);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            if constexpr (QK) {
+#pragma unroll
+                for (int u = 0; u < kB; ++u) {
+                    const int I = kB * B + u, ks = I / MB, mb = I % MB;
+                    sn[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[I % kSlots], qf.x[ks], sn[mb], 0, 0, 0);
+                }
+            }
+            if constexpr (EXP) {
+#pragma unroll
+                for (int e = B * EA; e < (B + 1) * EA; ++e)
+                    s[e / 16][e % 16] = fast_exp2(__builtin_fmaf(s[e / 16][e % 16], c, nmu));
+#pragma unroll
+                for (int st = B * EA / 8; st < (B + 1) * EA / 8; ++st) {
+                    const int mb = st >> 1, r0 = 8 * (st & 1);
+                    f32x8 x = {s[mb][r0 + 0], s[mb][r0 + 1], s[mb][r0 + 2], s[mb][r0 + 3],
+                               s[mb][r0 + 4], s[mb][r0 + 5], s[mb][r0 + 6], s[mb][r0 + 7]};
+                    pf.x[st] = __builtin_convertvector(x, bf16x8);
+                }
+            }
+            if constexpr (QK && EXP) {
+                constexpr int NV = (5 * EA / 2) / kB;   // fma + exp per score, one cvt per two
+#pragma unroll
+                for (int u = 0; u < kB; ++u) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x402, NV, 0);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            a_run<QK, EXP, B + 1>(sn, s, pf, qf, L, kbuf, op, c, nmu);
+        }
+    }
+    template <bool QK, bool EXP>
+    static __device__ __forceinline__ void region_a(f32x16 (&sn)[MB], f32x16 (&s)[MB], PF &pf, const QF &qf,
+                                                    const LN &L, const char *kbuf, float c, float nmu) {
+        bf16x8 op[kSlots];
+        if constexpr (QK) {
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) sn[mb] = f32x16{};
+            k_fetch<0>(op, L, kbuf);
+            k_fetch<1>(op, L, kbuf);
+            k_fetch<2>(op, L, kbuf);
+            k_fetch<3>(op, L, kbuf);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        a_run<QK, EXP, 0>(sn, s, pf, qf, L, kbuf, op, c, nmu);
+    }
+
+    // Region B, batch B: the reads of batch B+1, four PV MFMAs, the sum of
+    // weights [B*EB, (B+1)*EB) of this tile, and mask + max of the same
+    // scores of the next tile.
+    template <bool PV, bool NEXT, bool EDGE, int B>
+    static __device__ __forceinline__ void b_run(f32x16 (&o)[DB], const PF &pf, const f32x16 (&s)[MB],
+                                                 float (&sum)[2], f32x16 (&sn)[MB], float (&mx)[2], const LN &L,
+                                                 const char *vbuf, bf16x8 (&op)[kSlots], const EdgeMask &em) {
+        if constexpr (B < BPV) {
+            if constexpr (PV && B + 1 < BPV) {
+                v_fetch<kB * (B + 1) + 0>(op, L, vbuf);
+                v_fetch<kB * (B + 1) + 1>(op, L, vbuf);
+                v_fetch<kB * (B + 1) + 2>(op, L, vbuf);
+                v_fetch<kB * (B + 1) + 3>(op, L, vbuf);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            if constexpr (PV) {
+#pragma unroll
+                for (int u = 0; u < kB; ++u) {
+                    const int I = kB * B + u, st = I / DB, db = I % DB;
+                    o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[I % kSlots], pf.x[st], o[db], 0, 0, 0);
+                }
+#pragma unroll
+                for (int e = B * EB; e < (B + 1) * EB; ++e) sum[e & 1] += s[e / 16][e % 16];
+            }
+            if constexpr (NEXT) {
+#pragma unroll
+                for (int e = B * EB; e < (B + 1) * EB; ++e) {
+                    const int mb = e / 16, r = e % 16;
+                    if constexpr (EDGE) {
+                        const int j = em.k0 + mb * 32 + acc_row(r, em.h);
+                        sn[mb][r] = ((j >= em.lo) & (j <= em.hi)) ? sn[mb][r] : EEA_NEG_INF;
+                    }
+                    mx[e & 1] = fmaxf(mx[e & 1], sn[mb][r]);
+                }
+            }
+            if constexpr (PV && NEXT) {
+                constexpr int NV = (EDGE ? 6 * EB : 2 * EB) / kB;
+#pragma unroll
+                for (int u = 0; u < kB; ++u) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            b_run<PV, NEXT, EDGE, B + 1>(o, pf, s, sum, sn, mx, L, vbuf, op, em);
+        }
+    }
+    template <bool PV, bool NEXT, bool EDGE>
+    static __device__ __forceinline__ float region_b(f32x16 (&o)[DB], const PF &pf, const f32x16 (&s)[MB],
+                                                     float &lpart, f32x16 (&sn)[MB], const LN &L, const char *vbuf,
+                                                     const EdgeMask &em) {
+        bf16x8 op[kSlots];
+        float sum[2] = {0.f, 0.f}, mx[2] = {EEA_NEG_INF, EEA_NEG_INF};
+        if constexpr (PV) {
+            v_fetch<0>(op, L, vbuf);
+            v_fetch<1>(op, L, vbuf);
+            v_fetch<2>(op, L, vbuf);
+            v_fetch<3>(op, L, vbuf);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        b_run<PV, NEXT, EDGE, 0>(o, pf, s, sum, sn, mx, L, vbuf, op, em);
+        if constexpr (PV) lpart += sum[0] + sum[1];
+        return fmaxf(mx[0], mx[1]);
+    }
+};
+
+// Move the running max to cover a new tile whose lane max is mx (raw score
+// units); rescale O and the normaliser only when some row's max grew by more
+// than 2^kRescaleLog2.
+template <class P>
+__device__ __forceinline__ void raise_max(RowState<P> &rs, float mx, float c) {
+    mx = max_across_halves(mx);
+    const float mnew = fmaxf(rs.m, mx * c);
+    if (__any(mnew > rs.m + kRescaleLog2)) {
+        const float alpha = (mnew == EEA_NEG_INF) ? 1.f : fast_exp2(rs.m - mnew);
+        rs.m = mnew;
+        rs.lpart *= alpha;
+#pragma unroll
+        for (int db = 0; db < P::DB; ++db) rs.o[db] *= alpha;
+    }
+}
+
+template <int D>
+__global__ void __launch_bounds__(512) fwd_band_bf16(const FwdParams prm) {
+    typedef Bf16Path<D, 512> P;
+    typedef BandPipe<P> BP;
+    constexpr int BN = P::BN, BM = 32 * P::NW, MB = P::MB;
+
+    // Two K and two V buffers as distinct objects: the copy into one is never
+    // mistaken for a hazard of the reads from another.
+    __shared__ __attribute__((aligned(1024))) char kb0[P::TILE_BYTES];
+    __shared__ __attribute__((aligned(1024))) char kb1[P::TILE_BYTES];
+    __shared__ __attribute__((aligned(1024))) char vb0[P::TILE_BYTES];
+    __shared__ __attribute__((aligned(1024))) char vb1[P::TILE_BYTES];
+    __shared__ int s_gidx[kMaxGlobal];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int ln = lane & 31, h = lane >> 5;
+    const int N = prm.N;
+    const int ng = prm.n_global;
+    const Band band{N, prm.wl, prm.wr};
+
+    if (tid < kMaxGlobal) s_gidx[tid] = tid < ng ? prm.gidx[tid] : -1;
+
+    // --- work item: heaviest query tiles first under a causal mask, runs of
+    // consecutive items on one XCD
+    const int G = gridDim.x;
+    const int bid = blockIdx.x;
+    const int Lw = prm.xcd_remap ? (bid & 7) * (G >> 3) + (bid >> 3) : bid;
+    const int bh = Lw / prm.num_qt;
+    const int qi = Lw - bh * prm.num_qt;
+    const int unit = prm.causal ? prm.num_qt - 1 - qi : qi;
+    const uint16_t *qh = static_cast<const uint16_t *>(prm.q) + (long long)bh * prm.head_stride;
+    const uint16_t *kh = static_cast<const uint16_t *>(prm.k) + (long long)bh * prm.head_stride;
+    const uint16_t *vh = static_cast<const uint16_t *>(prm.v) + (long long)bh * prm.head_stride;
+
+    typename P::Lane L;
+    P::init_lane(L, lane, wave);
+
+    __syncthreads();   // s_gidx visible
+
+    const int q0 = unit * BM;
+    const int row = q0 + wave * 32 + ln;
+    const bool valid = row < N;
+    const int lo = row_lo(band, row);
+    const int hi = row_hi(band, row);
+    const int wr0 = q0 + wave * 32;
+    const int wr1 = imin(N - 1, wr0 + 31);
+    const bool wave_active = wr0 < N;
+    int kt_lo, kt_hi;
+    key_tile_range(band, q0, imin(N - 1, q0 + BM - 1), BN, &kt_lo, &kt_hi);
+    int w_lo = kt_hi + 1, w_hi = kt_hi;   // this wave's key tiles (none if inactive)
+    if (wave_active) key_tile_range(band, wr0, wr1, BN, &w_lo, &w_hi);
+
+    typename P::QFrag qf;
+    P::load_q(qf, qh, row, valid, h);
+
+    RowState<P> rs;
+    rs.m = EEA_NEG_INF;
+    rs.lpart = 0.f;
+#pragma unroll
+    for (int db = 0; db < P::DB; ++db) rs.o[db] = f32x16{};
+    const float c = prm.scale_log2;
+
+    // --- gathered tiles of global columns (one per BN globals), unpipelined
+    if (ng > 0) {
+        for (int g0 = 0; g0 < ng; g0 += BN) {
+            typename P::Stage st;
+            const TileSrc src{g0, 1, N, ng, s_gidx};
+            P::issue(st, L, kh, vh, kb0, vb0, src, s_gidx[0]);
+            P::finish(st, kb0, vb0, tid);
+            __syncthreads();
+            if (wave_active) {
+                f32x16 s[MB];
+                P::scores(s, qf, L, kb0);
+                // a global column counts here only outside the row's window
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int col = g0 + mb * 32 + acc_row(r, h);
+                        const int g = s_gidx[col < kMaxGlobal ? col : 0];
+                        const bool vis = (col < ng) & ((prm.causal == 0) | (g <= row)) & ((g < lo) | (g > hi));
+                        s[mb][r] = vis ? s[mb][r] : EEA_NEG_INF;
+                    }
+                softmax_pv_step<P>(rs, s, c, L, vb0);
+            }
+            __syncthreads();
+        }
+    }
+
+    // --- band tiles
+    auto in_w = [&](int kt) { return kt >= w_lo && kt <= w_hi; };
+    auto is_edge = [&](int kt) { return classify(band, wr0, wr1, kt * BN, kt * BN + BN - 1) != TILE_FULL; };
+
+    P::issue_k(L, kh, N, kb0, kt_lo * BN);
+    P::issue_v(L, vh, N, vb0, kt_lo * BN);
+    if (kt_lo + 1 <= kt_hi) P::issue_k(L, kh, N, kb1, (kt_lo + 1) * BN);
+    wait_vmem();
+    __syncthreads();
+
+    f32x16 sa[MB], sb[MB];
+    typename P::PFrag pf;
+    if (in_w(kt_lo)) {
+        P::scores(sa, qf, L, kb0);
+        const EdgeMask em{kt_lo * BN, lo, hi, h};
+        const float mx = is_edge(kt_lo) ? BP::template region_b<false, true, true>(rs.o, pf, sb, rs.lpart, sa, L, vb0, em)
+                                        : BP::template region_b<false, true, false>(rs.o, pf, sb, rs.lpart, sa, L, vb0, em);
+        raise_max<P>(rs, mx, c);
+    }
+    __syncthreads();   // every wave is done with kb0
+
+    // One iteration; s holds S(j), sn receives S(j+1).
+    auto iter = [&](int j, f32x16 (&s)[MB], f32x16 (&sn)[MB], const char *kr, const char *vr, char *kw, char *vw)
+        __attribute__((always_inline)) {
+        if (j + 2 <= kt_hi) P::issue_k(L, kh, N, kw, (j + 2) * BN);
+        if (j + 1 <= kt_hi) P::issue_v(L, vh, N, vw, (j + 1) * BN);
+        const bool cur = in_w(j), nxt = in_w(j + 1);
+        const EdgeMask em{(j + 1) * BN, lo, hi, h};
+        const float nmu = rs.m == EEA_NEG_INF ? 0.f : -rs.m;
+        if (cur) {
+            if (nxt) {
+                BP::template region_a<true, true>(sn, s, pf, qf, L, kr, c, nmu);
+                const float mx = is_edge(j + 1)
+                                     ? BP::template region_b<true, true, true>(rs.o, pf, s, rs.lpart, sn, L, vr, em)
+                                     : BP::template region_b<true, true, false>(rs.o, pf, s, rs.lpart, sn, L, vr, em);
+                raise_max<P>(rs, mx, c);
+            } else {
+                BP::template region_a<false, true>(sn, s, pf, qf, L, kr, c, nmu);
+                BP::template region_b<true, false, false>(rs.o, pf, s, rs.lpart, sn, L, vr, em);
+            }
+        } else if (nxt) {
+            BP::template region_a<true, false>(sn, s, pf, qf, L, kr, c, nmu);
+            const float mx = is_edge(j + 1)
+                                 ? BP::template region_b<false, true, true>(rs.o, pf, s, rs.lpart, sn, L, vr, em)
+                                 : BP::template region_b<false, true, false>(rs.o, pf, s, rs.lpart, sn, L, vr, em);
+            raise_max<P>(rs, mx, c);
+        }
+        wait_vmem();
+        __syncthreads();
+    };
+    // K(x) sits in kb[(x - kt_lo) & 1], V(x) in vb[(x - kt_lo) & 1]; the loop
+    // is unrolled by two so every buffer is a named object.
+    for (int j = kt_lo; j <= kt_hi; j += 2) {
+        iter(j, sa, sb, kb1, vb0, kb0, vb1);
+        if (j + 1 > kt_hi) break;
+        iter(j + 1, sb, sa, kb0, vb1, kb1, vb0);
+    }
+
+    // --- epilogue
+    if (!valid) return;
+    if (ng > 0) {
+        for (int t = 0; t < ng; ++t)
+            if (s_gidx[t] == row) return;   // global rows are written by the merge
+    }
+    const float l = sum_across_halves(rs.lpart);
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    uint16_t *oh = static_cast<uint16_t *>(prm.out) + (long long)bh * prm.head_stride;
+    P::store_out(oh, row, rs.o, inv, h);
+    if (h == 0) prm.lse[(long long)bh * N + row] = l > 0.f ? (rs.m + __log2f(l)) * kLn2 : EEA_NEG_INF;
+}
+
 // Merge of the split-key partials of one global row: the same rescaling
 // identity as the online softmax, applied across chunks.
 template <int D, bool F32>
@@ -700,7 +1149,10 @@ static hipError_t launch_impl(const FwdParams &p0, hipStream_t stream) {
     FwdParams p = p0;
     const int grid = p.BH * p.num_qt;
     p.xcd_remap = (grid % 8 == 0) ? 1 : 0;
-    hipLaunchKernelGGL((fwd_kernel<PB, MODE_BAND>), dim3(grid), dim3(PB::NT), 0, stream, p);
+    if constexpr (F32)
+        hipLaunchKernelGGL((fwd_kernel<PB, MODE_BAND>), dim3(grid), dim3(PB::NT), 0, stream, p);
+    else
+        hipLaunchKernelGGL((fwd_band_bf16<D>), dim3(grid), dim3(PB::NT), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.n_global == 0) return e;
     const int ggrid = p.BH * p.chunks;

@@ -66,7 +66,10 @@ typedef struct attn_opts {
  *   lse         [B][H][N] fp32 output: natural log of the sum over visible
  *               keys of exp(scaled score), the per-row log-sum-exp that a
  *               recomputing backward pass needs.
- *   B, H, N     batch, heads, tokens (each >= 1).
+ *   B, H, N     batch, heads, tokens (each >= 1). One head's K (or V) must
+ *               stay below 2 GiB (N * d * element size < 2^31), else
+ *               ATTN_ERR_UNSUPPORTED: tiles are addressed by 32-bit byte
+ *               offsets from the head's base.
  *   d           head size, 64 or 128 (others: ATTN_ERR_UNSUPPORTED).
  *   causal      1: key j is visible from row i only if j <= i. 0: no such limit.
  *   win_left    keys strictly left of the diagonal that row i may see:
