@@ -77,6 +77,8 @@ def _call(**over):
     (dict(out=FAKE + 256), ea.ATTN_ERR_INVALID_ARG, "overlaps"),
     (dict(lse=FAKE + (1 << 32) + 64), ea.ATTN_ERR_INVALID_ARG, "overlaps"),
     (dict(v=FAKE + (1 << 32) + 4096), ea.ATTN_ERR_INVALID_ARG, "overlaps"),
+    (dict(N=8388608, d=128), ea.ATTN_ERR_UNSUPPORTED, "2 GiB"),
+    (dict(N=4194304, d=128, dtype=ea.ATTN_F32), ea.ATTN_ERR_UNSUPPORTED, "2 GiB"),
     (dict(scale=-1.0), ea.ATTN_ERR_INVALID_ARG, "scale"),
     (dict(scale=float("inf")), ea.ATTN_ERR_INVALID_ARG, "scale"),
     (dict(global_idx=[0, 50], win_left=4, workspace=FAKE + (3 << 32), workspace_bytes=16),
