@@ -2,6 +2,9 @@
 """Throughput of the exact-attention forward on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--config tgt|c1|c2|c3|c4|c5]
+    python bench.py --sweep       (causal d=128 H=8 B=1, N = 512 ... 131072)
+    python bench.py --config c5 --cold   (a 1 GiB scratch write before every
+                                           timed call, so no input is in MALL)
 
 One step = one attn_fwd call (every pass the mask needs) over one batch of
 seeded synthetic inputs already resident in HBM. The default workload is
@@ -11,7 +14,8 @@ throughput target is quoted on. Useful FLOPs count visible pairs only:
 
 Prints one JSON line with the metric, a roofline object for the forward
 kernel (HIP events on the launch stream) and the CPU oracle timed on a bounded
-sample of the same workload.
+sample of the same workload. --sweep prints one JSON line per sequence length
+instead (time, useful TFLOP/s, free device memory before and after the call).
 """
 from __future__ import annotations
 
@@ -57,6 +61,17 @@ def traffic_for(config):
     if t.get("kernel_source_sha256") != source_hash():
         return None
     return t.get("hbm_bytes_per_launch")
+
+
+def blas_build():
+    try:
+        from threadpoolctl import threadpool_info
+        for i in threadpool_info():
+            if i.get("user_api") == "blas":
+                return f"{i.get('internal_api')} {i.get('version')} ({i.get('threading_layer', '')})"
+    except Exception:
+        pass
+    return "unknown"
 
 
 def blas_threads():
@@ -110,7 +125,8 @@ def cpu_baseline(w, budget_s, gpu_out=None, gpu_lse=None):
     return dict(value=flops / t_used / 1e12, unit="TFLOP/s", cores=blas_threads(), kind="oracle",
                 sample=f"{nrows} seeded query rows over {nheads} head(s) of the same workload, "
                        f"numpy fp64 full masked score rows, {t_used:.1f} s",
-                seconds=round(t_used, 2)), max_err
+                seconds=round(t_used, 2), rows=nrows, blas=blas_build(),
+                full_call_seconds_extrapolated=round(t_used * w.B * w.H * w.N / nrows, 1)), max_err
 
 
 def main():
@@ -122,6 +138,10 @@ def main():
     ap.add_argument("--config", default="tgt", choices=sorted(W.WORKLOADS))
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep", action="store_true",
+                    help="causal d=128 H=8 B=1 sequence-length sweep, one JSON line per N")
+    ap.add_argument("--cold", action="store_true",
+                    help="write a 1 GiB scratch buffer before every timed call (cold MALL)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="after timing, run one plain device copy of this many bytes "
                          "(calibration dispatch for HBM byte counters)")
@@ -140,6 +160,9 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         return 1
+
+    if args.sweep:
+        return sweep(args)
 
     w = W.WORKLOADS[args.config]
     print(f"[bench] generating {w.name}: B={w.B} H={w.H} N={w.N} d={w.d} {w.dtype}", file=sys.stderr,
@@ -167,10 +190,14 @@ def main():
         ea.fwd(q, k, v, causal=w.causal, win_left=w.win_left, win_right=w.win_right,
                global_idx=w.global_idx or None, out=out, lse=lse, workspace=ws, stream=stream)
 
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda") if args.cold else None
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    print(f"[bench] warmup done ({args.warmup}), timing {args.steps} steps", file=sys.stderr, flush=True)
+    print(f"[bench] warmup done ({args.warmup}), timing {args.steps} steps"
+          + (" (cold MALL: 1 GiB scratch write before each call)" if args.cold else ""),
+          file=sys.stderr, flush=True)
 
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
@@ -180,15 +207,18 @@ def main():
     wall0 = time.perf_counter()
     t_start.record(stream)
     for s, e in ev:
+        if scratch is not None:
+            scratch.fill_(1)
         s.record(stream)
         step()
         e.record(stream)
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    ms_step = t_start.elapsed_time(t_end) / args.steps
     launch_ms = sorted(s.elapsed_time(e) for s, e in ev)
     avg_launch_ms = sum(launch_ms) / len(launch_ms)
+    # with --cold the step is the call alone (the scratch writes are not attention work)
+    ms_step = avg_launch_ms if args.cold else t_start.elapsed_time(t_end) / args.steps
     value = flops / (ms_step * 1e-3) / 1e12
     achieved = flops / (avg_launch_ms * 1e-3) / 1e12
     peak = PEAK_F32 if w.dtype == "f32" else PEAK_BF16
@@ -224,6 +254,8 @@ def main():
                    "n_global": len(w.global_idx), "seed": w.seed,
                    "inputs": f"{w.dtype} ~N(0,{w.sigma}^2)", "useful_flop_per_step": flops},
         "pct_bf16_peak": round(100.0 * value / PEAK_BF16, 2),
+        "median_launch_ms": round(launch_ms[len(launch_ms) // 2], 4),
+        "mall": "cold" if args.cold else "warm",
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": traffic_for(args.config),
@@ -234,9 +266,61 @@ def main():
     if not args.no_cpu_baseline:
         print(f"[bench] timing the CPU oracle for ~{args.cpu_seconds:.0f} s", file=sys.stderr, flush=True)
         cb, err = cpu_baseline(w, args.cpu_seconds, out, lse)
+        cb["gpu_over_oracle"] = round(value / cb["value"], 1)
         result["cpu_baseline"] = cb
         result["sample_max_abs_err_vs_oracle"] = err
     print(json.dumps(result), flush=True)
+    return 0
+
+
+def sweep(args):
+    """Causal d=128, H=8, B=1 over N = 512 ... 131072: median launch time of
+    the attn_fwd call (at least 20 calls or 1 s), useful TFLOP/s, and the free
+    device memory just before and just after the call."""
+    import torch
+    import efficient_exact_attention_amd as ea
+    from efficient_exact_attention_amd import workloads as W
+    N = 512
+    while N <= 131072:
+        w = W.random_workload(f"sweep{N}", 1, 8, N, 128, causal=1, seed=200 + N.bit_length())
+        q, k, v = (torch.from_numpy(x.view("int16")).view(torch.bfloat16).cuda() for x in W.make_qkv(w))
+        out = torch.empty_like(q)
+        lse = torch.empty(1, 8, N, dtype=torch.float32, device="cuda")
+        pairs = ea.attn_plan_stats(N, 1, -1, -1, None, 128, 64)[0]
+        flops = 4 * 128 * pairs * 8
+        stream = torch.cuda.current_stream()
+
+        def call():
+            ea.fwd(q, k, v, causal=1, out=out, lse=lse, stream=stream)
+        for _ in range(args.warmup):
+            call()
+        torch.cuda.synchronize()
+        free0, total = torch.cuda.mem_get_info()
+        call()
+        torch.cuda.synchronize()
+        free1, _ = torch.cuda.mem_get_info()
+        times = []
+        t_end = time.perf_counter() + 1.0
+        while len(times) < max(20, args.steps) or time.perf_counter() < t_end:
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record(stream)
+            call()
+            e.record(stream)
+            e.synchronize()
+            times.append(s.elapsed_time(e))
+            if len(times) >= 2000:
+                break
+        times.sort()
+        ms = times[len(times) // 2]
+        print(json.dumps({"N": N, "B": 1, "H": 8, "d": 128, "causal": 1, "calls": len(times),
+                          "median_ms": round(ms, 4), "useful_tflops": round(flops / ms / 1e9, 1),
+                          "pct_bf16_peak": round(100 * flops / ms / 1e9 / PEAK_BF16, 2),
+                          "free_gib_before": round(free0 / 2**30, 3), "free_gib_after": round(free1 / 2**30, 3),
+                          "inputs_outputs_mib": round((4 * q.numel() * 2 + lse.numel() * 4) / 2**20, 1)}),
+              flush=True)
+        del q, k, v, out, lse
+        torch.cuda.empty_cache()
+        N *= 2
     return 0
 
 

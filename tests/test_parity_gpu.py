@@ -61,6 +61,15 @@ def test_small_fp32(mask, N, d):
     check(w, o, l, all_heads(w), np.arange(N), qkv, tol=(1e-4, 1e-5, 1e-4))
 
 
+def test_ragged_4097_all_rows():
+    """N = 4097: 16 full 256-row query tiles plus a one-row tail, whose key
+    tile holds a single valid key."""
+    w = W.random_workload("rag4097", 1, 2, 4097, 128, causal=1, seed=14)
+    qkv = W.make_qkv(w)
+    o, l = run_gpu(w, qkv)
+    check(w, o, l, all_heads(w), np.arange(w.N), qkv)
+
+
 def test_many_globals():
     g = tuple(range(0, 2000, 33))[:64]
     w = W.random_workload("g64", 1, 2, 2000, 64, causal=0, win_left=20, win_right=20,
