@@ -9,7 +9,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["AttnError", "attn_fwd", "attn_fwd_ex", "attn_workspace_bytes", "attn_plan_stats",
+__all__ = ["AttnError", "attn_fwd", "attn_fwd_ex", "attn_fwd_gqa", "attn_workspace_bytes", "attn_plan_stats",
            "attn_tile_shape", "attn_last_error", "attn_version", "fwd", "library_path",
            "ATTN_OK", "ATTN_ERR_INVALID_ARG", "ATTN_ERR_UNSUPPORTED", "ATTN_ERR_DEVICE",
            "ATTN_BF16", "ATTN_F32"]
@@ -53,6 +53,9 @@ def lib():
     L.attn_fwd.restype = ci
     L.attn_fwd_ex.argtypes = fwd_args + [ctypes.POINTER(_Opts)]
     L.attn_fwd_ex.restype = ci
+    L.attn_fwd_gqa.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, ci, ctypes.POINTER(ci), ci,
+                               ctypes.POINTER(_Opts)]
+    L.attn_fwd_gqa.restype = ci
     L.attn_workspace_bytes.argtypes = [ci, ci, ci, ci, ci]
     L.attn_workspace_bytes.restype = ctypes.c_size_t
     ll = ctypes.POINTER(ctypes.c_longlong)
@@ -103,6 +106,15 @@ def attn_fwd_ex(q, k, v, out, lse, B, H, N, d, causal, win_left, win_right, glob
                              ctypes.byref(opts)))
 
 
+def attn_fwd_gqa(q, k, v, out, lse, B, H, H_kv, N, d, causal, win_left, win_right, global_idx=None,
+                 *, dtype=ATTN_BF16, scale=0.0, stream=None, workspace=None, workspace_bytes=0):
+    """Raw grouped-query entry point: k and v hold H_kv heads per batch entry."""
+    g, ng = _gidx(global_idx)
+    opts = _Opts(dtype, float(scale), stream, workspace, workspace_bytes)
+    _check(lib().attn_fwd_gqa(q, k, v, out, lse, B, H, H_kv, N, d, causal, win_left, win_right, g, ng,
+                              ctypes.byref(opts)))
+
+
 def attn_workspace_bytes(B, H, N, d, n_global) -> int:
     return int(lib().attn_workspace_bytes(B, H, N, d, n_global))
 
@@ -124,7 +136,9 @@ def attn_tile_shape(d, dtype=ATTN_BF16):
 
 def fwd(q, k, v, *, causal=False, win_left=-1, win_right=-1, global_idx=None, scale=None,
         out=None, lse=None, workspace=None, stream=None):
-    """Attention forward on torch CUDA tensors [B, H, N, d] (bf16 or fp32).
+    """Attention forward on torch CUDA tensors: q [B, H, N, d], k and v
+    [B, H_kv, N, d] with H_kv dividing H (H_kv = H: multi-head; H_kv < H:
+    grouped-query; H_kv = 1: multi-query), bf16 or fp32.
 
     Allocates ``out`` (input dtype) and ``lse`` (fp32 [B, H, N]) with torch
     unless given, enqueues the kernels on torch's current stream (or
@@ -133,14 +147,17 @@ def fwd(q, k, v, *, causal=False, win_left=-1, win_right=-1, global_idx=None, sc
     import torch
     if q.dtype not in (torch.bfloat16, torch.float32):
         raise ValueError(f"unsupported dtype {q.dtype}")
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        if t.dtype != q.dtype or t.shape != q.shape:
-            raise ValueError(f"{name} must match q in dtype and shape")
-        if not t.is_cuda or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous device tensor")
-    if q.dim() != 4:
+    if q.dim() != 4 or k.dim() != 4:
         raise ValueError("tensors must be [B, H, N, d]")
     B, H, N, d = q.shape
+    H_kv = k.shape[1]
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype != q.dtype or (t.shape[0], t.shape[2], t.shape[3]) != (B, N, d):
+            raise ValueError(f"{name} must match q in dtype, batch, length and head size")
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    if v.shape != k.shape:
+        raise ValueError("k and v must have the same shape")
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
@@ -155,9 +172,9 @@ def fwd(q, k, v, *, causal=False, win_left=-1, win_right=-1, global_idx=None, sc
         stream = stream.cuda_stream
     ws, wsb = (workspace.data_ptr(), workspace.numel() * workspace.element_size()) \
         if workspace is not None else (None, 0)
-    attn_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                B, H, N, d, int(bool(causal)), int(win_left), int(win_right), global_idx,
-                dtype=ATTN_F32 if q.dtype == torch.float32 else ATTN_BF16,
-                scale=0.0 if scale is None else float(scale), stream=stream,
-                workspace=ws, workspace_bytes=wsb)
+    attn_fwd_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                 B, H, H_kv, N, d, int(bool(causal)), int(win_left), int(win_right), global_idx,
+                 dtype=ATTN_F32 if q.dtype == torch.float32 else ATTN_BF16,
+                 scale=0.0 if scale is None else float(scale), stream=stream,
+                 workspace=ws, workspace_bytes=wsb)
     return out, lse

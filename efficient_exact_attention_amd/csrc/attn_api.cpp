@@ -159,14 +159,22 @@ int attn_plan_stats(int N, int causal, int win_left, int win_right, const int *g
     return ATTN_OK;
 }
 
-int attn_fwd_ex(const void *q, const void *k, const void *v, void *out, float *lse, int B, int H, int N, int d,
-                int causal, int win_left, int win_right, const int *global_idx, int n_global,
-                const attn_opts *opts) {
+}  // extern "C"
+
+namespace {
+
+// The forward call with H_kv K/V heads per batch entry (H_kv == H: plain
+// multi-head attention).
+int fwd_impl(const void *q, const void *k, const void *v, void *out, float *lse, int B, int H, int H_kv, int N,
+             int d, int causal, int win_left, int win_right, const int *global_idx, int n_global,
+             const attn_opts *opts) {
     g_err.clear();
     const int dtype = opts ? opts->dtype : ATTN_BF16;
     if (!q || !k || !v || !out || !lse) return fail(ATTN_ERR_INVALID_ARG, "a tensor pointer is NULL");
     if (B <= 0 || H <= 0 || N <= 0)
         return fail(ATTN_ERR_INVALID_ARG, "sizes B=%d H=%d N=%d must be positive", B, H, N);
+    if (H_kv <= 0 || H % H_kv != 0)
+        return fail(ATTN_ERR_INVALID_ARG, "H_kv=%d must be positive and divide H=%d", H_kv, H);
     if (dtype != ATTN_BF16 && dtype != ATTN_F32) return fail(ATTN_ERR_INVALID_ARG, "unknown dtype %d", dtype);
     if (causal != 0 && causal != 1) return fail(ATTN_ERR_INVALID_ARG, "causal=%d must be 0 or 1", causal);
     if (win_left < -1 || win_right < -1)
@@ -185,14 +193,15 @@ int attn_fwd_ex(const void *q, const void *k, const void *v, void *out, float *l
     if ((long long)N * d * (long long)esize > INT_MAX)
         return fail(ATTN_ERR_UNSUPPORTED, "one head's K of N=%d x d=%d elements exceeds 2 GiB", N, d);
     const size_t tbytes = (size_t)BH * N * d * esize;   // < 2^31 * 2^31 * 128 * 4: fits in 64 bits
+    const size_t kvbytes = (size_t)B * H_kv * N * d * esize;
     const size_t lbytes = (size_t)BH * N * sizeof(float);
 
     if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out) & 15)
         return fail(ATTN_ERR_INVALID_ARG, "q, k, v and out must be 16-byte aligned");
     if ((uintptr_t)lse & 3) return fail(ATTN_ERR_INVALID_ARG, "lse must be 4-byte aligned");
-    if (overlaps(out, tbytes, q, tbytes) || overlaps(out, tbytes, k, tbytes) || overlaps(out, tbytes, v, tbytes))
+    if (overlaps(out, tbytes, q, tbytes) || overlaps(out, tbytes, k, kvbytes) || overlaps(out, tbytes, v, kvbytes))
         return fail(ATTN_ERR_INVALID_ARG, "out overlaps an input tensor");
-    if (overlaps(lse, lbytes, q, tbytes) || overlaps(lse, lbytes, k, tbytes) || overlaps(lse, lbytes, v, tbytes) ||
+    if (overlaps(lse, lbytes, q, tbytes) || overlaps(lse, lbytes, k, kvbytes) || overlaps(lse, lbytes, v, kvbytes) ||
         overlaps(lse, lbytes, out, tbytes))
         return fail(ATTN_ERR_INVALID_ARG, "lse overlaps another tensor");
 
@@ -212,6 +221,8 @@ int attn_fwd_ex(const void *q, const void *k, const void *v, void *out, float *l
     p.lse = lse;
     p.head_stride = (long long)N * d;
     p.BH = (int)BH;
+    p.H = H;
+    p.group = H / H_kv;
     p.N = N;
     p.wl = band.wl;
     p.wr = band.wr;
@@ -276,9 +287,26 @@ int attn_fwd_ex(const void *q, const void *k, const void *v, void *out, float *l
     return ATTN_OK;
 }
 
+}  // namespace
+
+extern "C" {
+
+int attn_fwd_ex(const void *q, const void *k, const void *v, void *out, float *lse, int B, int H, int N, int d,
+                int causal, int win_left, int win_right, const int *global_idx, int n_global,
+                const attn_opts *opts) {
+    return fwd_impl(q, k, v, out, lse, B, H, H, N, d, causal, win_left, win_right, global_idx, n_global, opts);
+}
+
+int attn_fwd_gqa(const void *q, const void *k, const void *v, void *out, float *lse, int B, int H, int H_kv,
+                 int N, int d, int causal, int win_left, int win_right, const int *global_idx, int n_global,
+                 const attn_opts *opts) {
+    return fwd_impl(q, k, v, out, lse, B, H, H_kv, N, d, causal, win_left, win_right, global_idx, n_global,
+                    opts);
+}
+
 int attn_fwd(const void *q, const void *k, const void *v, void *out, float *lse, int B, int H, int N, int d,
              int causal, int win_left, int win_right, const int *global_idx, int n_global) {
-    return attn_fwd_ex(q, k, v, out, lse, B, H, N, d, causal, win_left, win_right, global_idx, n_global, nullptr);
+    return fwd_impl(q, k, v, out, lse, B, H, H, N, d, causal, win_left, win_right, global_idx, n_global, nullptr);
 }
 
 }  // extern "C"

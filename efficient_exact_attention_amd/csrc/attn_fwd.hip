@@ -574,8 +574,8 @@ __global__ void __launch_bounds__(P::NT) fwd_kernel(const FwdParams prm) {
         unit = Lw - bh * prm.chunks;
     }
     const elem_t *qh = static_cast<const elem_t *>(prm.q) + (long long)bh * prm.head_stride;
-    const elem_t *kh = static_cast<const elem_t *>(prm.k) + (long long)bh * prm.head_stride;
-    const elem_t *vh = static_cast<const elem_t *>(prm.v) + (long long)bh * prm.head_stride;
+    const elem_t *kh = static_cast<const elem_t *>(prm.k) + kv_head(prm, bh) * prm.head_stride;
+    const elem_t *vh = static_cast<const elem_t *>(prm.v) + kv_head(prm, bh) * prm.head_stride;
 
     typename P::Lane L;
     P::init_lane(L, lane, wave);
@@ -963,8 +963,8 @@ __global__ void __launch_bounds__(512) fwd_band_bf16(const FwdParams prm) {
     const int qi = Lw - bh * prm.num_qt;
     const int unit = prm.causal ? prm.num_qt - 1 - qi : qi;
     const uint16_t *qh = static_cast<const uint16_t *>(prm.q) + (long long)bh * prm.head_stride;
-    const uint16_t *kh = static_cast<const uint16_t *>(prm.k) + (long long)bh * prm.head_stride;
-    const uint16_t *vh = static_cast<const uint16_t *>(prm.v) + (long long)bh * prm.head_stride;
+    const uint16_t *kh = static_cast<const uint16_t *>(prm.k) + kv_head(prm, bh) * prm.head_stride;
+    const uint16_t *vh = static_cast<const uint16_t *>(prm.v) + kv_head(prm, bh) * prm.head_stride;
 
     typename P::Lane L;
     P::init_lane(L, lane, wave);

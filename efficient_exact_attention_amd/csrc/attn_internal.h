@@ -19,7 +19,9 @@ struct FwdParams {
     float *lse;
     float *part;          // global-row partials [B*H][n_global][chunks][d + 2]
     long long head_stride;  // N * d elements
-    int BH;               // B * H
+    int BH;               // B * H (query heads)
+    int H;                // query heads per batch entry
+    int group;            // query heads per K/V head (H / H_kv; 1 for plain multi-head)
     int N;
     int wl, wr;           // normalised band (see attn_plan.h)
     int causal;
@@ -31,6 +33,13 @@ struct FwdParams {
     float scale_log2;     // score scale * log2(e)
     int gidx[kMaxGlobal]; // sorted global positions
 };
+
+// K/V head (over B * H_kv) read by query head bh (over B * H): query heads
+// h = g*group .. g*group + group - 1 of one batch entry share K/V head g.
+__host__ __device__ __forceinline__ long long kv_head(const FwdParams &p, int bh) {
+    const int b = bh / p.H, h = bh - b * p.H;
+    return (long long)b * (p.H / p.group) + h / p.group;
+}
 
 // Tile shapes chosen per (d, dtype).
 int tile_bm(int d, int f32);

@@ -103,6 +103,26 @@ int attn_fwd_ex(const void *q, const void *k, const void *v, void *out, float *l
                 const int *global_idx, int n_global, const attn_opts *opts);
 
 /*
+ * attn_fwd_gqa - as attn_fwd_ex with fewer K/V heads than query heads:
+ * grouped-query attention (H_kv groups of H/H_kv query heads, each group
+ * sharing one K head and one V head) and, with H_kv = 1, multi-query
+ * attention (one K/V head for every query head). Both are exact attention
+ * with K and V shared, not an approximation (week-17 lecture notes on
+ * efficient attention, the MQA / GQA passage on shrinking the KV cache).
+ *
+ *   q, out      [B][H][N][d]
+ *   k, v        [B][H_kv][N][d]; query head h of batch entry b reads K/V
+ *               head h / (H / H_kv) of the same b.
+ *   H_kv        >= 1 and divides H (else ATTN_ERR_INVALID_ARG). H_kv = H is
+ *               exactly attn_fwd_ex.
+ * Every other argument, the outputs, the workspace and the error behaviour
+ * are those of attn_fwd_ex (the workspace depends on B*H, not on H_kv).
+ */
+int attn_fwd_gqa(const void *q, const void *k, const void *v, void *out, float *lse,
+                 int B, int H, int H_kv, int N, int d, int causal, int win_left, int win_right,
+                 const int *global_idx, int n_global, const attn_opts *opts);
+
+/*
  * attn_workspace_bytes - device scratch a call with these sizes needs for the
  * global-row partial results; 0 when n_global = 0. It grows with
  * B*H*n_global*d and a chunk count bounded by N/64, never with N*N.

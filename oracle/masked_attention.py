@@ -84,7 +84,12 @@ def attention(q, k, v, *, causal: int, win_left: int = -1, win_right: int = -1,
               row_block: int = 256):
     """Masked softmax attention in fp64.
 
-    q, k, v: [B, H, N, d] arrays (any real dtype; upcast to float64).
+    q:       [B, H, N, d]; k, v: [B, H_kv, N, d] with H_kv dividing H (any
+             real dtype; upcast to float64). H_kv < H is grouped-query
+             attention and H_kv = 1 multi-query attention (week-17 notes, the
+             MQA / GQA passage: groups of query heads share one K and one V
+             head). Reading: the groups are runs of consecutive query heads,
+             query head h using K/V head h // (H // H_kv).
     rows:    optional 1-D array of query rows to compute (default: all).
     Returns (O [B, H, R, d] float64, LSE [B, H, R] float64).
     """
@@ -92,6 +97,10 @@ def attention(q, k, v, *, causal: int, win_left: int = -1, win_right: int = -1,
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
     B, H, N, d = q.shape
+    H_kv = k.shape[1]
+    if H_kv < 1 or H % H_kv or v.shape[1] != H_kv:
+        raise ValueError(f"K/V heads {H_kv} must divide query heads {H}")
+    group = H // H_kv
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     rows = np.arange(N) if rows is None else np.asarray(rows, dtype=np.int64)
@@ -104,14 +113,15 @@ def attention(q, k, v, *, causal: int, win_left: int = -1, win_right: int = -1,
         any_vis = vis.any(axis=1)
         for b in range(B):
             for h in range(H):
-                s = (q[b, h, rb] @ k[b, h].T) * scale          # full score rows
+                kh = h // group                                # shared K/V head
+                s = (q[b, h, rb] @ k[b, kh].T) * scale         # full score rows
                 s = np.where(vis, s, -np.inf)
                 m = s.max(axis=1, keepdims=True)
                 m = np.where(np.isfinite(m), m, 0.0)
                 p = np.exp(s - m)                              # masked -> 0
                 l = p.sum(axis=1, keepdims=True)
                 safe_l = np.where(l > 0, l, 1.0)
-                out[b, h, r0:r0 + len(rb)] = np.where(any_vis[:, None], (p @ v[b, h]) / safe_l, 0.0)
+                out[b, h, r0:r0 + len(rb)] = np.where(any_vis[:, None], (p @ v[b, kh]) / safe_l, 0.0)
                 lse[b, h, r0:r0 + len(rb)] = np.where(any_vis, m[:, 0] + np.log(safe_l[:, 0]), -np.inf)
     return out, lse
 

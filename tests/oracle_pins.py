@@ -231,9 +231,34 @@ def pin_torch_sdpa(attn):
     assert np.max(np.abs(O - ref.numpy())) <= 1e-12
 
 
+def pin_grouped_heads(attn):
+    """Grouped-query and multi-query attention (week-17 notes, the MQA / GQA
+    passage: groups of query heads share one K and one V head) against
+    torch's SDPA with enable_gqa, which repeats each K/V head over a run of
+    consecutive query heads: H = 6 query heads with H_kv = 6, 3, 2 and 1, under
+    a causal and a windowed mask."""
+    import torch
+    import torch.nn.functional as F
+    masks = [dict(causal=1, win_left=-1, win_right=-1, global_idx=()),
+             dict(causal=0, win_left=9, win_right=4, global_idx=(0, 77))]
+    for t, H_kv in enumerate((6, 3, 2, 1)):
+        rng = np.random.default_rng(81 + t)
+        N, d = 150 + 11 * t, 16
+        q = rng.standard_normal((2, 6, N, d))
+        k = rng.standard_normal((2, H_kv, N, d))
+        v = rng.standard_normal((2, H_kv, N, d))
+        for m in masks:
+            O, _ = attn(q, k, v, **m)
+            mask = np.array([[loop_visible(i, j, N, m) for j in range(N)] for i in range(N)])
+            ref = F.scaled_dot_product_attention(torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v),
+                                                 attn_mask=torch.from_numpy(mask), enable_gqa=True)
+            assert O.shape == (2, 6, N, d)
+            assert np.max(np.abs(O - ref.numpy())) <= 1e-12, (H_kv, m)
+
+
 ALL_PINS = ["pin_bruteforce", "pin_closed_forms", "pin_constant_v", "pin_identical_keys",
             "pin_window_covers_causal", "pin_key_shift", "pin_permutation",
-            "pin_special_cases", "pin_torch_sdpa"]
+            "pin_special_cases", "pin_torch_sdpa", "pin_grouped_heads"]
 
 
 def run_pin(name, attn):

@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert {"attn_fwd", "attn_fwd_ex", "attn_workspace_bytes", "attn_plan_stats",
+    assert {"attn_fwd", "attn_fwd_ex", "attn_fwd_gqa", "attn_workspace_bytes", "attn_plan_stats",
             "attn_last_error", "attn_version", "attn_tile_shape"} <= set(names)
     L = ctypes.CDLL(ea.library_path())
     for n in names:
@@ -88,6 +88,36 @@ def test_validation(over, status, text):
     err = _call(**over)
     assert err.status == status
     assert text in err.message
+
+
+def _call_gqa(H, H_kv, scale=0.0, **over):
+    a = dict(q=FAKE, k=FAKE + (3 << 32), v=FAKE + (4 << 32), out=FAKE + (1 << 32), lse=FAKE + (2 << 32),
+             B=2, N=100, d=128)
+    a.update(over)
+    with pytest.raises(ea.AttnError) as ei:
+        ea.attn_fwd_gqa(a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"], H, H_kv, a["N"], a["d"],
+                        1, -1, -1, None, scale=scale)
+    return ei.value
+
+
+@pytest.mark.parametrize("H,H_kv", [(8, 0), (8, -1), (8, 3), (6, 4), (4, 8)])
+def test_gqa_head_counts(H, H_kv):
+    err = _call_gqa(H, H_kv)
+    assert err.status == ea.ATTN_ERR_INVALID_ARG
+    assert "H_kv" in err.message
+
+
+def test_gqa_overlap_uses_kv_size():
+    """k holds B*H_kv heads (here 2): an out buffer inside them is rejected,
+    one starting right after them passes the overlap check (the call is
+    then stopped by the invalid scale, which is checked after it, so no case
+    reaches the device)."""
+    head = 100 * 128 * 2
+    kv = FAKE + (3 << 32)
+    err = _call_gqa(8, 1, k=kv, out=kv + head)
+    assert "overlaps" in err.message
+    err = _call_gqa(8, 1, scale=-1.0, k=kv, v=kv + (1 << 30), out=kv + 2 * head, lse=kv + (1 << 31))
+    assert "scale" in err.message
 
 
 def test_inputs_may_alias():

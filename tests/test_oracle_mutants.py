@@ -15,7 +15,7 @@ def _fails(attn, monkey=None):
     for name in P.ALL_PINS:
         try:
             P.run_pin(name, attn)
-        except AssertionError:
+        except (AssertionError, ValueError):   # a pin the mutant cannot even run also catches it
             failed.append(name)
     return failed
 
@@ -67,8 +67,22 @@ def causal_ignored(q, k, v, **kw):
     return oracle.attention(q, k, v, **dict(kw, causal=0))
 
 
+def groups_interleaved(q, k, v, **kw):
+    # query head h reads K/V head h % H_kv instead of h // (H / H_kv)
+    H, H_kv = q.shape[1], k.shape[1]
+    idx = [h % H_kv for h in range(H)]
+    return oracle.attention(q, k[:, idx], v[:, idx], **kw)
+
+
+def first_kv_head_only(q, k, v, **kw):
+    # every query head reads K/V head 0
+    H = q.shape[1]
+    return oracle.attention(q, k[:, [0] * H], v[:, [0] * H], **kw)
+
+
 MUTANTS = [no_scale, swapped_kv, transposed_scores, lse_log2, lse_unscaled, sign_flip,
-           globals_dropped, window_shift_left, window_right_ignored, causal_ignored]
+           globals_dropped, window_shift_left, window_right_ignored, causal_ignored,
+           groups_interleaved, first_kv_head_only]
 
 
 @pytest.mark.parametrize("mutant", MUTANTS, ids=lambda f: f.__name__)
