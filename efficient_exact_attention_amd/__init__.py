@@ -9,7 +9,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["AttnError", "attn_fwd", "attn_fwd_ex", "attn_fwd_gqa", "attn_workspace_bytes", "attn_plan_stats",
+__all__ = ["AttnError", "attn_fwd", "attn_fwd_ex", "attn_fwd_gqa", "attn_bwd", "attn_bwd_workspace_bytes", "bwd", "attn_workspace_bytes", "attn_plan_stats",
            "attn_tile_shape", "attn_last_error", "attn_version", "fwd", "library_path",
            "ATTN_OK", "ATTN_ERR_INVALID_ARG", "ATTN_ERR_UNSUPPORTED", "ATTN_ERR_DEVICE",
            "ATTN_BF16", "ATTN_F32"]
@@ -56,6 +56,11 @@ def lib():
     L.attn_fwd_gqa.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, ci, ctypes.POINTER(ci), ci,
                                ctypes.POINTER(_Opts)]
     L.attn_fwd_gqa.restype = ci
+    L.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, ci,
+                           ctypes.POINTER(ci), ci, ctypes.POINTER(_Opts)]
+    L.attn_bwd.restype = ci
+    L.attn_bwd_workspace_bytes.argtypes = [ci, ci, ci, ci]
+    L.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
     L.attn_workspace_bytes.argtypes = [ci, ci, ci, ci, ci]
     L.attn_workspace_bytes.restype = ctypes.c_size_t
     ll = ctypes.POINTER(ctypes.c_longlong)
@@ -113,6 +118,19 @@ def attn_fwd_gqa(q, k, v, out, lse, B, H, H_kv, N, d, causal, win_left, win_righ
     opts = _Opts(dtype, float(scale), stream, workspace, workspace_bytes)
     _check(lib().attn_fwd_gqa(q, k, v, out, lse, B, H, H_kv, N, d, causal, win_left, win_right, g, ng,
                               ctypes.byref(opts)))
+
+
+def attn_bwd(q, k, v, out, dout, lse, dq, dk, dv, B, H, H_kv, N, d, causal, win_left, win_right,
+             global_idx=None, *, dtype=ATTN_BF16, scale=0.0, stream=None, workspace=None, workspace_bytes=0):
+    """Raw backward entry point: every tensor is an integer device address."""
+    g, ng = _gidx(global_idx)
+    opts = _Opts(dtype, float(scale), stream, workspace, workspace_bytes)
+    _check(lib().attn_bwd(q, k, v, out, dout, lse, dq, dk, dv, B, H, H_kv, N, d, causal, win_left, win_right,
+                          g, ng, ctypes.byref(opts)))
+
+
+def attn_bwd_workspace_bytes(B, H, N, d) -> int:
+    return int(lib().attn_bwd_workspace_bytes(B, H, N, d))
 
 
 def attn_workspace_bytes(B, H, N, d, n_global) -> int:
@@ -178,3 +196,38 @@ def fwd(q, k, v, *, causal=False, win_left=-1, win_right=-1, global_idx=None, sc
                  scale=0.0 if scale is None else float(scale), stream=stream,
                  workspace=ws, workspace_bytes=wsb)
     return out, lse
+
+
+def bwd(q, k, v, out, dout, lse, *, causal=False, win_left=-1, win_right=-1, global_idx=None, scale=None,
+        dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """Gradients (dq, dk, dv) of ``fwd`` on torch CUDA bf16 tensors: q, out,
+    dout [B, H, N, d], k, v [B, H_kv, N, d], lse fp32 [B, H, N] from the
+    forward call with the same mask and scale. Allocates the gradients with
+    torch unless given and enqueues the kernels without synchronising."""
+    import torch
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("tensors must be [B, H, N, d]")
+    B, H, N, d = q.shape
+    H_kv = k.shape[1]
+    for name, t, shape in (("q", q, q.shape), ("out", out, q.shape), ("dout", dout, q.shape),
+                           ("k", k, k.shape), ("v", v, k.shape)):
+        if t.dtype != torch.bfloat16 or t.shape != shape or (t.shape[0], t.shape[2], t.shape[3]) != (B, N, d):
+            raise ValueError(f"{name} must be bf16 and shaped consistently with q")
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous fp32 tensor [B, H, N]")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    ws, wsb = (workspace.data_ptr(), workspace.numel() * workspace.element_size()) \
+        if workspace is not None else (None, 0)
+    attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+             dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, H_kv, N, d, int(bool(causal)), int(win_left),
+             int(win_right), global_idx, scale=0.0 if scale is None else float(scale), stream=stream,
+             workspace=ws, workspace_bytes=wsb)
+    return dq, dk, dv

@@ -38,8 +38,10 @@ int fail(int code, const char *fmt, ...) {
 struct DeviceSlot {
     int arch_checked = 0;
     int arch_ok = 0;
-    void *scratch = nullptr;
+    void *scratch = nullptr;        // forward: global-row partials
     size_t scratch_bytes = 0;
+    void *bwd_scratch = nullptr;    // backward: per-row terms
+    size_t bwd_scratch_bytes = 0;
 };
 std::mutex g_mu;
 std::vector<DeviceSlot> g_dev;
@@ -287,9 +289,168 @@ int fwd_impl(const void *q, const void *k, const void *v, void *out, float *lse,
     return ATTN_OK;
 }
 
+// Current device, checked to be gfx950, and (when need > 0 and the caller
+// gave no workspace) a per-device scratch buffer of at least `need` bytes,
+// grown under the mutex and never freed while in use by this library.
+int device_and_scratch(size_t need, void **buf, bool backward) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(ATTN_ERR_DEVICE, "hipGetDevice: %s", hipGetErrorString(e));
+    std::lock_guard<std::mutex> lk(g_mu);
+    DeviceSlot &s = slot(dev);
+    if (!s.arch_checked) {
+        hipDeviceProp_t prop;
+        e = hipGetDeviceProperties(&prop, dev);
+        if (e != hipSuccess) return fail(ATTN_ERR_DEVICE, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+        s.arch_ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+        s.arch_checked = 1;
+    }
+    if (!s.arch_ok) return fail(ATTN_ERR_UNSUPPORTED, "device %d is not gfx950 (MI355X)", dev);
+    if (need == 0 || !buf || *buf) return ATTN_OK;
+    void *&ptr = backward ? s.bwd_scratch : s.scratch;
+    size_t &bytes = backward ? s.bwd_scratch_bytes : s.scratch_bytes;
+    if (bytes < need) {
+        if (ptr) {
+            e = hipFree(ptr);
+            ptr = nullptr;
+            bytes = 0;
+            if (e != hipSuccess) return fail(ATTN_ERR_DEVICE, "hipFree: %s", hipGetErrorString(e));
+        }
+        e = hipMalloc(&ptr, need);
+        if (e != hipSuccess) {
+            ptr = nullptr;
+            return fail(ATTN_ERR_DEVICE, "hipMalloc(%zu): %s", need, hipGetErrorString(e));
+        }
+        bytes = need;
+    }
+    *buf = ptr;
+    return ATTN_OK;
+}
+
+size_t bwd_workspace(long long BH, int N) {
+    const size_t raw = (size_t)BH * N * sizeof(float);
+    return (raw + 255) & ~(size_t)255;
+}
+
+int bwd_impl(const void *q, const void *k, const void *v, const void *out, const void *dout, const float *lse,
+             void *dq, void *dk, void *dv, int B, int H, int H_kv, int N, int d, int causal, int win_left,
+             int win_right, const int *global_idx, int n_global, const attn_opts *opts) {
+    g_err.clear();
+    const int dtype = opts ? opts->dtype : ATTN_BF16;
+    if (!q || !k || !v || !out || !dout || !lse || !dq || !dk || !dv)
+        return fail(ATTN_ERR_INVALID_ARG, "a tensor pointer is NULL");
+    if (B <= 0 || H <= 0 || N <= 0)
+        return fail(ATTN_ERR_INVALID_ARG, "sizes B=%d H=%d N=%d must be positive", B, H, N);
+    if (H_kv <= 0 || H % H_kv != 0)
+        return fail(ATTN_ERR_INVALID_ARG, "H_kv=%d must be positive and divide H=%d", H_kv, H);
+    if (dtype != ATTN_BF16 && dtype != ATTN_F32) return fail(ATTN_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+    if (dtype == ATTN_F32) return fail(ATTN_ERR_UNSUPPORTED, "the backward pass supports bf16 tensors only");
+    if (causal != 0 && causal != 1) return fail(ATTN_ERR_INVALID_ARG, "causal=%d must be 0 or 1", causal);
+    if (win_left < -1 || win_right < -1)
+        return fail(ATTN_ERR_INVALID_ARG, "window (%d, %d) must be >= -1", win_left, win_right);
+    if (d != 64 && d != 128) return fail(ATTN_ERR_UNSUPPORTED, "head size d=%d is not supported (64 or 128)", d);
+    std::vector<int> G;
+    int rc = check_globals(global_idx, n_global, N, G);
+    if (rc != ATTN_OK) return rc;
+    const eea::Band band = eea::make_band(N, causal, win_left, win_right);
+    if (n_global > 0 && !eea::band_is_everything(band, causal))
+        return fail(ATTN_ERR_UNSUPPORTED, "the backward pass does not support global tokens");
+
+    const long long BH = (long long)B * H;
+    const int bq = eea::bwd_tile_q(d), bk = eea::bwd_tile_k(d);
+    const long long nqt = (N + (long long)bq - 1) / bq, nkt = (N + (long long)bk - 1) / bk;
+    if (BH > INT_MAX || BH * nqt > INT_MAX || (long long)B * H_kv * nkt > INT_MAX)
+        return fail(ATTN_ERR_INVALID_ARG, "B*H=%lld with N=%d exceeds the launch grid", BH, N);
+    if ((long long)N * d * 2 > INT_MAX)
+        return fail(ATTN_ERR_UNSUPPORTED, "one head's K of N=%d x d=%d elements exceeds 2 GiB", N, d);
+    const size_t qbytes = (size_t)BH * N * d * 2;
+    const size_t kvbytes = (size_t)B * H_kv * N * d * 2;
+    const size_t lbytes = (size_t)BH * N * sizeof(float);
+    if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out | (uintptr_t)dout | (uintptr_t)dq |
+         (uintptr_t)dk | (uintptr_t)dv) & 15)
+        return fail(ATTN_ERR_INVALID_ARG, "q, k, v, out, dout, dq, dk and dv must be 16-byte aligned");
+    if ((uintptr_t)lse & 3) return fail(ATTN_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+    const void *ins[6] = {q, k, v, out, dout, lse};
+    const size_t insz[6] = {qbytes, kvbytes, kvbytes, qbytes, qbytes, lbytes};
+    void *outs[3] = {dq, dk, dv};
+    const size_t outsz[3] = {qbytes, kvbytes, kvbytes};
+    for (int a = 0; a < 3; ++a) {
+        for (int i = 0; i < 6; ++i)
+            if (overlaps(outs[a], outsz[a], ins[i], insz[i]))
+                return fail(ATTN_ERR_INVALID_ARG, "gradient output %d overlaps an input tensor", a);
+        for (int o = 0; o < a; ++o)
+            if (overlaps(outs[a], outsz[a], outs[o], outsz[o]))
+                return fail(ATTN_ERR_INVALID_ARG, "gradient outputs %d and %d overlap", o, a);
+    }
+    const float scale = (opts && opts->scale != 0.f) ? opts->scale : 1.0f / std::sqrt((float)d);
+    if (!(scale > 0.f) || !std::isfinite(scale))
+        return fail(ATTN_ERR_INVALID_ARG, "scale must be positive and finite");
+
+    const size_t need = bwd_workspace(BH, N);
+    void *ws = nullptr;
+    if (opts && opts->workspace) {
+        if (opts->workspace_bytes < need)
+            return fail(ATTN_ERR_INVALID_ARG, "workspace of %zu bytes is smaller than the %zu needed",
+                        opts->workspace_bytes, need);
+        if ((uintptr_t)opts->workspace & 15) return fail(ATTN_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+        ws = opts->workspace;
+        const void *all[9] = {q, k, v, out, dout, lse, dq, dk, dv};
+        const size_t allsz[9] = {qbytes, kvbytes, kvbytes, qbytes, qbytes, lbytes, qbytes, kvbytes, kvbytes};
+        for (int i = 0; i < 9; ++i)
+            if (overlaps(ws, need, all[i], allsz[i]))
+                return fail(ATTN_ERR_INVALID_ARG, "workspace overlaps a tensor");
+    }
+
+    eea::BwdParams p;
+    std::memset(&p, 0, sizeof p);
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.out = out;
+    p.dout = dout;
+    p.lse = lse;
+    p.dq = dq;
+    p.dk = dk;
+    p.dv = dv;
+    p.head_stride = (long long)N * d;
+    p.BH = (int)BH;
+    p.H = H;
+    p.group = H / H_kv;
+    p.N = N;
+    p.wl = band.wl;
+    p.wr = band.wr;
+    p.causal = causal;
+    p.num_qt = (int)nqt;
+    p.num_kt = (int)nkt;
+    p.scale = scale;
+    p.scale_log2 = scale * 1.4426950408889634f;
+
+    // ---- first HIP call
+    rc = device_and_scratch(need, &ws, true);
+    if (rc != ATTN_OK) return rc;
+    p.delta = static_cast<float *>(ws);
+    hipStream_t stream = opts ? static_cast<hipStream_t>(opts->stream) : nullptr;
+    hipError_t e = eea::launch_backward(p, d, stream);
+    if (e != hipSuccess) return fail(ATTN_ERR_DEVICE, "kernel launch: %s", hipGetErrorString(e));
+    return ATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int attn_bwd(const void *q, const void *k, const void *v, const void *out, const void *dout, const float *lse,
+             void *dq, void *dk, void *dv, int B, int H, int H_kv, int N, int d, int causal, int win_left,
+             int win_right, const int *global_idx, int n_global, const attn_opts *opts) {
+    return bwd_impl(q, k, v, out, dout, lse, dq, dk, dv, B, H, H_kv, N, d, causal, win_left, win_right,
+                    global_idx, n_global, opts);
+}
+
+size_t attn_bwd_workspace_bytes(int B, int H, int N, int d) {
+    if (B <= 0 || H <= 0 || N <= 0 || (d != 64 && d != 128)) return 0;
+    if ((long long)B * H > INT_MAX) return 0;
+    return bwd_workspace((long long)B * H, N);
+}
 
 int attn_fwd_ex(const void *q, const void *k, const void *v, void *out, float *lse, int B, int H, int N, int d,
                 int causal, int win_left, int win_right, const int *global_idx, int n_global,

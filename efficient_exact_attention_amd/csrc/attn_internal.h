@@ -41,6 +41,29 @@ __host__ __device__ __forceinline__ long long kv_head(const FwdParams &p, int bh
     return (long long)b * (p.H / p.group) + h / p.group;
 }
 
+// Backward arguments (bf16 tensors, fp32 LSE and row terms).
+struct BwdParams {
+    const void *q, *k, *v, *out, *dout;
+    const float *lse;       // forward LSE, natural log, [B*H][N]
+    void *dq, *dk, *dv;
+    float *delta;           // workspace: rowsum(dO * O), [B*H][N]
+    long long head_stride;  // N * d elements
+    int BH;                 // B * H
+    int H, group;           // query heads per batch entry; per K/V head
+    int N;
+    int wl, wr;             // normalised band
+    int causal;
+    int num_qt;             // query tiles of the dQ pass
+    int num_kt;             // key tiles of the dK/dV pass
+    int xcd_remap_q, xcd_remap_k;
+    float scale;            // score scale
+    float scale_log2;       // scale * log2(e)
+};
+
+hipError_t launch_backward(const BwdParams &p, int d, hipStream_t stream);
+int bwd_tile_q(int d);      // query rows per dQ workgroup
+int bwd_tile_k(int d);      // keys per dK/dV workgroup
+
 // Tile shapes chosen per (d, dtype).
 int tile_bm(int d, int f32);
 int tile_bn(int d, int f32);

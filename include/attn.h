@@ -123,6 +123,48 @@ int attn_fwd_gqa(const void *q, const void *k, const void *v, void *out, float *
                  const int *global_idx, int n_global, const attn_opts *opts);
 
 /*
+ * attn_bwd - gradients of attn_fwd / attn_fwd_gqa with respect to q, k and v,
+ * by recomputation: the scores are recomputed tile by tile and turned into
+ * the exact softmax weights with the forward's lse, so no N x N matrix is
+ * stored or built ("Efficient Transformers: Sparse Attention, Linear
+ * Attention and FlashAttention", "Family 3": the tiled exact attention
+ * recomputes what the backward pass needs). With P the softmax weights and
+ * scale the score scale:
+ *     dV = P^T dO,  dP = dO V^T,  dS = P * (dP - rowsum(dO * out)),
+ *     dQ = scale dS K,  dK = scale dS^T Q,
+ * and a K/V head shared by a group of query heads receives the sum of their
+ * contributions.
+ *
+ *   q, out, dout  [B][H][N][d] bf16: the forward's inputs, its output and the
+ *                 gradient of the loss with respect to that output.
+ *   k, v          [B][H_kv][N][d] bf16 (H_kv = H for plain multi-head).
+ *   lse           [B][H][N] fp32: the forward's log-sum-exp output.
+ *   dq            [B][H][N][d] bf16 output; dk, dv [B][H_kv][N][d] bf16
+ *                 outputs. Every element is written; none may overlap an
+ *                 input or another output.
+ *   B, H, H_kv, N, d, causal, win_left, win_right: as in attn_fwd_gqa, and
+ *                 they must be the forward call's values.
+ *   global_idx, n_global: global tokens are not supported by the backward
+ *                 pass: n_global > 0 gives ATTN_ERR_UNSUPPORTED unless the
+ *                 window already covers every visible key.
+ *   opts          as in attn_fwd_ex: only ATTN_BF16 (ATTN_F32 gives
+ *                 ATTN_ERR_UNSUPPORTED), scale (must be the forward's),
+ *                 stream, and a workspace of at least attn_bwd_workspace_bytes
+ *                 (else the library's per-device scratch is used).
+ * Errors are reported as for attn_fwd_ex, before any launch.
+ */
+int attn_bwd(const void *q, const void *k, const void *v, const void *out, const void *dout,
+             const float *lse, void *dq, void *dk, void *dv,
+             int B, int H, int H_kv, int N, int d, int causal, int win_left, int win_right,
+             const int *global_idx, int n_global, const attn_opts *opts);
+
+/*
+ * attn_bwd_workspace_bytes - device scratch attn_bwd needs: one fp32 row term
+ * per query row (B*H*N*4 bytes, rounded up to 256). 0 for invalid sizes.
+ */
+size_t attn_bwd_workspace_bytes(int B, int H, int N, int d);
+
+/*
  * attn_workspace_bytes - device scratch a call with these sizes needs for the
  * global-row partial results; 0 when n_global = 0. It grows with
  * B*H*n_global*d and a chunk count bounded by N/64, never with N*N.

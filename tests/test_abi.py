@@ -26,7 +26,8 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert {"attn_fwd", "attn_fwd_ex", "attn_fwd_gqa", "attn_workspace_bytes", "attn_plan_stats",
+    assert {"attn_fwd", "attn_fwd_ex", "attn_fwd_gqa", "attn_bwd", "attn_bwd_workspace_bytes",
+            "attn_workspace_bytes", "attn_plan_stats",
             "attn_last_error", "attn_version", "attn_tile_shape"} <= set(names)
     L = ctypes.CDLL(ea.library_path())
     for n in names:
@@ -118,6 +119,57 @@ def test_gqa_overlap_uses_kv_size():
     assert "overlaps" in err.message
     err = _call_gqa(8, 1, scale=-1.0, k=kv, v=kv + (1 << 30), out=kv + 2 * head, lse=kv + (1 << 31))
     assert "scale" in err.message
+
+
+def _call_bwd(**over):
+    base = FAKE
+    a = dict(q=base, k=base + (1 << 32), v=base + (2 << 32), out=base + (3 << 32), dout=base + (4 << 32),
+             lse=base + (5 << 32), dq=base + (6 << 32), dk=base + (7 << 32), dv=base + (8 << 32),
+             B=1, H=4, H_kv=2, N=100, d=128, causal=1, win_left=-1, win_right=-1, global_idx=None)
+    opts = {}
+    for key in ("dtype", "scale", "workspace", "workspace_bytes"):
+        if key in over:
+            opts[key] = over.pop(key)
+    a.update(over)
+    with pytest.raises(ea.AttnError) as ei:
+        ea.attn_bwd(a["q"], a["k"], a["v"], a["out"], a["dout"], a["lse"], a["dq"], a["dk"], a["dv"],
+                    a["B"], a["H"], a["H_kv"], a["N"], a["d"], a["causal"], a["win_left"], a["win_right"],
+                    a["global_idx"], **opts)
+    return ei.value
+
+
+@pytest.mark.parametrize("over,status,text", [
+    (dict(dout=0), ea.ATTN_ERR_INVALID_ARG, "NULL"),
+    (dict(dv=0), ea.ATTN_ERR_INVALID_ARG, "NULL"),
+    (dict(H_kv=3), ea.ATTN_ERR_INVALID_ARG, "H_kv"),
+    (dict(d=96), ea.ATTN_ERR_UNSUPPORTED, "head size"),
+    (dict(dtype=ea.ATTN_F32), ea.ATTN_ERR_UNSUPPORTED, "bf16"),
+    (dict(global_idx=[0, 50], win_left=4, causal=0, win_right=4), ea.ATTN_ERR_UNSUPPORTED, "global"),
+    (dict(dq=FAKE + (1 << 32) + 64), ea.ATTN_ERR_INVALID_ARG, "overlaps an input"),
+    (dict(dk=FAKE + (6 << 32) + 1024), ea.ATTN_ERR_INVALID_ARG, "overlap"),
+    (dict(dk=FAKE + (7 << 32) + 8), ea.ATTN_ERR_INVALID_ARG, "aligned"),
+    (dict(scale=-2.0), ea.ATTN_ERR_INVALID_ARG, "scale"),
+    (dict(workspace=FAKE + (9 << 32), workspace_bytes=64), ea.ATTN_ERR_INVALID_ARG, "workspace"),
+    (dict(workspace=FAKE + (6 << 32), workspace_bytes=1 << 20), ea.ATTN_ERR_INVALID_ARG, "workspace overlaps"),
+])
+def test_bwd_validation(over, status, text):
+    err = _call_bwd(**over)
+    assert err.status == status, err.message
+    assert text in err.message, err.message
+
+
+def test_bwd_globals_covered_by_window_are_accepted():
+    """Global tokens add nothing when the window already covers every visible
+    key (causal, unbounded left): validation passes them (the call then stops
+    on the invalid scale, before the device)."""
+    err = _call_bwd(global_idx=[0, 7], causal=1, win_left=-1, scale=-1.0)
+    assert "scale" in err.message
+
+
+def test_bwd_workspace_bytes():
+    assert ea.attn_bwd_workspace_bytes(2, 8, 1000, 128) == (2 * 8 * 1000 * 4 + 255) // 256 * 256
+    assert ea.attn_bwd_workspace_bytes(0, 8, 1000, 128) == 0
+    assert ea.attn_bwd_workspace_bytes(1, 1, 16, 96) == 0
 
 
 def test_inputs_may_alias():
