@@ -140,6 +140,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", action="store_true",
                     help="causal d=128 H=8 B=1 sequence-length sweep, one JSON line per N")
+    ap.add_argument("--bwd", action="store_true",
+                    help="time the backward pass (attn_bwd) of the workload instead; useful FLOP = "
+                         "10*d per visible pair (five matrix products)")
     ap.add_argument("--cold", action="store_true",
                     help="write a 1 GiB scratch buffer before every timed call (cold MALL)")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -163,6 +166,8 @@ def main():
 
     if args.sweep:
         return sweep(args)
+    if args.bwd:
+        return bench_bwd(args)
 
     w = W.WORKLOADS[args.config]
     print(f"[bench] generating {w.name}: B={w.B} H={w.H} N={w.N} d={w.d} {w.dtype}", file=sys.stderr,
@@ -270,6 +275,50 @@ def main():
         result["cpu_baseline"] = cb
         result["sample_max_abs_err_vs_oracle"] = err
     print(json.dumps(result), flush=True)
+    return 0
+
+
+def bench_bwd(args):
+    """Backward pass of the workload: one step = one attn_bwd call (row
+    terms, dK/dV pass, dQ pass) with the forward's output and LSE and a
+    seeded upstream gradient resident in HBM. Prints one JSON line."""
+    import torch
+    import efficient_exact_attention_amd as ea
+    from efficient_exact_attention_amd import workloads as W
+    w = W.WORKLOADS[args.config]
+    if w.dtype != "bf16" or w.global_idx:
+        print("the backward pass covers bf16 band masks only", file=sys.stderr)
+        return 2
+    q, k, v, g = (torch.from_numpy(x.view("int16")).view(torch.bfloat16).cuda()
+                  for x in (*W.make_qkv(w), W.make_tensor(w.with_(seed=w.seed + 7), 0)))
+    kw = dict(causal=w.causal, win_left=w.win_left, win_right=w.win_right)
+    out, lse = ea.fwd(q, k, v, **kw)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    stream = torch.cuda.current_stream()
+    pairs = ea.attn_plan_stats(w.N, w.causal, w.win_left, w.win_right, None, 128, 64)[0]
+    flops = 10 * w.d * pairs * w.B * w.H
+
+    def step():
+        ea.bwd(q, k, v, out, g, lse, dq=dq, dk=dk, dv=dv, stream=stream, **kw)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for s_, e_ in ev:
+        s_.record(stream)
+        step()
+        e_.record(stream)
+    torch.cuda.synchronize()
+    ms = sorted(s_.elapsed_time(e_) for s_, e_ in ev)
+    avg = sum(ms) / len(ms)
+    value = flops / (avg * 1e-3) / 1e12
+    print(json.dumps({"metric": "bwd attention TFLOP/s (unmasked FLOPs only: 10*d per visible pair)",
+                      "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+                      "warmup": args.warmup, "ms_per_step": round(avg, 4), "median_launch_ms": round(ms[len(ms) // 2], 4),
+                      "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
+                      "config": {"workload": f"{mask_name(w)} attention backward B={w.B} H={w.H} N={w.N} d={w.d}",
+                                 "useful_flop_per_step": flops},
+                      "pct_bf16_peak": round(100 * value / PEAK_BF16, 2)}), flush=True)
     return 0
 
 
