@@ -49,27 +49,50 @@ import numpy as np
 
 
 def visible(i: int, j: int, N: int, causal: int, win_left: int, win_right: int,
-            global_set) -> bool:
-    """Scalar visibility predicate: may query row i attend to key j?"""
+            global_set, block: int = 0, dilation: int = 1) -> bool:
+    """Scalar visibility predicate: may query row i attend to key j?
+
+    The local part of the mask is one of
+      * the window: j in [i - win_left, i + win_right] (-1: unbounded side);
+      * block-sparse (block > 0): j lies in the block of i or in the block
+        just before it, blocks being runs of `block` positions ("Sparse &
+        sub-quadratic attention", "Escape 1": attend within your block and
+        the previous one); win_left / win_right are not used;
+      * dilated (dilation k > 1): j = i - m*k for whole m ("Week 17 lecture
+        notes", dilated passage: i, i-k, i-2k, ...), with the window counted
+        in dilated steps: -win_right <= m <= win_left.
+    Causal (j <= i) is ANDed with everything; global rows and columns are
+    ORed with the local part."""
     if not (0 <= i < N and 0 <= j < N):
         return False
     if causal and j > i:
         return False
-    in_band = (win_left < 0 or j >= i - win_left) and (win_right < 0 or j <= i + win_right)
-    return bool(in_band or (i in global_set) or (j in global_set))
+    if block > 0:
+        local = (j // block) in (i // block, i // block - 1)
+    elif dilation > 1:
+        diff = i - j
+        local = (diff % dilation == 0 and (win_left < 0 or diff <= win_left * dilation)
+                 and (win_right < 0 or -diff <= win_right * dilation))
+    else:
+        local = (win_left < 0 or j >= i - win_left) and (win_right < 0 or j <= i + win_right)
+    return bool(local or (i in global_set) or (j in global_set))
 
 
 def mask_rows(rows, N: int, causal: int, win_left: int, win_right: int,
-              global_idx=()) -> np.ndarray:
+              global_idx=(), block: int = 0, dilation: int = 1) -> np.ndarray:
     """Boolean visibility matrix [len(rows), N]: the predicate of `visible`
     evaluated for every (row, key) pair."""
     i = np.asarray(rows, dtype=np.int64)[:, None]
     j = np.arange(N, dtype=np.int64)[None, :]
-    band = np.ones((i.shape[0], N), dtype=bool)
-    if win_left >= 0:
-        band &= j >= i - win_left
-    if win_right >= 0:
-        band &= j <= i + win_right
+    if block > 0:
+        band = (j // block == i // block) | (j // block == i // block - 1)
+    else:
+        k = max(int(dilation), 1)
+        band = ((i - j) % k == 0) if k > 1 else np.ones((i.shape[0], N), dtype=bool)
+        if win_left >= 0:
+            band = band & (j >= i - win_left * k)
+        if win_right >= 0:
+            band = band & (j <= i + win_right * k)
     is_global = np.zeros(N, dtype=bool)
     if len(global_idx):
         is_global[np.asarray(global_idx, dtype=np.int64)] = True
@@ -81,7 +104,7 @@ def mask_rows(rows, N: int, causal: int, win_left: int, win_right: int,
 
 def attention(q, k, v, *, causal: int, win_left: int = -1, win_right: int = -1,
               global_idx=(), rows=None, scale: float | None = None,
-              row_block: int = 256):
+              row_block: int = 256, block: int = 0, dilation: int = 1):
     """Masked softmax attention in fp64.
 
     q:       [B, H, N, d]; k, v: [B, H_kv, N, d] with H_kv dividing H (any
@@ -109,7 +132,7 @@ def attention(q, k, v, *, causal: int, win_left: int = -1, win_right: int = -1,
     lse = np.full((B, H, R), -np.inf, dtype=np.float64)
     for r0 in range(0, R, row_block):
         rb = rows[r0:r0 + row_block]
-        vis = mask_rows(rb, N, causal, win_left, win_right, global_idx)
+        vis = mask_rows(rb, N, causal, win_left, win_right, global_idx, block, dilation)
         any_vis = vis.any(axis=1)
         for b in range(B):
             for h in range(H):
@@ -127,7 +150,8 @@ def attention(q, k, v, *, causal: int, win_left: int = -1, win_right: int = -1,
 
 
 def probabilities(q, k, *, causal: int, win_left: int = -1, win_right: int = -1,
-                  global_idx=(), rows=None, scale: float | None = None):
+                  global_idx=(), rows=None, scale: float | None = None, block: int = 0,
+                  dilation: int = 1):
     """Softmax weights [B, H, R, N] (fp64) of the same definition; used to
     check that visible weights sum to one and masked weights are zero."""
     q = np.asarray(q, dtype=np.float64)
@@ -136,7 +160,7 @@ def probabilities(q, k, *, causal: int, win_left: int = -1, win_right: int = -1,
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     rows = np.arange(N) if rows is None else np.asarray(rows, dtype=np.int64)
-    vis = mask_rows(rows, N, causal, win_left, win_right, global_idx)
+    vis = mask_rows(rows, N, causal, win_left, win_right, global_idx, block, dilation)
     s = np.einsum("bhrd,bhnd->bhrn", q[:, :, rows], k) * scale
     s = np.where(vis[None, None], s, -np.inf)
     m = s.max(axis=-1, keepdims=True)
@@ -190,12 +214,13 @@ def online_softmax_rows(q_rows, k, v, vis, block: int, scale: float | None = Non
 # ---- visible-pair counting -------------------------------------------------
 
 def visible_pairs_bruteforce(N: int, causal: int, win_left: int, win_right: int,
-                             global_idx=(), row_block: int = 4096) -> int:
+                             global_idx=(), row_block: int = 4096, block: int = 0,
+                             dilation: int = 1) -> int:
     """Count of visible (i, j) pairs of one head by evaluating the mask."""
     total = 0
     for r0 in range(0, N, row_block):
         rows = np.arange(r0, min(N, r0 + row_block))
-        total += int(mask_rows(rows, N, causal, win_left, win_right, global_idx).sum())
+        total += int(mask_rows(rows, N, causal, win_left, win_right, global_idx, block, dilation).sum())
     return total
 
 
