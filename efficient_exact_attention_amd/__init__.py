@@ -9,7 +9,8 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["AttnError", "attn_fwd", "attn_fwd_ex", "attn_fwd_gqa", "attn_bwd", "attn_bwd_workspace_bytes", "bwd", "attn_workspace_bytes", "attn_plan_stats",
+__all__ = ["AttnError", "attn_fwd", "attn_fwd_ex", "attn_fwd_gqa", "attn_fwd_masked", "attn_bwd", "attn_bwd_masked",
+           "attn_bwd_workspace_bytes", "attn_plan_stats_masked", "bwd", "attn_workspace_bytes", "attn_plan_stats",
            "attn_tile_shape", "attn_last_error", "attn_version", "fwd", "library_path",
            "ATTN_OK", "ATTN_ERR_INVALID_ARG", "ATTN_ERR_UNSUPPORTED", "ATTN_ERR_DEVICE",
            "ATTN_BF16", "ATTN_F32"]
@@ -32,6 +33,20 @@ class AttnError(RuntimeError):
 class _Opts(ctypes.Structure):
     _fields_ = [("dtype", ctypes.c_int), ("scale", ctypes.c_float), ("stream", ctypes.c_void_p),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+
+
+class _Mask(ctypes.Structure):
+    _fields_ = [("causal", ctypes.c_int), ("win_left", ctypes.c_int), ("win_right", ctypes.c_int),
+                ("block", ctypes.c_int), ("dilation", ctypes.c_int),
+                ("global_idx", ctypes.POINTER(ctypes.c_int)), ("n_global", ctypes.c_int)]
+
+
+def _mask(causal, win_left, win_right, block, dilation, global_idx):
+    g, ng = _gidx(global_idx)
+    m = _Mask(int(bool(causal)), int(win_left), int(win_right), int(block), int(dilation),
+              ctypes.cast(g, ctypes.POINTER(ctypes.c_int)) if g is not None else None, ng)
+    m._keep = g   # the index array must outlive the call
+    return m
 
 
 def library_path() -> str:
@@ -59,11 +74,19 @@ def lib():
     L.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, ci,
                            ctypes.POINTER(ci), ci, ctypes.POINTER(_Opts)]
     L.attn_bwd.restype = ci
+    L.attn_fwd_masked.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ctypes.POINTER(_Mask),
+                                  ctypes.POINTER(_Opts)]
+    L.attn_fwd_masked.restype = ci
+    L.attn_bwd_masked.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ctypes.POINTER(_Mask),
+                                  ctypes.POINTER(_Opts)]
+    L.attn_bwd_masked.restype = ci
     L.attn_bwd_workspace_bytes.argtypes = [ci, ci, ci, ci]
     L.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
     L.attn_workspace_bytes.argtypes = [ci, ci, ci, ci, ci]
     L.attn_workspace_bytes.restype = ctypes.c_size_t
     ll = ctypes.POINTER(ctypes.c_longlong)
+    L.attn_plan_stats_masked.argtypes = [ci, ctypes.POINTER(_Mask), ci, ci, ll, ll, ll]
+    L.attn_plan_stats_masked.restype = ci
     L.attn_plan_stats.argtypes = [ci, ci, ci, ci, ctypes.POINTER(ci), ci, ci, ci, ll, ll, ll]
     L.attn_plan_stats.restype = ci
     L.attn_tile_shape.argtypes = [ci, ci, ctypes.POINTER(ci), ctypes.POINTER(ci)]
@@ -129,6 +152,35 @@ def attn_bwd(q, k, v, out, dout, lse, dq, dk, dv, B, H, H_kv, N, d, causal, win_
                           g, ng, ctypes.byref(opts)))
 
 
+def attn_fwd_masked(q, k, v, out, lse, B, H, H_kv, N, d, *, causal=0, win_left=-1, win_right=-1, block=0,
+                    dilation=1, global_idx=None, dtype=ATTN_BF16, scale=0.0, stream=None, workspace=None,
+                    workspace_bytes=0):
+    """Raw forward entry point with an attn_mask descriptor."""
+    m = _mask(causal, win_left, win_right, block, dilation, global_idx)
+    opts = _Opts(dtype, float(scale), stream, workspace, workspace_bytes)
+    _check(lib().attn_fwd_masked(q, k, v, out, lse, B, H, H_kv, N, d, ctypes.byref(m), ctypes.byref(opts)))
+
+
+def attn_bwd_masked(q, k, v, out, dout, lse, dq, dk, dv, B, H, H_kv, N, d, *, causal=0, win_left=-1,
+                    win_right=-1, block=0, dilation=1, global_idx=None, dtype=ATTN_BF16, scale=0.0, stream=None,
+                    workspace=None, workspace_bytes=0):
+    """Raw backward entry point with an attn_mask descriptor."""
+    m = _mask(causal, win_left, win_right, block, dilation, global_idx)
+    opts = _Opts(dtype, float(scale), stream, workspace, workspace_bytes)
+    _check(lib().attn_bwd_masked(q, k, v, out, dout, lse, dq, dk, dv, B, H, H_kv, N, d, ctypes.byref(m),
+                                 ctypes.byref(opts)))
+
+
+def attn_plan_stats_masked(N, bm, bn, *, causal=0, win_left=-1, win_right=-1, block=0, dilation=1,
+                           global_idx=None):
+    """(visible_pairs, tiles_full, tiles_edge) of one head for an attn_mask."""
+    m = _mask(causal, win_left, win_right, block, dilation, global_idx)
+    a, b, c = ctypes.c_longlong(), ctypes.c_longlong(), ctypes.c_longlong()
+    _check(lib().attn_plan_stats_masked(N, ctypes.byref(m), bm, bn, ctypes.byref(a), ctypes.byref(b),
+                                        ctypes.byref(c)))
+    return a.value, b.value, c.value
+
+
 def attn_bwd_workspace_bytes(B, H, N, d) -> int:
     return int(lib().attn_bwd_workspace_bytes(B, H, N, d))
 
@@ -153,7 +205,7 @@ def attn_tile_shape(d, dtype=ATTN_BF16):
 
 
 def fwd(q, k, v, *, causal=False, win_left=-1, win_right=-1, global_idx=None, scale=None,
-        out=None, lse=None, workspace=None, stream=None):
+        out=None, lse=None, workspace=None, stream=None, block=0, dilation=1):
     """Attention forward on torch CUDA tensors: q [B, H, N, d], k and v
     [B, H_kv, N, d] with H_kv dividing H (H_kv = H: multi-head; H_kv < H:
     grouped-query; H_kv = 1: multi-query), bf16 or fp32.
@@ -190,16 +242,17 @@ def fwd(q, k, v, *, causal=False, win_left=-1, win_right=-1, global_idx=None, sc
         stream = stream.cuda_stream
     ws, wsb = (workspace.data_ptr(), workspace.numel() * workspace.element_size()) \
         if workspace is not None else (None, 0)
-    attn_fwd_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                 B, H, H_kv, N, d, int(bool(causal)), int(win_left), int(win_right), global_idx,
-                 dtype=ATTN_F32 if q.dtype == torch.float32 else ATTN_BF16,
-                 scale=0.0 if scale is None else float(scale), stream=stream,
-                 workspace=ws, workspace_bytes=wsb)
+    attn_fwd_masked(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                    B, H, H_kv, N, d, causal=causal, win_left=win_left, win_right=win_right, block=block,
+                    dilation=dilation, global_idx=global_idx,
+                    dtype=ATTN_F32 if q.dtype == torch.float32 else ATTN_BF16,
+                    scale=0.0 if scale is None else float(scale), stream=stream,
+                    workspace=ws, workspace_bytes=wsb)
     return out, lse
 
 
 def bwd(q, k, v, out, dout, lse, *, causal=False, win_left=-1, win_right=-1, global_idx=None, scale=None,
-        dq=None, dk=None, dv=None, workspace=None, stream=None):
+        dq=None, dk=None, dv=None, workspace=None, stream=None, block=0, dilation=1):
     """Gradients (dq, dk, dv) of ``fwd`` on torch CUDA bf16 tensors: q, out,
     dout [B, H, N, d], k, v [B, H_kv, N, d], lse fp32 [B, H, N] from the
     forward call with the same mask and scale. Allocates the gradients with
@@ -226,8 +279,9 @@ def bwd(q, k, v, out, dout, lse, *, causal=False, win_left=-1, win_right=-1, glo
         stream = stream.cuda_stream
     ws, wsb = (workspace.data_ptr(), workspace.numel() * workspace.element_size()) \
         if workspace is not None else (None, 0)
-    attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(), lse.data_ptr(),
-             dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, H_kv, N, d, int(bool(causal)), int(win_left),
-             int(win_right), global_idx, scale=0.0 if scale is None else float(scale), stream=stream,
-             workspace=ws, workspace_bytes=wsb)
+    attn_bwd_masked(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+                    dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, H_kv, N, d, causal=causal,
+                    win_left=win_left, win_right=win_right, block=block, dilation=dilation,
+                    global_idx=global_idx, scale=0.0 if scale is None else float(scale), stream=stream,
+                    workspace=ws, workspace_bytes=wsb)
     return dq, dk, dv

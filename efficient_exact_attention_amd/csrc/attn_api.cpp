@@ -108,50 +108,81 @@ static int check_globals(const int *global_idx, int n_global, int N, std::vector
     return ATTN_OK;
 }
 
-int attn_plan_stats(int N, int causal, int win_left, int win_right, const int *global_idx, int n_global,
-                    int bm, int bn, long long *visible_pairs, long long *tiles_full, long long *tiles_edge) {
-    g_err.clear();
-    if (N <= 0) return fail(ATTN_ERR_INVALID_ARG, "N=%d must be positive", N);
-    if (bm <= 0 || bn <= 0) return fail(ATTN_ERR_INVALID_ARG, "tile shape %dx%d must be positive", bm, bn);
+}  // extern "C"
+
+namespace {
+
+// A validated, normalised mask.
+struct MaskSpec {
+    int causal = 0;
+    int dil = 1;          // dilation (1: off)
+    eea::Band band{};     // window or block rule; with dil > 1 the window counts steps
+    std::vector<int> G;   // sorted global positions
+    int ng = 0;           // globals in use (0 when the band already holds every visible key)
+};
+
+int resolve_mask(int N, int causal, int win_left, int win_right, int block, int dilation, const int *global_idx,
+                 int n_global, MaskSpec &m) {
     if (causal != 0 && causal != 1) return fail(ATTN_ERR_INVALID_ARG, "causal=%d must be 0 or 1", causal);
     if (win_left < -1 || win_right < -1)
         return fail(ATTN_ERR_INVALID_ARG, "window (%d, %d) must be >= -1", win_left, win_right);
-    std::vector<int> G;
-    int rc = check_globals(global_idx, n_global, N, G);
+    if (block < 0) return fail(ATTN_ERR_INVALID_ARG, "block=%d must be >= 0", block);
+    if (dilation < 0) return fail(ATTN_ERR_INVALID_ARG, "dilation=%d must be >= 0", dilation);
+    if (block > 0 && (win_left != -1 || win_right != -1))
+        return fail(ATTN_ERR_INVALID_ARG, "the block rule replaces the window: win_left and win_right must be -1");
+    if (block > 0 && dilation > 1)
+        return fail(ATTN_ERR_UNSUPPORTED, "block-sparse and dilated rules cannot be combined");
+    int rc = check_globals(global_idx, n_global, N, m.G);
     if (rc != ATTN_OK) return rc;
+    m.causal = causal;
+    m.dil = dilation > 1 ? dilation : 1;
+    if (m.dil > 1 && n_global > 0)
+        return fail(ATTN_ERR_UNSUPPORTED, "global tokens cannot be combined with a dilated mask");
+    m.band = block > 0 ? eea::make_block_band(N, causal, block) : eea::make_band(N, causal, win_left, win_right);
+    m.ng = (m.dil == 1 && eea::band_is_everything(m.band, causal)) ? 0 : n_global;
+    return ATTN_OK;
+}
 
-    const eea::Band band = eea::make_band(N, causal, win_left, win_right);
-    const bool use_g = n_global > 0 && !eea::band_is_everything(band, causal);
+int plan_impl(int N, const MaskSpec &m, int bm, int bn, long long *visible_pairs, long long *tiles_full,
+              long long *tiles_edge) {
+    if (bm <= 0 || bn <= 0) return fail(ATTN_ERR_INVALID_ARG, "tile shape %dx%d must be positive", bm, bn);
+    const bool use_g = m.ng > 0;
+    const int causal = m.causal;
     std::vector<char> is_g(N, 0);
     if (use_g)
-        for (int g : G) is_g[g] = 1;
-
+        for (int g : m.G) is_g[g] = 1;
     long long pairs = 0, full = 0, edge = 0;
-    for (int i = 0; i < N; ++i) {
-        const int lo = eea::row_lo(band, i), hi = eea::row_hi(band, i);
-        if (use_g && is_g[i]) {
-            pairs += causal ? (long long)i + 1 : (long long)N;
-            continue;
+    // every residue class (one class unless dilated) is a band of its own
+    for (int r = 0; r < m.dil && r < N; ++r) {
+        eea::Band band = m.band;
+        band.N = (N - r + m.dil - 1) / m.dil;
+        const int Nr = band.N;
+        for (int i = 0; i < Nr; ++i) {
+            const int lo = eea::row_lo(band, i), hi = eea::row_hi(band, i);
+            if (use_g && is_g[i]) {
+                pairs += causal ? (long long)i + 1 : (long long)N;
+                continue;
+            }
+            pairs += hi - lo + 1;
+            if (use_g)
+                for (int g : m.G)
+                    if ((g < lo || g > hi) && (!causal || g <= i)) ++pairs;
         }
-        pairs += hi - lo + 1;
-        if (use_g)
-            for (int g : G)
-                if ((g < lo || g > hi) && (!causal || g <= i)) ++pairs;
-    }
-    const int nqt = (N + bm - 1) / bm;
-    for (int qt = 0; qt < nqt; ++qt) {
-        const int r0 = qt * bm, r1 = std::min(N - 1, r0 + bm - 1);
-        int klo, khi;
-        eea::key_tile_range(band, r0, r1, bn, &klo, &khi);
-        for (int kt = klo; kt <= khi; ++kt) {
-            const int cl = eea::classify(band, r0, r1, kt * bn, kt * bn + bn - 1);
-            if (cl == eea::TILE_FULL) ++full;
-            else if (cl == eea::TILE_EDGE) ++edge;
+        const int nqt = (Nr + bm - 1) / bm;
+        for (int qt = 0; qt < nqt; ++qt) {
+            const int r0 = qt * bm, r1 = std::min(Nr - 1, r0 + bm - 1);
+            int klo, khi;
+            eea::key_tile_range(band, r0, r1, bn, &klo, &khi);
+            for (int kt = klo; kt <= khi; ++kt) {
+                const int cl = eea::classify(band, r0, r1, kt * bn, kt * bn + bn - 1);
+                if (cl == eea::TILE_FULL) ++full;
+                else if (cl == eea::TILE_EDGE) ++edge;
+            }
+            if (use_g) edge += (m.ng + bn - 1) / bn;   // gathered tiles of global columns
         }
-        if (use_g) edge += (n_global + bn - 1) / bn;   // gathered tiles of global columns
     }
     if (use_g)
-        for (int g : G) {
+        for (int g : m.G) {
             const long long keys = causal ? (long long)g + 1 : (long long)N;
             edge += (keys + bn - 1) / bn;
         }
@@ -161,6 +192,32 @@ int attn_plan_stats(int N, int causal, int win_left, int win_right, const int *g
     return ATTN_OK;
 }
 
+}  // namespace
+
+extern "C" {
+
+int attn_plan_stats(int N, int causal, int win_left, int win_right, const int *global_idx, int n_global,
+                    int bm, int bn, long long *visible_pairs, long long *tiles_full, long long *tiles_edge) {
+    g_err.clear();
+    if (N <= 0) return fail(ATTN_ERR_INVALID_ARG, "N=%d must be positive", N);
+    MaskSpec m;
+    int rc = resolve_mask(N, causal, win_left, win_right, 0, 1, global_idx, n_global, m);
+    if (rc != ATTN_OK) return rc;
+    return plan_impl(N, m, bm, bn, visible_pairs, tiles_full, tiles_edge);
+}
+
+int attn_plan_stats_masked(int N, const attn_mask *mask, int bm, int bn, long long *visible_pairs,
+                           long long *tiles_full, long long *tiles_edge) {
+    g_err.clear();
+    if (N <= 0) return fail(ATTN_ERR_INVALID_ARG, "N=%d must be positive", N);
+    if (!mask) return fail(ATTN_ERR_INVALID_ARG, "mask is NULL");
+    MaskSpec m;
+    int rc = resolve_mask(N, mask->causal, mask->win_left, mask->win_right, mask->block, mask->dilation,
+                          mask->global_idx, mask->n_global, m);
+    if (rc != ATTN_OK) return rc;
+    return plan_impl(N, m, bm, bn, visible_pairs, tiles_full, tiles_edge);
+}
+
 }  // extern "C"
 
 namespace {
@@ -168,8 +225,8 @@ namespace {
 // The forward call with H_kv K/V heads per batch entry (H_kv == H: plain
 // multi-head attention).
 int fwd_impl(const void *q, const void *k, const void *v, void *out, float *lse, int B, int H, int H_kv, int N,
-             int d, int causal, int win_left, int win_right, const int *global_idx, int n_global,
-             const attn_opts *opts) {
+             int d, int causal, int win_left, int win_right, int block, int dilation, const int *global_idx,
+             int n_global, const attn_opts *opts) {
     g_err.clear();
     const int dtype = opts ? opts->dtype : ATTN_BF16;
     if (!q || !k || !v || !out || !lse) return fail(ATTN_ERR_INVALID_ARG, "a tensor pointer is NULL");
@@ -178,18 +235,19 @@ int fwd_impl(const void *q, const void *k, const void *v, void *out, float *lse,
     if (H_kv <= 0 || H % H_kv != 0)
         return fail(ATTN_ERR_INVALID_ARG, "H_kv=%d must be positive and divide H=%d", H_kv, H);
     if (dtype != ATTN_BF16 && dtype != ATTN_F32) return fail(ATTN_ERR_INVALID_ARG, "unknown dtype %d", dtype);
-    if (causal != 0 && causal != 1) return fail(ATTN_ERR_INVALID_ARG, "causal=%d must be 0 or 1", causal);
-    if (win_left < -1 || win_right < -1)
-        return fail(ATTN_ERR_INVALID_ARG, "window (%d, %d) must be >= -1", win_left, win_right);
-    if (d != 64 && d != 128) return fail(ATTN_ERR_UNSUPPORTED, "head size d=%d is not supported (64 or 128)", d);
-    std::vector<int> G;
-    int rc = check_globals(global_idx, n_global, N, G);
+    MaskSpec m;
+    int rc = resolve_mask(N, causal, win_left, win_right, block, dilation, global_idx, n_global, m);
     if (rc != ATTN_OK) return rc;
+    if (d != 64 && d != 128) return fail(ATTN_ERR_UNSUPPORTED, "head size d=%d is not supported (64 or 128)", d);
+    if (m.dil > 1 && dtype == ATTN_F32)
+        return fail(ATTN_ERR_UNSUPPORTED, "dilated masks are supported for bf16 tensors only");
+    const std::vector<int> &G = m.G;
 
     const long long BH = (long long)B * H;
     const int bm = eea::tile_bm(d, dtype == ATTN_F32);
-    const long long nqt = (N + (long long)bm - 1) / bm;
-    if (BH > INT_MAX || BH * nqt > INT_MAX)
+    // query tiles per residue class (the longest class: ceil(N / dil) rows)
+    const long long nqt = ((N + (long long)m.dil - 1) / m.dil + bm - 1) / bm;
+    if (BH > INT_MAX || BH * m.dil * nqt > INT_MAX)
         return fail(ATTN_ERR_INVALID_ARG, "B*H=%lld with N=%d exceeds the launch grid", BH, N);
     const size_t esize = dtype == ATTN_F32 ? 4 : 2;
     if ((long long)N * d * (long long)esize > INT_MAX)
@@ -211,8 +269,8 @@ int fwd_impl(const void *q, const void *k, const void *v, void *out, float *lse,
     if (!(scale > 0.f) || !std::isfinite(scale))
         return fail(ATTN_ERR_INVALID_ARG, "scale must be positive and finite");
 
-    const eea::Band band = eea::make_band(N, causal, win_left, win_right);
-    const int ng = eea::band_is_everything(band, causal) ? 0 : n_global;
+    const eea::Band band = m.band;
+    const int ng = m.ng;
 
     eea::FwdParams p;
     std::memset(&p, 0, sizeof p);
@@ -228,6 +286,9 @@ int fwd_impl(const void *q, const void *k, const void *v, void *out, float *lse,
     p.N = N;
     p.wl = band.wl;
     p.wr = band.wr;
+    p.block = band.block;
+    p.cap = band.cap;
+    p.dil = m.dil;
     p.causal = causal;
     p.n_global = ng;
     p.num_qt = (int)nqt;
@@ -334,7 +395,7 @@ size_t bwd_workspace(long long BH, int N) {
 
 int bwd_impl(const void *q, const void *k, const void *v, const void *out, const void *dout, const float *lse,
              void *dq, void *dk, void *dv, int B, int H, int H_kv, int N, int d, int causal, int win_left,
-             int win_right, const int *global_idx, int n_global, const attn_opts *opts) {
+             int win_right, int block, int dilation, const int *global_idx, int n_global, const attn_opts *opts) {
     g_err.clear();
     const int dtype = opts ? opts->dtype : ATTN_BF16;
     if (!q || !k || !v || !out || !dout || !lse || !dq || !dk || !dv)
@@ -345,16 +406,13 @@ int bwd_impl(const void *q, const void *k, const void *v, const void *out, const
         return fail(ATTN_ERR_INVALID_ARG, "H_kv=%d must be positive and divide H=%d", H_kv, H);
     if (dtype != ATTN_BF16 && dtype != ATTN_F32) return fail(ATTN_ERR_INVALID_ARG, "unknown dtype %d", dtype);
     if (dtype == ATTN_F32) return fail(ATTN_ERR_UNSUPPORTED, "the backward pass supports bf16 tensors only");
-    if (causal != 0 && causal != 1) return fail(ATTN_ERR_INVALID_ARG, "causal=%d must be 0 or 1", causal);
-    if (win_left < -1 || win_right < -1)
-        return fail(ATTN_ERR_INVALID_ARG, "window (%d, %d) must be >= -1", win_left, win_right);
-    if (d != 64 && d != 128) return fail(ATTN_ERR_UNSUPPORTED, "head size d=%d is not supported (64 or 128)", d);
-    std::vector<int> G;
-    int rc = check_globals(global_idx, n_global, N, G);
+    MaskSpec m;
+    int rc = resolve_mask(N, causal, win_left, win_right, block, dilation, global_idx, n_global, m);
     if (rc != ATTN_OK) return rc;
-    const eea::Band band = eea::make_band(N, causal, win_left, win_right);
-    if (n_global > 0 && !eea::band_is_everything(band, causal))
-        return fail(ATTN_ERR_UNSUPPORTED, "the backward pass does not support global tokens");
+    if (d != 64 && d != 128) return fail(ATTN_ERR_UNSUPPORTED, "head size d=%d is not supported (64 or 128)", d);
+    if (m.ng > 0) return fail(ATTN_ERR_UNSUPPORTED, "the backward pass does not support global tokens");
+    if (m.dil > 1) return fail(ATTN_ERR_UNSUPPORTED, "the backward pass does not support dilated masks");
+    const eea::Band band = m.band;
 
     const long long BH = (long long)B * H;
     const int bq = eea::bwd_tile_q(d), bk = eea::bwd_tile_k(d);
@@ -419,6 +477,8 @@ int bwd_impl(const void *q, const void *k, const void *v, const void *out, const
     p.N = N;
     p.wl = band.wl;
     p.wr = band.wr;
+    p.block = band.block;
+    p.cap = band.cap;
     p.causal = causal;
     p.num_qt = (int)nqt;
     p.num_kt = (int)nkt;
@@ -442,8 +502,19 @@ extern "C" {
 int attn_bwd(const void *q, const void *k, const void *v, const void *out, const void *dout, const float *lse,
              void *dq, void *dk, void *dv, int B, int H, int H_kv, int N, int d, int causal, int win_left,
              int win_right, const int *global_idx, int n_global, const attn_opts *opts) {
-    return bwd_impl(q, k, v, out, dout, lse, dq, dk, dv, B, H, H_kv, N, d, causal, win_left, win_right,
+    return bwd_impl(q, k, v, out, dout, lse, dq, dk, dv, B, H, H_kv, N, d, causal, win_left, win_right, 0, 1,
                     global_idx, n_global, opts);
+}
+
+int attn_bwd_masked(const void *q, const void *k, const void *v, const void *out, const void *dout,
+                    const float *lse, void *dq, void *dk, void *dv, int B, int H, int H_kv, int N, int d,
+                    const attn_mask *mask, const attn_opts *opts) {
+    if (!mask) {
+        g_err.clear();
+        return fail(ATTN_ERR_INVALID_ARG, "mask is NULL");
+    }
+    return bwd_impl(q, k, v, out, dout, lse, dq, dk, dv, B, H, H_kv, N, d, mask->causal, mask->win_left,
+                    mask->win_right, mask->block, mask->dilation, mask->global_idx, mask->n_global, opts);
 }
 
 size_t attn_bwd_workspace_bytes(int B, int H, int N, int d) {
@@ -455,19 +526,31 @@ size_t attn_bwd_workspace_bytes(int B, int H, int N, int d) {
 int attn_fwd_ex(const void *q, const void *k, const void *v, void *out, float *lse, int B, int H, int N, int d,
                 int causal, int win_left, int win_right, const int *global_idx, int n_global,
                 const attn_opts *opts) {
-    return fwd_impl(q, k, v, out, lse, B, H, H, N, d, causal, win_left, win_right, global_idx, n_global, opts);
+    return fwd_impl(q, k, v, out, lse, B, H, H, N, d, causal, win_left, win_right, 0, 1, global_idx, n_global,
+                    opts);
 }
 
 int attn_fwd_gqa(const void *q, const void *k, const void *v, void *out, float *lse, int B, int H, int H_kv,
                  int N, int d, int causal, int win_left, int win_right, const int *global_idx, int n_global,
                  const attn_opts *opts) {
-    return fwd_impl(q, k, v, out, lse, B, H, H_kv, N, d, causal, win_left, win_right, global_idx, n_global,
-                    opts);
+    return fwd_impl(q, k, v, out, lse, B, H, H_kv, N, d, causal, win_left, win_right, 0, 1, global_idx,
+                    n_global, opts);
+}
+
+int attn_fwd_masked(const void *q, const void *k, const void *v, void *out, float *lse, int B, int H, int H_kv,
+                    int N, int d, const attn_mask *mask, const attn_opts *opts) {
+    if (!mask) {
+        g_err.clear();
+        return fail(ATTN_ERR_INVALID_ARG, "mask is NULL");
+    }
+    return fwd_impl(q, k, v, out, lse, B, H, H_kv, N, d, mask->causal, mask->win_left, mask->win_right,
+                    mask->block, mask->dilation, mask->global_idx, mask->n_global, opts);
 }
 
 int attn_fwd(const void *q, const void *k, const void *v, void *out, float *lse, int B, int H, int N, int d,
              int causal, int win_left, int win_right, const int *global_idx, int n_global) {
-    return fwd_impl(q, k, v, out, lse, B, H, H, N, d, causal, win_left, win_right, global_idx, n_global, nullptr);
+    return fwd_impl(q, k, v, out, lse, B, H, H, N, d, causal, win_left, win_right, 0, 1, global_idx, n_global,
+                    nullptr);
 }
 
 }  // extern "C"

@@ -93,7 +93,7 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_dkdv(const BwdParams prm) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int ln = lane & 31, h = lane >> 5;
     const int N = prm.N;
-    const Band band{N, prm.wl, prm.wr};
+    const Band band{N, prm.wl, prm.wr, prm.block, prm.cap};
     const int H_kv = prm.H / prm.group;
 
     const int G = gridDim.x, bid = blockIdx.x;
@@ -112,12 +112,10 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_dkdv(const BwdParams prm) {
     const bool kvalid = key < N;
     const int k0w = K0 + wave * 32, k1w = imin(N - 1, k0w + 31);
     const bool wave_active = k0w < N;
-    // rows that see this lane's key: key in [i - wl, i + wr]  <=>  i in [key - wr, key + wl]
-    const int qlo = band.wr < 0 ? 0 : key - band.wr;
-    const int qhi = band.wl < 0 ? N - 1 : imin(N - 1, key + band.wl);
-    // query tiles of the workgroup's keys
-    const int glo = band.wr < 0 ? 0 : imax(0, K0 - band.wr);
-    const int ghi = band.wl < 0 ? N - 1 : imin(N - 1, imin(N - 1, K0 + BK - 1) + band.wl);
+    // rows whose local interval holds this lane's key, and the query tiles
+    // of the workgroup's keys (both bounds never decrease with the key)
+    const int qlo = col_lo(band, key), qhi = col_hi(band, key);
+    const int glo = col_lo(band, K0), ghi = col_hi(band, imin(N - 1, K0 + BK - 1));
     const int qt_lo = glo / BQ, nqt = ghi / BQ - qt_lo + 1;
     const int T = prm.group * nqt;   // (query head, query tile) pairs
 
@@ -249,7 +247,7 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_dq(const BwdParams prm) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int ln = lane & 31, h = lane >> 5;
     const int N = prm.N;
-    const Band band{N, prm.wl, prm.wr};
+    const Band band{N, prm.wl, prm.wr, prm.block, prm.cap};
 
     const int G = gridDim.x, bid = blockIdx.x;
     const int Lw = prm.xcd_remap_q ? (bid & 7) * (G >> 3) + (bid >> 3) : bid;

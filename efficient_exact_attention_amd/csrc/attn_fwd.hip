@@ -247,7 +247,7 @@ __global__ void __launch_bounds__(P::NT) fwd_kernel(const FwdParams prm) {
     const int ln = lane & 31, h = lane >> 5;
     const int N = prm.N;
     const int ng = prm.n_global;
-    const Band band{N, prm.wl, prm.wr};
+    const Band band{N, prm.wl, prm.wr, prm.block, prm.cap};
 
     if (tid < kMaxGlobal) s_gidx[tid] = tid < ng ? prm.gidx[tid] : -1;
 
@@ -639,26 +639,37 @@ __global__ void __launch_bounds__(512) fwd_band_bf16(const FwdParams prm) {
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int ln = lane & 31, h = lane >> 5;
-    const int N = prm.N;
     const int ng = prm.n_global;
-    const Band band{N, prm.wl, prm.wr};
 
-    if (tid < kMaxGlobal) s_gidx[tid] = tid < ng ? prm.gidx[tid] : -1;
-
-    // --- work item: heaviest query tiles first under a causal mask, runs of
-    // consecutive items on one XCD
+    // --- work item: (head, residue class, query tile); heaviest query tiles
+    // first under a causal mask, runs of consecutive items on one XCD. With a
+    // dilated mask (dilation k) the rows r, r+k, r+2k, ... of residue class r
+    // see only each other, so each class is a band attention over a strided
+    // sequence of its own (the window counted in its steps); k = 1 is the
+    // plain sequence.
     const int G = gridDim.x;
     const int bid = blockIdx.x;
     const int Lw = prm.xcd_remap ? (bid & 7) * (G >> 3) + (bid >> 3) : bid;
-    const int bh = Lw / prm.num_qt;
-    const int qi = Lw - bh * prm.num_qt;
+    const int dil = prm.dil;
+    const int per_head = dil * prm.num_qt;
+    const int bh = Lw / per_head;
+    const int rcls = (Lw - bh * per_head) / prm.num_qt;
+    const int qi = Lw - bh * per_head - rcls * prm.num_qt;
     const int unit = prm.causal ? prm.num_qt - 1 - qi : qi;
-    const uint16_t *qh = static_cast<const uint16_t *>(prm.q) + (long long)bh * prm.head_stride;
-    const uint16_t *kh = static_cast<const uint16_t *>(prm.k) + kv_head(prm, bh) * prm.head_stride;
-    const uint16_t *vh = static_cast<const uint16_t *>(prm.v) + kv_head(prm, bh) * prm.head_stride;
+    const int N = (prm.N - rcls + dil - 1) / dil;   // rows of this residue class
+    if (unit * BM >= N) return;                      // whole workgroup: a shorter class
+    const Band band{N, prm.wl, prm.wr, prm.block, prm.cap};
+
+    if (tid < kMaxGlobal) s_gidx[tid] = tid < ng ? prm.gidx[tid] : -1;
+
+    const uint16_t *qh = static_cast<const uint16_t *>(prm.q) + (long long)bh * prm.head_stride + (long long)rcls * D;
+    const uint16_t *kh =
+        static_cast<const uint16_t *>(prm.k) + kv_head(prm, bh) * prm.head_stride + (long long)rcls * D;
+    const uint16_t *vh =
+        static_cast<const uint16_t *>(prm.v) + kv_head(prm, bh) * prm.head_stride + (long long)rcls * D;
 
     typename P::Lane L;
-    P::init_lane(L, lane, wave);
+    P::init_lane(L, lane, wave, dil);
 
     __syncthreads();   // s_gidx visible
 
@@ -676,7 +687,7 @@ __global__ void __launch_bounds__(512) fwd_band_bf16(const FwdParams prm) {
     if (wave_active) key_tile_range(band, wr0, wr1, BN, &w_lo, &w_hi);
 
     typename P::QFrag qf;
-    P::load_q(qf, qh, row, valid, h);
+    P::load_q(qf, qh, row * dil, valid, h);
 
     RowState<P> rs;
     rs.m = EEA_NEG_INF;
@@ -686,6 +697,7 @@ __global__ void __launch_bounds__(512) fwd_band_bf16(const FwdParams prm) {
     const float c = prm.scale_log2;
 
     // --- gathered tiles of global columns (one per BN globals), unpipelined
+    // (global tokens are not combined with a dilated mask)
     if (ng > 0) {
         for (int g0 = 0; g0 < ng; g0 += BN) {
             typename P::Stage st;
@@ -716,9 +728,9 @@ __global__ void __launch_bounds__(512) fwd_band_bf16(const FwdParams prm) {
     auto in_w = [&](int kt) { return kt >= w_lo && kt <= w_hi; };
     auto is_edge = [&](int kt) { return classify(band, wr0, wr1, kt * BN, kt * BN + BN - 1) != TILE_FULL; };
 
-    P::issue_k(L, kh, N, kb0, kt_lo * BN);
-    P::issue_v(L, vh, N, vb0, kt_lo * BN);
-    if (kt_lo + 1 <= kt_hi) P::issue_k(L, kh, N, kb1, (kt_lo + 1) * BN);
+    P::issue_k(L, kh, N, kb0, kt_lo * BN, dil);
+    P::issue_v(L, vh, N, vb0, kt_lo * BN, dil);
+    if (kt_lo + 1 <= kt_hi) P::issue_k(L, kh, N, kb1, (kt_lo + 1) * BN, dil);
     wait_vmem();
     __syncthreads();
 
@@ -736,8 +748,8 @@ __global__ void __launch_bounds__(512) fwd_band_bf16(const FwdParams prm) {
     // One iteration; s holds S(j), sn receives S(j+1).
     auto iter = [&](int j, f32x16 (&s)[MB], f32x16 (&sn)[MB], const char *kr, const char *vr, char *kw, char *vw)
         __attribute__((always_inline)) {
-        if (j + 2 <= kt_hi) P::issue_k(L, kh, N, kw, (j + 2) * BN);
-        if (j + 1 <= kt_hi) P::issue_v(L, vh, N, vw, (j + 1) * BN);
+        if (j + 2 <= kt_hi) P::issue_k(L, kh, N, kw, (j + 2) * BN, dil);
+        if (j + 1 <= kt_hi) P::issue_v(L, vh, N, vw, (j + 1) * BN, dil);
         const bool cur = in_w(j), nxt = in_w(j + 1);
         const EdgeMask em{(j + 1) * BN, lo, hi, h};
         const float nmu = rs.m == EEA_NEG_INF ? 0.f : -rs.m;
@@ -772,15 +784,16 @@ __global__ void __launch_bounds__(512) fwd_band_bf16(const FwdParams prm) {
 
     // --- epilogue
     if (!valid) return;
+    const int orow = rcls + row * dil;   // row index in the stored sequence
     if (ng > 0) {
         for (int t = 0; t < ng; ++t)
-            if (s_gidx[t] == row) return;   // global rows are written by the merge
+            if (s_gidx[t] == orow) return;   // global rows are written by the merge
     }
     const float l = sum_across_halves(rs.lpart);
     const float inv = l > 0.f ? 1.f / l : 0.f;
     uint16_t *oh = static_cast<uint16_t *>(prm.out) + (long long)bh * prm.head_stride;
-    P::store_out(oh, row, rs.o, inv, h);
-    if (h == 0) prm.lse[(long long)bh * N + row] = l > 0.f ? (rs.m + __log2f(l)) * kLn2 : EEA_NEG_INF;
+    P::store_out(oh, orow, rs.o, inv, h);
+    if (h == 0) prm.lse[(long long)bh * prm.N + orow] = l > 0.f ? (rs.m + __log2f(l)) * kLn2 : EEA_NEG_INF;
 }
 
 // Merge of the split-key partials of one global row: the same rescaling
@@ -844,7 +857,7 @@ int global_chunks(int BH, int N, int d, int f32, int *chunk_tiles) {
 template <class PB, class PG64, class PG128, int D, bool F32>
 static hipError_t launch_impl(const FwdParams &p0, hipStream_t stream) {
     FwdParams p = p0;
-    const int grid = p.BH * p.num_qt;
+    const int grid = p.BH * p.dil * p.num_qt;
     p.xcd_remap = (grid % 8 == 0) ? 1 : 0;
     if constexpr (F32)
         hipLaunchKernelGGL((fwd_kernel<PB, MODE_BAND>), dim3(grid), dim3(PB::NT), 0, stream, p);

@@ -24,9 +24,11 @@ struct FwdParams {
     int group;            // query heads per K/V head (H / H_kv; 1 for plain multi-head)
     int N;
     int wl, wr;           // normalised band (see attn_plan.h)
+    int block, cap;       // block-sparse rule (0: window rule)
+    int dil;              // dilation: rows r, r+dil, ... form one sequence (1: plain)
     int causal;
     int n_global;         // 0 when the band already covers every visible key
-    int num_qt;           // query tiles per head
+    int num_qt;           // query tiles per head (per residue class when dil > 1)
     int chunks;           // key chunks per global row (split-key pass)
     int chunk_tiles;      // key tiles per chunk
     int xcd_remap;        // 1: group consecutive work items on one XCD
@@ -52,6 +54,7 @@ struct BwdParams {
     int H, group;           // query heads per batch entry; per K/V head
     int N;
     int wl, wr;             // normalised band
+    int block, cap;         // block-sparse rule (0: window rule)
     int causal;
     int num_qt;             // query tiles of the dQ pass
     int num_kt;             // key tiles of the dK/dV pass

@@ -24,8 +24,10 @@ namespace eea {
 
 struct Band {
     int N;
-    int wl;   // keys left of the diagonal, -1 = unbounded
-    int wr;   // keys right of the diagonal, -1 = unbounded (0 under causal)
+    int wl;      // keys left of the diagonal, -1 = unbounded
+    int wr;      // keys right of the diagonal, -1 = unbounded (0 under causal)
+    int block;   // > 0: block-sparse rule instead of the window (own block and the previous one)
+    int cap;     // block rule under causal: keys beyond the row are cut
 };
 
 EEA_HD int imin(int a, int b) { return a < b ? a : b; }
@@ -39,16 +41,52 @@ EEA_HD Band make_band(int N, int causal, int win_left, int win_right) {
     b.wl = (win_left < 0 || win_left >= N - 1) ? -1 : win_left;
     int wr = causal ? 0 : win_right;
     b.wr = (wr < 0 || wr >= N - 1) ? -1 : wr;
+    b.block = 0;
+    b.cap = 0;
     return b;
 }
 
-EEA_HD int row_lo(const Band &b, int i) { return b.wl < 0 ? 0 : imax(0, i - b.wl); }
-EEA_HD int row_hi(const Band &b, int i) { return b.wr < 0 ? b.N - 1 : imin(b.N - 1, i + b.wr); }
+// Block-sparse rule ("Sparse & sub-quadratic attention", "Escape 1": attend
+// within your block and the previous one): row i sees keys
+// [(i/block - 1) * block, (i/block + 1) * block - 1], cut at i under causal.
+// A block covering the sequence is the unbounded window.
+EEA_HD Band make_block_band(int N, int causal, int block) {
+    if (block >= N) return make_band(N, causal, -1, -1);
+    Band b;
+    b.N = N;
+    b.wl = -1;
+    b.wr = -1;
+    b.block = block;
+    b.cap = causal;
+    return b;
+}
+
+// First and last key of row i's local interval: both never decrease with i,
+// which is what the tile classification below relies on.
+EEA_HD int row_lo(const Band &b, int i) {
+    if (b.block > 0) return imax(0, (i / b.block - 1) * b.block);
+    return b.wl < 0 ? 0 : imax(0, i - b.wl);
+}
+EEA_HD int row_hi(const Band &b, int i) {
+    if (b.block > 0) return b.cap ? imin(b.N - 1, i) : imin(b.N - 1, (i / b.block + 1) * b.block - 1);
+    return b.wr < 0 ? b.N - 1 : imin(b.N - 1, i + b.wr);
+}
+
+// First and last row whose local interval holds key j (the same relation
+// read column-wise; also never decreasing in j).
+EEA_HD int col_lo(const Band &b, int j) {
+    if (b.block > 0) return b.cap ? j : (j / b.block) * b.block;
+    return b.wr < 0 ? 0 : imax(0, j - b.wr);
+}
+EEA_HD int col_hi(const Band &b, int j) {
+    if (b.block > 0) return imin(b.N - 1, (j / b.block + 2) * b.block - 1);
+    return b.wl < 0 ? b.N - 1 : imin(b.N - 1, j + b.wl);
+}
 
 // True when the band already holds every key a row may see under the causal
 // rule, so global tokens add nothing.
 EEA_HD bool band_is_everything(const Band &b, int causal) {
-    return b.wl < 0 && (causal || b.wr < 0);
+    return b.block == 0 && b.wl < 0 && (causal || b.wr < 0);
 }
 
 enum TileKind { TILE_SKIP = 0, TILE_EDGE = 1, TILE_FULL = 2 };

@@ -102,7 +102,9 @@ struct Bf16Path {
         int ldv[SPW];      // byte offset of load i's V chunk from the tile's first row
     };
 
-    static __device__ __forceinline__ void init_lane(Lane &L, int lane, int wave) {
+    // dil: distance in rows of the stored tensor between consecutive tile
+    // rows (1 for contiguous rows; k for one residue class of a dilated mask).
+    static __device__ __forceinline__ void init_lane(Lane &L, int lane, int wave, int dil = 1) {
         const int ln = lane & 31, h = lane >> 5;
         // K row ln, logical chunk 2ks + h
 #pragma unroll
@@ -123,8 +125,8 @@ struct Bf16Path {
             L.ldkcol[i] = (phys ^ kx(row)) * 8;
             L.ldvcol[i] = (phys ^ vx(row)) * 8;
             L.ldlds[i] = (wave * SPW + i) * 1024;
-            L.ldk[i] = row * ROWB + 2 * L.ldkcol[i];
-            L.ldv[i] = row * ROWB + 2 * L.ldvcol[i];
+            L.ldk[i] = row * dil * ROWB + 2 * L.ldkcol[i];
+            L.ldv[i] = row * dil * ROWB + 2 * L.ldvcol[i];
         }
     }
 
@@ -167,17 +169,22 @@ struct Bf16Path {
     // Band tiles: the copy of the K (or V) tile whose first key is k0. Rows
     // past the end of the sequence lie past the buffer's last record, so the
     // copy fills them with zeros (finite values that the edge mask drops).
-    static __device__ __forceinline__ void issue_k(const Lane &L, const elem_t *kh, int N, char *kbuf, int k0) {
-        const __amdgpu_buffer_rsrc_t kr = head_rsrc(kh, N);
-        const unsigned base = (unsigned)k0 * ROWB;
+    // With dil > 1 (init_lane given the same dil), tile row r is stored row
+    // (k0 + r) * dil of the tensor at kh, and N counts the rows of that
+    // strided sequence; rows past it still read as zeros.
+    static __device__ __forceinline__ void issue_k(const Lane &L, const elem_t *kh, int N, char *kbuf, int k0,
+                                                   int dil = 1) {
+        const __amdgpu_buffer_rsrc_t kr = head_rsrc(kh, (N - 1) * dil + 1);
+        const unsigned base = (unsigned)k0 * dil * ROWB;
 #pragma unroll
         for (int i = 0; i < SPW; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (EEA_LDS void *)(kbuf + L.ldlds[i]), 16, base + L.ldk[i], 0,
                                                      0, 0);
     }
-    static __device__ __forceinline__ void issue_v(const Lane &L, const elem_t *vh, int N, char *vbuf, int k0) {
-        const __amdgpu_buffer_rsrc_t vr = head_rsrc(vh, N);
-        const unsigned base = (unsigned)k0 * ROWB;
+    static __device__ __forceinline__ void issue_v(const Lane &L, const elem_t *vh, int N, char *vbuf, int k0,
+                                                   int dil = 1) {
+        const __amdgpu_buffer_rsrc_t vr = head_rsrc(vh, (N - 1) * dil + 1);
+        const unsigned base = (unsigned)k0 * dil * ROWB;
 #pragma unroll
         for (int i = 0; i < SPW; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (EEA_LDS void *)(vbuf + L.ldlds[i]), 16, base + L.ldv[i], 0,

@@ -103,6 +103,41 @@ int attn_fwd_ex(const void *q, const void *k, const void *v, void *out, float *l
                 const int *global_idx, int n_global, const attn_opts *opts);
 
 /*
+ * attn_mask - which (query row i, key j) pairs are visible, as one
+ * descriptor. The local rule is one of
+ *   window (block = 0, dilation <= 1): i - win_left <= j <= i + win_right,
+ *       -1 for an unbounded side (the masks of attn_fwd);
+ *   block-sparse (block > 0): j lies in the block of i or in the block just
+ *       before it, blocks being runs of `block` positions ("Sparse &
+ *       sub-quadratic attention", "Escape 1": attend within your block and
+ *       the previous one). win_left and win_right must be -1;
+ *   dilated (dilation = k > 1): j = i - m*k for whole m (week-17 lecture
+ *       notes, dilated passage: i, i-k, i-2k, ...), with the window counted
+ *       in those steps: -win_right <= m <= win_left. bf16 forward only, and
+ *       not combined with global tokens.
+ * causal (j <= i) is ANDed with the result, global tokens (rows that see
+ * everything and columns seen by everyone) ORed with the local rule.
+ */
+typedef struct attn_mask {
+    int causal;             /* 0 or 1 */
+    int win_left;           /* >= -1 */
+    int win_right;          /* >= -1 */
+    int block;              /* >= 0; 0 = no block rule */
+    int dilation;           /* >= 0; 0 or 1 = no dilation */
+    const int *global_idx;  /* host array of distinct positions in [0, N), or NULL */
+    int n_global;           /* 0..64 */
+} attn_mask;
+
+/*
+ * attn_fwd_masked - attn_fwd_gqa with the mask given as an attn_mask (which
+ * adds the block-sparse and dilated rules). Arguments, outputs, workspace
+ * and errors otherwise as attn_fwd_gqa; a NULL mask is ATTN_ERR_INVALID_ARG,
+ * invalid combinations as described at attn_mask.
+ */
+int attn_fwd_masked(const void *q, const void *k, const void *v, void *out, float *lse,
+                    int B, int H, int H_kv, int N, int d, const attn_mask *mask, const attn_opts *opts);
+
+/*
  * attn_fwd_gqa - as attn_fwd_ex with fewer K/V heads than query heads:
  * grouped-query attention (H_kv groups of H/H_kv query heads, each group
  * sharing one K head and one V head) and, with H_kv = 1, multi-query
@@ -159,6 +194,15 @@ int attn_bwd(const void *q, const void *k, const void *v, const void *out, const
              const int *global_idx, int n_global, const attn_opts *opts);
 
 /*
+ * attn_bwd_masked - attn_bwd with the mask given as an attn_mask: window and
+ * block-sparse rules (dilated masks and global tokens give
+ * ATTN_ERR_UNSUPPORTED).
+ */
+int attn_bwd_masked(const void *q, const void *k, const void *v, const void *out, const void *dout,
+                    const float *lse, void *dq, void *dk, void *dv,
+                    int B, int H, int H_kv, int N, int d, const attn_mask *mask, const attn_opts *opts);
+
+/*
  * attn_bwd_workspace_bytes - device scratch attn_bwd needs: one fp32 row term
  * per query row (B*H*N*4 bytes, rounded up to 256). 0 for invalid sizes.
  */
@@ -187,6 +231,15 @@ int attn_plan_stats(int N, int causal, int win_left, int win_right,
                     const int *global_idx, int n_global, int bm, int bn,
                     long long *visible_pairs, long long *tiles_full,
                     long long *tiles_edge);
+
+/*
+ * attn_plan_stats_masked - attn_plan_stats for an attn_mask. With a dilated
+ * mask the counts are summed over the residue classes, each planned as its
+ * own band over its strided rows (the way the forward kernel visits them).
+ */
+int attn_plan_stats_masked(int N, const attn_mask *mask, int bm, int bn,
+                           long long *visible_pairs, long long *tiles_full,
+                           long long *tiles_edge);
 
 /*
  * attn_tile_shape - the tile shape (query rows, keys) the forward kernel uses

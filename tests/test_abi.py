@@ -26,7 +26,8 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert {"attn_fwd", "attn_fwd_ex", "attn_fwd_gqa", "attn_bwd", "attn_bwd_workspace_bytes",
+    assert {"attn_fwd", "attn_fwd_ex", "attn_fwd_gqa", "attn_fwd_masked", "attn_bwd", "attn_bwd_masked",
+            "attn_plan_stats_masked", "attn_bwd_workspace_bytes",
             "attn_workspace_bytes", "attn_plan_stats",
             "attn_last_error", "attn_version", "attn_tile_shape"} <= set(names)
     L = ctypes.CDLL(ea.library_path())
@@ -170,6 +171,88 @@ def test_bwd_workspace_bytes():
     assert ea.attn_bwd_workspace_bytes(2, 8, 1000, 128) == (2 * 8 * 1000 * 4 + 255) // 256 * 256
     assert ea.attn_bwd_workspace_bytes(0, 8, 1000, 128) == 0
     assert ea.attn_bwd_workspace_bytes(1, 1, 16, 96) == 0
+
+
+def _call_masked(mask=None, dtype=ea.ATTN_BF16, **m):
+    with pytest.raises(ea.AttnError) as ei:
+        if mask is False:
+            L = ea.lib()
+            opts = ea._Opts(dtype, 0.0, None, None, 0)
+            ea._check(L.attn_fwd_masked(FAKE, FAKE + (1 << 32), FAKE + (2 << 32), FAKE + (3 << 32),
+                                        FAKE + (4 << 32), 1, 2, 2, 100, 128, None, ctypes.byref(opts)))
+        else:
+            ea.attn_fwd_masked(FAKE, FAKE + (1 << 32), FAKE + (2 << 32), FAKE + (3 << 32), FAKE + (4 << 32),
+                               1, 2, 2, 100, 128, dtype=dtype, **m)
+    return ei.value
+
+
+@pytest.mark.parametrize("m,status,text", [
+    (dict(block=16, win_left=3), ea.ATTN_ERR_INVALID_ARG, "replaces the window"),
+    (dict(block=16, dilation=2), ea.ATTN_ERR_UNSUPPORTED, "cannot be combined"),
+    (dict(dilation=3, global_idx=[5]), ea.ATTN_ERR_UNSUPPORTED, "dilated"),
+    (dict(block=-1), ea.ATTN_ERR_INVALID_ARG, "block"),
+    (dict(dilation=-2), ea.ATTN_ERR_INVALID_ARG, "dilation"),
+    (dict(dilation=2, dtype=ea.ATTN_F32), ea.ATTN_ERR_UNSUPPORTED, "bf16"),
+    (dict(dilation=2, causal=1, scale=-1.0), ea.ATTN_ERR_INVALID_ARG, "scale"),
+])
+def test_masked_validation(m, status, text):
+    dtype = m.pop("dtype", ea.ATTN_BF16)
+    err = _call_masked(dtype=dtype, **m)
+    assert err.status == status, err.message
+    assert text in err.message, err.message
+
+
+def test_masked_null_mask():
+    err = _call_masked(mask=False)
+    assert err.status == ea.ATTN_ERR_INVALID_ARG and "mask" in err.message
+
+
+def test_bwd_rejects_dilation():
+    err = _call_bwd_masked(dilation=2)
+    assert err.status == ea.ATTN_ERR_UNSUPPORTED and "dilated" in err.message
+
+
+def _call_bwd_masked(**m):
+    base = FAKE
+    with pytest.raises(ea.AttnError) as ei:
+        ea.attn_bwd_masked(base, base + (1 << 32), base + (2 << 32), base + (3 << 32), base + (4 << 32),
+                           base + (5 << 32), base + (6 << 32), base + (7 << 32), base + (8 << 32),
+                           1, 4, 2, 100, 128, **m)
+    return ei.value
+
+
+@pytest.mark.parametrize("N", [1, 63, 64, 300, 1000])
+@pytest.mark.parametrize("m", [dict(block=64), dict(block=64, causal=1), dict(block=100, causal=1),
+                               dict(block=7), dict(block=3000), dict(dilation=2, causal=1),
+                               dict(dilation=3), dict(dilation=5, win_left=7, win_right=2),
+                               dict(dilation=4, causal=1, win_left=20, win_right=0),
+                               dict(block=50, causal=1, global_idx=[0, 17])])
+def test_masked_plan_pairs_match_oracle(N, m):
+    G = tuple(g for g in m.get("global_idx", ()) if g < N)
+    mm = dict(m, global_idx=list(G))
+    pairs = ea.attn_plan_stats_masked(N, 256, 64, **mm)[0]
+    ref = oracle.visible_pairs_bruteforce(N, m.get("causal", 0), m.get("win_left", -1), m.get("win_right", -1),
+                                          G, block=m.get("block", 0), dilation=m.get("dilation", 1))
+    assert pairs == ref
+
+
+@pytest.mark.parametrize("N,b", [(300, 64), (1000, 100), (513, 7)])
+@pytest.mark.parametrize("causal", [0, 1])
+def test_block_tiles_match_bruteforce(N, b, causal):
+    """Tile classes of the block rule against the oracle's mask, tile by tile."""
+    vis = oracle.mask_rows(np.arange(N), N, causal, -1, -1, (), b, 1)
+    full = edge = 0
+    for q0 in range(0, N, 256):
+        for k0 in range(0, N, 64):
+            blk = vis[q0:q0 + 256, k0:k0 + 64]
+            if not blk.any():
+                continue
+            if blk.all() and blk.shape == (min(256, N - q0), 64):
+                full += 1
+            else:
+                edge += 1
+    _, f, e = ea.attn_plan_stats_masked(N, 256, 64, causal=causal, block=b)
+    assert (f, e) == (full, edge)
 
 
 def test_inputs_may_alias():
