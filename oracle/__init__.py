@@ -6,7 +6,8 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 from .masked_attention import (attention, probabilities, online_softmax_rows, visible,
                         mask_rows, visible_pairs_bruteforce, useful_flops)
 from .masked_attention_bwd import attention_backward, delta_rows
+from .decode import decode, cache_to_sequence, slot_of
 
 __all__ = ["attention", "probabilities", "online_softmax_rows", "visible",
            "mask_rows", "visible_pairs_bruteforce", "useful_flops",
-           "attention_backward", "delta_rows"]
+           "attention_backward", "delta_rows", "decode", "cache_to_sequence", "slot_of"]
