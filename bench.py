@@ -32,6 +32,7 @@ sys.path.insert(0, ROOT)
 # MI355X dense bf16 MFMA peak: 256 CUs x 2.4 GHz x 4096 flop/clk/CU = 2516.6
 # TFLOP/s (AMD's published 2.5 PFLOP/s); dense fp32 MFMA: 157.3 TFLOP/s.
 PEAK_BF16 = 2516.6
+PEAK_HBM_GBS = 8000.0   # MI355X HBM3E, published
 PEAK_F32 = 157.3
 METRIC = "fwd attention TFLOP/s (unmasked FLOPs only) + % of bf16 MFMA peak"
 KERNEL_SRC = os.path.join(ROOT, "efficient_exact_attention_amd", "csrc", "attn_fwd.hip")
@@ -143,6 +144,9 @@ def main():
     ap.add_argument("--bwd", action="store_true",
                     help="time the backward pass (attn_bwd) of the workload instead; useful FLOP = "
                          "10*d per visible pair (five matrix products)")
+    ap.add_argument("--decode", default=None, choices=sorted(W.DECODE_WORKLOADS),
+                    help="time one decoding step (attn_decode) of this cache workload instead; "
+                         "HBM-bound, reported in GB/s of K/V cache read")
     ap.add_argument("--cold", action="store_true",
                     help="write a 1 GiB scratch buffer before every timed call (cold MALL)")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -168,6 +172,8 @@ def main():
         return sweep(args)
     if args.bwd:
         return bench_bwd(args)
+    if args.decode:
+        return bench_decode(args)
 
     w = W.WORKLOADS[args.config]
     print(f"[bench] generating {w.name}: B={w.B} H={w.H} N={w.N} d={w.d} {w.dtype}", file=sys.stderr,
@@ -319,6 +325,66 @@ def bench_bwd(args):
                       "config": {"workload": f"{mask_name(w)} attention backward B={w.B} H={w.H} N={w.N} d={w.d}",
                                  "useful_flop_per_step": flops},
                       "pct_bf16_peak": round(100 * value / PEAK_BF16, 2)}), flush=True)
+    return 0
+
+
+def decode_bytes(w):
+    """Algorithmic HBM bytes of one decoding step: the K and V rows of every
+    position some new query sees (each read once), the queries, the bf16
+    outputs and the fp32 LSE."""
+    seen = 0
+    for L in w.seq_len:
+        span = L if w.win_left < 0 else min(L, w.Nq + w.win_left)
+        seen += min(span, w.S)
+    return 2 * seen * w.H_kv * w.d * 2 + w.B * w.H * w.Nq * (2 * w.d * 2 + 4)
+
+
+def bench_decode(args):
+    """One decoding step over a K/V cache resident in HBM: the split-KV pass
+    and the merge (one attn_decode call). Prints one JSON line whose
+    roofline is HBM bandwidth over the algorithmic bytes."""
+    import torch
+    import efficient_exact_attention_amd as ea
+    from efficient_exact_attention_amd import workloads as W
+    w = W.DECODE_WORKLOADS[args.decode]
+    print(f"[bench] generating {w.name}: {w.desc}", file=sys.stderr, flush=True)
+    q, kc, vc, seq = W.make_decode(w)
+    dq, dk, dv = (torch.from_numpy(x.view("int16")).view(torch.bfloat16).cuda() for x in (q, kc, vc))
+    ds = torch.from_numpy(seq).cuda()
+    out = torch.empty_like(dq)
+    lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    nbytes = decode_bytes(w)
+
+    def step():
+        ea.decode(dq, dk, dv, ds, win_left=w.win_left, rolling=bool(w.rolling), out=out, lse=lse, stream=stream)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for s_, e_ in ev:
+        s_.record(stream)
+        step()
+        e_.record(stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = sorted(s_.elapsed_time(e_) for s_, e_ in ev)
+    avg = sum(ms) / len(ms)
+    gbs = nbytes / (avg * 1e-3) / 1e9
+    steps_s = 1e3 / avg
+    print(json.dumps({"metric": "decode steps/s (one new token per sequence, all heads)",
+                      "value": round(steps_s, 2), "unit": "steps/s", "n_gpus": 1, "steps": args.steps,
+                      "warmup": args.warmup, "ms_per_step": round(t0.elapsed_time(t1) / args.steps, 4),
+                      "median_launch_ms": round(ms[len(ms) // 2], 4), "higher_is_better": True,
+                      "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+                      "config": {"workload": f"decode {w.desc}: B={w.B} H={w.H} H_kv={w.H_kv} Nq={w.Nq} "
+                                             f"S={w.S} d={w.d}", "algorithmic_bytes_per_step": nbytes},
+                      "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                                   "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}}),
+          flush=True)
     return 0
 
 

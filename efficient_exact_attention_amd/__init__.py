@@ -10,7 +10,8 @@ import ctypes
 import os
 
 __all__ = ["AttnError", "attn_fwd", "attn_fwd_ex", "attn_fwd_gqa", "attn_fwd_masked", "attn_bwd", "attn_bwd_masked",
-           "attn_bwd_workspace_bytes", "attn_plan_stats_masked", "bwd", "attn_workspace_bytes", "attn_plan_stats",
+           "attn_bwd_workspace_bytes", "attn_plan_stats_masked", "bwd", "attn_decode",
+           "attn_decode_workspace_bytes", "decode", "attn_workspace_bytes", "attn_plan_stats",
            "attn_tile_shape", "attn_last_error", "attn_version", "fwd", "library_path",
            "ATTN_OK", "ATTN_ERR_INVALID_ARG", "ATTN_ERR_UNSUPPORTED", "ATTN_ERR_DEVICE",
            "ATTN_BF16", "ATTN_F32"]
@@ -80,6 +81,10 @@ def lib():
     L.attn_bwd_masked.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ctypes.POINTER(_Mask),
                                   ctypes.POINTER(_Opts)]
     L.attn_bwd_masked.restype = ci
+    L.attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, ci, ctypes.POINTER(_Opts)]
+    L.attn_decode.restype = ci
+    L.attn_decode_workspace_bytes.argtypes = [ci, ci, ci, ci, ci, ci]
+    L.attn_decode_workspace_bytes.restype = ctypes.c_size_t
     L.attn_bwd_workspace_bytes.argtypes = [ci, ci, ci, ci]
     L.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
     L.attn_workspace_bytes.argtypes = [ci, ci, ci, ci, ci]
@@ -179,6 +184,18 @@ def attn_plan_stats_masked(N, bm, bn, *, causal=0, win_left=-1, win_right=-1, bl
     _check(lib().attn_plan_stats_masked(N, ctypes.byref(m), bm, bn, ctypes.byref(a), ctypes.byref(b),
                                         ctypes.byref(c)))
     return a.value, b.value, c.value
+
+
+def attn_decode(q, k_cache, v_cache, seq_len, out, lse, B, H, H_kv, Nq, S, d, win_left=-1, rolling=0, *,
+                dtype=ATTN_BF16, scale=0.0, stream=None, workspace=None, workspace_bytes=0):
+    """Raw decoding entry point (seq_len is a device int32 array of B)."""
+    opts = _Opts(dtype, float(scale), stream, workspace, workspace_bytes)
+    _check(lib().attn_decode(q, k_cache, v_cache, seq_len, out, lse, B, H, H_kv, Nq, S, d, win_left, rolling,
+                             ctypes.byref(opts)))
+
+
+def attn_decode_workspace_bytes(B, H, H_kv, Nq, S, d) -> int:
+    return int(lib().attn_decode_workspace_bytes(B, H, H_kv, Nq, S, d))
 
 
 def attn_bwd_workspace_bytes(B, H, N, d) -> int:
@@ -285,3 +302,41 @@ def bwd(q, k, v, out, dout, lse, *, causal=False, win_left=-1, win_right=-1, glo
                     global_idx=global_idx, scale=0.0 if scale is None else float(scale), stream=stream,
                     workspace=ws, workspace_bytes=wsb)
     return dq, dk, dv
+
+
+def decode(q, k_cache, v_cache, seq_len, *, win_left=-1, rolling=False, scale=None, out=None, lse=None,
+           workspace=None, stream=None):
+    """One decoding step on torch CUDA bf16 tensors: q [B, H, Nq, d] holds the
+    queries of each sequence's Nq newest positions, k_cache and v_cache
+    [B, H_kv, S, d] the cached keys and values (the new positions included),
+    seq_len a device int32 tensor [B] of sequence lengths. ``rolling`` keeps
+    position p in slot p % S. Returns (out [B, H, Nq, d], lse fp32 [B, H, Nq])
+    without synchronising."""
+    import torch
+    if q.dim() != 4 or k_cache.dim() != 4:
+        raise ValueError("q must be [B, H, Nq, d] and the caches [B, H_kv, S, d]")
+    B, H, Nq, d = q.shape
+    H_kv, S = k_cache.shape[1], k_cache.shape[2]
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
+        if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous bf16 device tensor")
+    if v_cache.shape != k_cache.shape or k_cache.shape[0] != B or k_cache.shape[3] != d:
+        raise ValueError("caches must be [B, H_kv, S, d] matching q")
+    if seq_len.dtype != torch.int32 or seq_len.shape != (B,) or not seq_len.is_cuda or not seq_len.is_contiguous():
+        raise ValueError("seq_len must be a contiguous int32 device tensor [B]")
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if lse is None else lse
+    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor shaped and typed like q")
+    if lse.shape != (B, H, Nq) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous fp32 tensor [B, H, Nq]")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    ws, wsb = (workspace.data_ptr(), workspace.numel() * workspace.element_size()) \
+        if workspace is not None else (None, 0)
+    attn_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), seq_len.data_ptr(), out.data_ptr(),
+                lse.data_ptr(), B, H, H_kv, Nq, S, d, win_left, int(bool(rolling)),
+                scale=0.0 if scale is None else float(scale), stream=stream, workspace=ws, workspace_bytes=wsb)
+    return out, lse

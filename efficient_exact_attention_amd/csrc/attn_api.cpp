@@ -495,9 +495,111 @@ int bwd_impl(const void *q, const void *k, const void *v, const void *out, const
     return ATTN_OK;
 }
 
+size_t decode_workspace(int B, int H, int H_kv, int Nq, int S, int d) {
+    const int group = H / H_kv;
+    const long long R = (long long)group * Nq;
+    const int nrg = (int)((R + eea::kDecRows - 1) / eea::kDecRows);
+    const int chunks = eea::decode_chunks(B, H_kv, nrg, S, nullptr);
+    return (size_t)B * H * Nq * chunks * (d + 2) * sizeof(float);
+}
+
+int decode_impl(const void *q, const void *kc, const void *vc, const int *seq_len, void *out, float *lse, int B,
+                int H, int H_kv, int Nq, int S, int d, int win_left, int rolling, const attn_opts *opts) {
+    g_err.clear();
+    const int dtype = opts ? opts->dtype : ATTN_BF16;
+    if (!q || !kc || !vc || !seq_len || !out || !lse) return fail(ATTN_ERR_INVALID_ARG, "a pointer is NULL");
+    if (B <= 0 || H <= 0 || Nq <= 0 || S <= 0)
+        return fail(ATTN_ERR_INVALID_ARG, "sizes B=%d H=%d Nq=%d S=%d must be positive", B, H, Nq, S);
+    if (H_kv <= 0 || H % H_kv != 0)
+        return fail(ATTN_ERR_INVALID_ARG, "H_kv=%d must be positive and divide H=%d", H_kv, H);
+    if (dtype != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "decoding supports bf16 tensors only");
+    if (d != 64 && d != 128) return fail(ATTN_ERR_UNSUPPORTED, "head size d=%d is not supported (64 or 128)", d);
+    if (win_left < -1) return fail(ATTN_ERR_INVALID_ARG, "win_left=%d must be >= -1", win_left);
+    if (rolling != 0 && rolling != 1) return fail(ATTN_ERR_INVALID_ARG, "rolling=%d must be 0 or 1", rolling);
+    if (Nq > S) return fail(ATTN_ERR_INVALID_ARG, "Nq=%d new tokens do not fit a cache of S=%d slots", Nq, S);
+    if (rolling && (win_left < 0 || (long long)Nq + win_left > S))
+        return fail(ATTN_ERR_INVALID_ARG,
+                    "a rolling cache of S=%d slots needs a window with Nq + win_left <= S (Nq=%d, win_left=%d)", S,
+                    Nq, win_left);
+    if ((long long)S * d * 2 > INT_MAX)
+        return fail(ATTN_ERR_UNSUPPORTED, "one head's cache of S=%d x d=%d elements exceeds 2 GiB", S, d);
+    const long long BH = (long long)B * H;
+    const long long R = (long long)(H / H_kv) * Nq;
+    const int nrg = (int)((R + eea::kDecRows - 1) / eea::kDecRows);
+    int ct = 0;
+    const int chunks = eea::decode_chunks(B, H_kv, nrg, S, &ct);
+    if (BH * Nq > INT_MAX || (long long)B * H_kv * nrg * chunks > INT_MAX)
+        return fail(ATTN_ERR_INVALID_ARG, "sizes exceed the launch grid");
+    const size_t qbytes = (size_t)BH * Nq * d * 2;
+    const size_t cbytes = (size_t)B * H_kv * S * d * 2;
+    const size_t lbytes = (size_t)BH * Nq * sizeof(float);
+    if (((uintptr_t)q | (uintptr_t)kc | (uintptr_t)vc | (uintptr_t)out) & 15)
+        return fail(ATTN_ERR_INVALID_ARG, "q, k_cache, v_cache and out must be 16-byte aligned");
+    if (((uintptr_t)lse | (uintptr_t)seq_len) & 3) return fail(ATTN_ERR_INVALID_ARG, "lse and seq_len must be 4-byte aligned");
+    if (overlaps(out, qbytes, q, qbytes) || overlaps(out, qbytes, kc, cbytes) || overlaps(out, qbytes, vc, cbytes) ||
+        overlaps(out, qbytes, seq_len, (size_t)B * 4))
+        return fail(ATTN_ERR_INVALID_ARG, "out overlaps an input");
+    if (overlaps(lse, lbytes, q, qbytes) || overlaps(lse, lbytes, kc, cbytes) || overlaps(lse, lbytes, vc, cbytes) ||
+        overlaps(lse, lbytes, out, qbytes) || overlaps(lse, lbytes, seq_len, (size_t)B * 4))
+        return fail(ATTN_ERR_INVALID_ARG, "lse overlaps another tensor");
+    const float scale = (opts && opts->scale != 0.f) ? opts->scale : 1.0f / std::sqrt((float)d);
+    if (!(scale > 0.f) || !std::isfinite(scale))
+        return fail(ATTN_ERR_INVALID_ARG, "scale must be positive and finite");
+    const size_t need = (size_t)BH * Nq * chunks * (d + 2) * sizeof(float);
+    void *ws = nullptr;
+    if (opts && opts->workspace) {
+        if (opts->workspace_bytes < need)
+            return fail(ATTN_ERR_INVALID_ARG, "workspace of %zu bytes is smaller than the %zu needed",
+                        opts->workspace_bytes, need);
+        if ((uintptr_t)opts->workspace & 15) return fail(ATTN_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+        ws = opts->workspace;
+    }
+
+    eea::DecParams p;
+    std::memset(&p, 0, sizeof p);
+    p.q = q;
+    p.kc = kc;
+    p.vc = vc;
+    p.out = out;
+    p.lse = lse;
+    p.seq_len = seq_len;
+    p.B = B;
+    p.H = H;
+    p.H_kv = H_kv;
+    p.group = H / H_kv;
+    p.Nq = Nq;
+    p.S = S;
+    p.win = win_left;
+    p.rolling = rolling;
+    p.R = (int)R;
+    p.nrg = nrg;
+    p.chunks = chunks;
+    p.chunk_tiles = ct;
+    p.scale_log2 = scale * 1.4426950408889634f;
+
+    int rc = device_and_scratch(need, &ws, true);
+    if (rc != ATTN_OK) return rc;
+    p.part = static_cast<float *>(ws);
+    hipStream_t stream = opts ? static_cast<hipStream_t>(opts->stream) : nullptr;
+    hipError_t e = eea::launch_decode(p, d, stream);
+    if (e != hipSuccess) return fail(ATTN_ERR_DEVICE, "kernel launch: %s", hipGetErrorString(e));
+    return ATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int attn_decode(const void *q, const void *k_cache, const void *v_cache, const int *seq_len, void *out,
+                float *lse, int B, int H, int H_kv, int Nq, int S, int d, int win_left, int rolling,
+                const attn_opts *opts) {
+    return decode_impl(q, k_cache, v_cache, seq_len, out, lse, B, H, H_kv, Nq, S, d, win_left, rolling, opts);
+}
+
+size_t attn_decode_workspace_bytes(int B, int H, int H_kv, int Nq, int S, int d) {
+    if (B <= 0 || H <= 0 || H_kv <= 0 || H % H_kv != 0 || Nq <= 0 || S <= 0 || (d != 64 && d != 128)) return 0;
+    return decode_workspace(B, H, H_kv, Nq, S, d);
+}
 
 int attn_bwd(const void *q, const void *k, const void *v, const void *out, const void *dout, const float *lse,
              void *dq, void *dk, void *dv, int B, int H, int H_kv, int N, int d, int causal, int win_left,

@@ -64,6 +64,28 @@ struct BwdParams {
 };
 
 hipError_t launch_backward(const BwdParams &p, int d, hipStream_t stream);
+
+// Decode arguments: the newest Nq queries of each sequence against a cache.
+struct DecParams {
+    const void *q;          // [B][H][Nq][d] bf16
+    const void *kc, *vc;    // [B][H_kv][S][d] bf16
+    void *out;              // [B][H][Nq][d] bf16
+    float *lse;             // [B][H][Nq]
+    float *part;            // workspace: [B*H*Nq][chunks][d + 2] partial (o, m, l)
+    const int *seq_len;     // device [B]: total length of each sequence
+    int B, H, H_kv, group, Nq, S;
+    int win;                // positions i - win .. i are visible (-1: unbounded)
+    int rolling;            // 1: position p lives in slot p % S
+    int R;                  // query rows per K/V head: group * Nq
+    int nrg;                // row groups of kDecRows per K/V head
+    int chunks;             // key chunks per row group
+    int chunk_tiles;        // 64-slot tiles per chunk
+    float scale_log2;
+};
+
+constexpr int kDecRows = 64;   // query rows per decode workgroup (two waves)
+hipError_t launch_decode(const DecParams &p, int d, hipStream_t stream);
+int decode_chunks(int B, int H_kv, int nrg, int S, int *chunk_tiles);
 int bwd_tile_q(int d);      // query rows per dQ workgroup
 int bwd_tile_k(int d);      // keys per dK/dV workgroup
 

@@ -16,6 +16,12 @@ The shapes and mask arguments are the five workloads of the exact-attention
 pages (causal, Mistral-style sliding window, long-context causal,
 Longformer/BigBird-style local+global) plus the causal N=32768 d=128 shape the
 throughput target is quoted on.
+
+Decoding workloads (``DecodeWorkload``) draw the Nq new queries [B][H][Nq][d]
+and the K and V caches [B][H_kv][S][d] with the same per-head recipe (Q from
+one seed, the caches from seed + 1); cache slots that hold no position of a
+sequence (slot >= min(S, L_b)) are set to bf16 NaN, so a kernel that reads
+them shows it.
 """
 from __future__ import annotations
 
@@ -157,3 +163,71 @@ def random_workload(name: str, B: int, H: int, N: int, d: int, *, dtype="bf16",
                     global_idx=(), seed=0) -> Workload:
     return Workload(name, B, H, N, d, dtype, sigma, causal, win_left, win_right,
                     tuple(global_idx), seed, "ad-hoc")
+
+
+@dataclass(frozen=True)
+class DecodeWorkload:
+    """One decoding step: Nq new tokens per sequence against a cache of S
+    slots per K/V head; seq_len[b] counts the sequence's tokens, new ones
+    included."""
+    name: str
+    B: int
+    H: int
+    H_kv: int
+    Nq: int
+    S: int
+    d: int
+    win_left: int
+    rolling: int
+    seq_len: tuple
+    seed: int = 0
+    desc: str = ""
+
+    def cache_bytes(self) -> int:
+        """Bytes of K and V cache slots that hold a position of some sequence."""
+        used = sum(min(self.S, L) for L in self.seq_len)
+        return 2 * used * self.H_kv * self.d * 2
+
+
+DECODE_WORKLOADS = {
+    # 64 query heads over 8 K/V heads (the grouped-query shape of the GQA
+    # passage), one new token, a full 32768-token contiguous cache
+    "dec_full": DecodeWorkload("dec_full", 8, 64, 8, 1, 32768, 128, -1, 0, (32768,) * 8, 201,
+                               "GQA 64/8, contiguous cache, L=32768"),
+    # the same heads over a rolling sliding-window cache of 4096 positions at
+    # L=32768 (each cache 8x smaller than the full one)
+    "dec_swa": DecodeWorkload("dec_swa", 64, 64, 8, 1, 4096, 128, 4095, 1, (32768,) * 64, 202,
+                              "GQA 64/8, rolling cache W=4096, L=32768"),
+}
+
+_BF16_NAN = np.uint16(0x7FC0)
+
+
+def make_decode(w: DecodeWorkload, b_list=None):
+    """(q, k_cache, v_cache, seq_len) host arrays: bf16 bit patterns and int32
+    lengths. b_list restricts the draw to those batch entries (the others
+    stay zero), for checks that read a few entries of a large workload."""
+    sq = np.random.SeedSequence(w.seed).spawn(w.B * w.H)
+    sk = np.random.SeedSequence(w.seed + 1).spawn(2 * w.B * w.H_kv)
+    q = np.zeros((w.B, w.H, w.Nq, w.d), np.uint16)
+    kc = np.zeros((w.B, w.H_kv, w.S, w.d), np.uint16)
+    vc = np.zeros((w.B, w.H_kv, w.S, w.d), np.uint16)
+    bs = range(w.B) if b_list is None else b_list
+
+    def fill(job):
+        t, b, h = job
+        if t == 0:
+            x = np.random.default_rng(sq[b * w.H + h]).standard_normal((w.Nq, w.d), dtype=np.float32)
+            q[b, h] = round_to_bf16_bits(x)
+            return
+        dst = kc if t == 1 else vc
+        x = np.random.default_rng(sk[(t - 1) * w.B * w.H_kv + b * w.H_kv + h]).standard_normal(
+            (w.S, w.d), dtype=np.float32)
+        dst[b, h] = round_to_bf16_bits(x)
+        dst[b, h, min(w.S, w.seq_len[b]):] = _BF16_NAN
+
+    jobs = [(0, b, h) for b in bs for h in range(w.H)] + \
+        [(t, b, h) for t in (1, 2) for b in bs for h in range(w.H_kv)]
+    with ThreadPoolExecutor(min(16, len(os.sched_getaffinity(0)))) as ex:
+        list(ex.map(fill, jobs))
+    return q, kc, vc, np.asarray(w.seq_len, np.int32)

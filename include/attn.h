@@ -209,6 +209,45 @@ int attn_bwd_masked(const void *q, const void *k, const void *v, const void *out
 size_t attn_bwd_workspace_bytes(int B, int H, int N, int d);
 
 /*
+ * attn_decode - one decoding step over a key/value cache: the Nq newest
+ * tokens of each sequence attend over the keys and values kept for every
+ * earlier token and themselves (week-17 lecture notes: per-token inference
+ * with a KV cache; "Beyond attention": a sliding window needs a rolling cache
+ * of only W positions). Exact: the result equals the last Nq rows of the
+ * causal (optionally windowed) forward over the whole sequence.
+ *
+ *   q           [B][H][Nq][d] bf16: queries of positions L_b-Nq .. L_b-1.
+ *   k_cache,
+ *   v_cache     [B][H_kv][S][d] bf16 caches of S slots (H_kv divides H;
+ *               query head h reads K/V head h / (H / H_kv)).
+ *   seq_len     DEVICE array of B int32: L_b, the length of sequence b
+ *               including the Nq new tokens, whose keys and values must
+ *               already be in the cache. Must satisfy Nq <= L_b, and
+ *               L_b <= S for a contiguous cache; values outside are clamped
+ *               into that range.
+ *   out         [B][H][Nq][d] bf16 output; lse [B][H][Nq] fp32 (natural log).
+ *   win_left    position i sees positions i - win_left .. i (-1: all earlier
+ *               positions).
+ *   rolling     0: position p is in slot p (contiguous cache). 1: position p
+ *               is in slot p % S (the cache keeps the last S positions); needs
+ *               win_left >= 0 and Nq + win_left <= S so every visible
+ *               position is still cached.
+ *   opts        bf16 only; scale, stream; workspace of at least
+ *               attn_decode_workspace_bytes (else the library's scratch).
+ * Errors are reported as for attn_fwd_ex, before any launch.
+ */
+int attn_decode(const void *q, const void *k_cache, const void *v_cache, const int *seq_len,
+                void *out, float *lse, int B, int H, int H_kv, int Nq, int S, int d,
+                int win_left, int rolling, const attn_opts *opts);
+
+/*
+ * attn_decode_workspace_bytes - device scratch attn_decode needs for its
+ * per-chunk partial results (B*H*Nq*chunks*(d+2)*4 bytes, chunks <= S/64);
+ * 0 for invalid sizes.
+ */
+size_t attn_decode_workspace_bytes(int B, int H, int H_kv, int Nq, int S, int d);
+
+/*
  * attn_workspace_bytes - device scratch a call with these sizes needs for the
  * global-row partial results; 0 when n_global = 0. It grows with
  * B*H*n_global*d and a chunk count bounded by N/64, never with N*N.

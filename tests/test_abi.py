@@ -27,7 +27,7 @@ def declared_functions():
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
     assert {"attn_fwd", "attn_fwd_ex", "attn_fwd_gqa", "attn_fwd_masked", "attn_bwd", "attn_bwd_masked",
-            "attn_plan_stats_masked", "attn_bwd_workspace_bytes",
+            "attn_plan_stats_masked", "attn_bwd_workspace_bytes", "attn_decode", "attn_decode_workspace_bytes",
             "attn_workspace_bytes", "attn_plan_stats",
             "attn_last_error", "attn_version", "attn_tile_shape"} <= set(names)
     L = ctypes.CDLL(ea.library_path())
@@ -359,3 +359,60 @@ def test_window_equivalence_gives_same_plan():
     a = ea.attn_plan_stats(1000, 1, -1, -1, None, 128, 64)
     for wl in (999, 5000):
         assert ea.attn_plan_stats(1000, 1, wl, 0, None, 128, 64) == a
+
+
+# ---- decoding: validation only (no call reaches the device) -----------------------
+
+def _call_decode(**over):
+    a = dict(q=FAKE, k=FAKE + (1 << 32), v=FAKE + (2 << 32), seq=FAKE + (3 << 32), out=FAKE + (4 << 32),
+             lse=FAKE + (5 << 32), B=2, H=8, H_kv=2, Nq=1, S=1000, d=128, win_left=-1, rolling=0)
+    opts = {}
+    for key in ("dtype", "scale", "workspace", "workspace_bytes"):
+        if key in over:
+            opts[key] = over.pop(key)
+    a.update(over)
+    with pytest.raises(ea.AttnError) as ei:
+        ea.attn_decode(a["q"], a["k"], a["v"], a["seq"], a["out"], a["lse"], a["B"], a["H"], a["H_kv"],
+                       a["Nq"], a["S"], a["d"], a["win_left"], a["rolling"], **opts)
+    return ei.value
+
+
+@pytest.mark.parametrize("over,status,text", [
+    (dict(q=0), ea.ATTN_ERR_INVALID_ARG, "NULL"),
+    (dict(seq=0), ea.ATTN_ERR_INVALID_ARG, "NULL"),
+    (dict(B=0), ea.ATTN_ERR_INVALID_ARG, "positive"),
+    (dict(Nq=0), ea.ATTN_ERR_INVALID_ARG, "positive"),
+    (dict(S=-1), ea.ATTN_ERR_INVALID_ARG, "positive"),
+    (dict(H_kv=3), ea.ATTN_ERR_INVALID_ARG, "divide"),
+    (dict(H_kv=0), ea.ATTN_ERR_INVALID_ARG, "divide"),
+    (dict(dtype=ea.ATTN_F32), ea.ATTN_ERR_UNSUPPORTED, "bf16"),
+    (dict(d=96), ea.ATTN_ERR_UNSUPPORTED, "head size"),
+    (dict(win_left=-2), ea.ATTN_ERR_INVALID_ARG, "win_left"),
+    (dict(rolling=2), ea.ATTN_ERR_INVALID_ARG, "rolling"),
+    (dict(Nq=1001), ea.ATTN_ERR_INVALID_ARG, "do not fit"),
+    (dict(rolling=1), ea.ATTN_ERR_INVALID_ARG, "rolling cache"),
+    (dict(rolling=1, win_left=1000), ea.ATTN_ERR_INVALID_ARG, "rolling cache"),
+    (dict(rolling=1, Nq=4, win_left=997), ea.ATTN_ERR_INVALID_ARG, "rolling cache"),
+    (dict(q=FAKE + 8), ea.ATTN_ERR_INVALID_ARG, "aligned"),
+    (dict(seq=FAKE + (3 << 32) + 2), ea.ATTN_ERR_INVALID_ARG, "aligned"),
+    (dict(out=FAKE + 512), ea.ATTN_ERR_INVALID_ARG, "overlaps"),
+    (dict(lse=FAKE + (4 << 32) + 64), ea.ATTN_ERR_INVALID_ARG, "overlaps"),
+    (dict(scale=-1.0), ea.ATTN_ERR_INVALID_ARG, "scale"),
+    (dict(workspace=FAKE + (9 << 32), workspace_bytes=64), ea.ATTN_ERR_INVALID_ARG, "workspace"),
+    # a valid rolling configuration passes every check and stops at the scale
+    (dict(rolling=1, Nq=4, win_left=996, scale=-1.0), ea.ATTN_ERR_INVALID_ARG, "scale"),
+])
+def test_decode_validation(over, status, text):
+    err = _call_decode(**over)
+    assert err.status == status, err.message
+    assert text in err.message, err.message
+
+
+def test_decode_workspace_bytes():
+    for (B, H, Hkv, Nq, S, d) in [(1, 32, 8, 1, 32768, 128), (4, 8, 8, 4, 100, 64), (2, 64, 1, 1, 4096, 128)]:
+        n = ea.attn_decode_workspace_bytes(B, H, Hkv, Nq, S, d)
+        per_row = n // (B * H * Nq * (d + 2) * 4)
+        assert n == B * H * Nq * (d + 2) * 4 * per_row
+        assert 1 <= per_row <= max(1, (S + 63) // 64)      # one partial per key chunk
+    assert ea.attn_decode_workspace_bytes(1, 6, 4, 1, 100, 128) == 0
+    assert ea.attn_decode_workspace_bytes(1, 8, 8, 1, 100, 96) == 0
