@@ -83,7 +83,7 @@ def lib():
     L.attn_bwd_masked.restype = ci
     L.attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, ci, ctypes.POINTER(_Opts)]
     L.attn_decode.restype = ci
-    L.attn_decode_workspace_bytes.argtypes = [ci, ci, ci, ci, ci, ci]
+    L.attn_decode_workspace_bytes.argtypes = [ci, ci, ci, ci, ci, ci, ci, ci]
     L.attn_decode_workspace_bytes.restype = ctypes.c_size_t
     L.attn_bwd_workspace_bytes.argtypes = [ci, ci, ci, ci]
     L.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
@@ -194,8 +194,8 @@ def attn_decode(q, k_cache, v_cache, seq_len, out, lse, B, H, H_kv, Nq, S, d, wi
                              ctypes.byref(opts)))
 
 
-def attn_decode_workspace_bytes(B, H, H_kv, Nq, S, d) -> int:
-    return int(lib().attn_decode_workspace_bytes(B, H, H_kv, Nq, S, d))
+def attn_decode_workspace_bytes(B, H, H_kv, Nq, S, d, win_left=-1, rolling=0) -> int:
+    return int(lib().attn_decode_workspace_bytes(B, H, H_kv, Nq, S, d, win_left, int(bool(rolling))))
 
 
 def attn_bwd_workspace_bytes(B, H, N, d) -> int:

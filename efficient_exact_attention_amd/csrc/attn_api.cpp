@@ -495,12 +495,12 @@ int bwd_impl(const void *q, const void *k, const void *v, const void *out, const
     return ATTN_OK;
 }
 
-size_t decode_workspace(int B, int H, int H_kv, int Nq, int S, int d) {
+size_t decode_workspace(int B, int H, int H_kv, int Nq, int S, int d, int win_left, int rolling) {
     const int group = H / H_kv;
     const long long R = (long long)group * Nq;
     const int nrg = (int)((R + eea::kDecRows - 1) / eea::kDecRows);
-    const int chunks = eea::decode_chunks(B, H_kv, nrg, S, nullptr);
-    return (size_t)B * H * Nq * chunks * (d + 2) * sizeof(float);
+    const int chunks = eea::decode_chunks(B, H_kv, nrg, S, Nq, win_left, rolling);
+    return chunks == 1 ? 0 : (size_t)B * H * Nq * chunks * (d + 2) * sizeof(float);
 }
 
 int decode_impl(const void *q, const void *kc, const void *vc, const int *seq_len, void *out, float *lse, int B,
@@ -526,8 +526,7 @@ int decode_impl(const void *q, const void *kc, const void *vc, const int *seq_le
     const long long BH = (long long)B * H;
     const long long R = (long long)(H / H_kv) * Nq;
     const int nrg = (int)((R + eea::kDecRows - 1) / eea::kDecRows);
-    int ct = 0;
-    const int chunks = eea::decode_chunks(B, H_kv, nrg, S, &ct);
+    const int chunks = eea::decode_chunks(B, H_kv, nrg, S, Nq, win_left, rolling);
     if (BH * Nq > INT_MAX || (long long)B * H_kv * nrg * chunks > INT_MAX)
         return fail(ATTN_ERR_INVALID_ARG, "sizes exceed the launch grid");
     const size_t qbytes = (size_t)BH * Nq * d * 2;
@@ -545,7 +544,7 @@ int decode_impl(const void *q, const void *kc, const void *vc, const int *seq_le
     const float scale = (opts && opts->scale != 0.f) ? opts->scale : 1.0f / std::sqrt((float)d);
     if (!(scale > 0.f) || !std::isfinite(scale))
         return fail(ATTN_ERR_INVALID_ARG, "scale must be positive and finite");
-    const size_t need = (size_t)BH * Nq * chunks * (d + 2) * sizeof(float);
+    const size_t need = decode_workspace(B, H, H_kv, Nq, S, d, win_left, rolling);
     void *ws = nullptr;
     if (opts && opts->workspace) {
         if (opts->workspace_bytes < need)
@@ -574,7 +573,6 @@ int decode_impl(const void *q, const void *kc, const void *vc, const int *seq_le
     p.R = (int)R;
     p.nrg = nrg;
     p.chunks = chunks;
-    p.chunk_tiles = ct;
     p.scale_log2 = scale * 1.4426950408889634f;
 
     int rc = device_and_scratch(need, &ws, true);
@@ -596,9 +594,11 @@ int attn_decode(const void *q, const void *k_cache, const void *v_cache, const i
     return decode_impl(q, k_cache, v_cache, seq_len, out, lse, B, H, H_kv, Nq, S, d, win_left, rolling, opts);
 }
 
-size_t attn_decode_workspace_bytes(int B, int H, int H_kv, int Nq, int S, int d) {
-    if (B <= 0 || H <= 0 || H_kv <= 0 || H % H_kv != 0 || Nq <= 0 || S <= 0 || (d != 64 && d != 128)) return 0;
-    return decode_workspace(B, H, H_kv, Nq, S, d);
+size_t attn_decode_workspace_bytes(int B, int H, int H_kv, int Nq, int S, int d, int win_left, int rolling) {
+    if (B <= 0 || H <= 0 || H_kv <= 0 || H % H_kv != 0 || Nq <= 0 || S <= 0 || (d != 64 && d != 128) ||
+        win_left < -1)
+        return 0;
+    return decode_workspace(B, H, H_kv, Nq, S, d, win_left, rolling != 0);
 }
 
 int attn_bwd(const void *q, const void *k, const void *v, const void *out, const void *dout, const float *lse,

@@ -15,6 +15,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <climits>
+#include <type_traits>
+#include <utility>
 
 #include "attn_internal.h"
 #include "attn_plan.h"
@@ -22,27 +24,84 @@
 
 namespace eea {
 
-constexpr int kDecThreads = 128;   // two waves, kDecRows query rows
+constexpr int kDecThreads = 256;     // four waves of 32 query rows each
+constexpr int kDecLds = 163840;      // the whole LDS of a CU: one workgroup per CU
+constexpr int kDecCUs = 256;         // compute units of an MI355X
 
-// Position held by cache slot s when the sequence has length L (negative:
-// the slot holds no position of this sequence). A rolling cache keeps
-// position p in slot p % S, so slot s holds the newest p <= L-1 with
-// p = s (mod S).
-__device__ __forceinline__ int slot_position(int s, int L, int S, int rolling) {
-    if (s >= S) return -1;
-    if (!rolling) return s < L ? s : -1;
-    const int x = L - 1 - s;
-    return L - 1 - ((x % S) + S) % S;
+// s_waitcnt vmcnt(C) leaving the other counters alone (gfx9 encoding).
+template <int C>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(C >= 0 && C < 64, "vmcnt holds 6 bits");
+    __builtin_amdgcn_s_waitcnt((C & 15) | ((C >> 4) << 14) | 0x0F70);
 }
 
-template <int D>
+// Wait until at most `younger` tiles of LPT loads each are still in flight
+// (younger is wave-uniform, 0 .. N).
+template <int LPT, int N>
+__device__ __forceinline__ void wait_tiles(int younger) {
+    if constexpr (N == 0) {
+        wait_vm<0>();
+    } else {
+        if (younger >= N) wait_vm<N * LPT>();
+        else wait_tiles<LPT, N - 1>(younger);
+    }
+}
+
+// f(integral_constant<int, 0>) .. f(integral_constant<int, N-1>), unrolled.
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// Slot -> position. With sl = (L-1) mod S the slot of the newest position,
+// a rolling cache holds position s + off in slots s <= sl and s + off - S
+// in slots s > sl, where off = L-1-sl (a negative result: the slot holds
+// no position yet). A contiguous cache is the case off = 0, sl >= every s.
+struct SlotMap {
+    int off, sl, S;
+    __device__ __forceinline__ int pos(int s) const { return s + off - (s > sl ? S : 0); }
+};
+
+// KS2 (for at most 64 query rows): waves 2w and 2w+1 hold the same 32 rows
+// and take the first and the second 32-key block of every tile, each with an
+// online softmax of its own, combined at the end; every wave then computes.
+// Otherwise each wave holds 32 rows of its own against whole tiles.
+template <int D, bool KS2>
 __global__ void __launch_bounds__(kDecThreads) decode_kernel(const DecParams prm) {
     typedef Bf16Path<D, kDecThreads> P;
-    constexpr int BN = P::BN, MB = P::MB, DB = P::DB;
-    __shared__ __attribute__((aligned(1024))) char kb0[P::TILE_BYTES];
-    __shared__ __attribute__((aligned(1024))) char kb1[P::TILE_BYTES];
-    __shared__ __attribute__((aligned(1024))) char vb0[P::TILE_BYTES];
-    __shared__ __attribute__((aligned(1024))) char vb1[P::TILE_BYTES];
+    constexpr int BN = P::BN, MB = P::MB, DB = P::DB, TB = P::TILE_BYTES;
+    constexpr int NB = KS2 ? 1 : MB;   // 32-key blocks a wave takes per tile
+    // Pipeline stages, each one K tile and one V tile: 5 (d=128) or 8
+    // (d=64). Every stage is an LDS variable of its own and the loop below
+    // names stages by constants, so the compiler can tell that a read of one
+    // stage does not alias the copies in flight to the others (it would
+    // otherwise wait for every copy before each LDS read).
+    constexpr int NS = kDecLds / (2 * TB) < 8 ? kDecLds / (2 * TB) : 8;
+    constexpr int LPT = 2 * P::SPW;          // copies per wave per tile (K and V)
+    static_assert((NS - 2) * LPT < 64, "in-flight copies must fit the vmcnt counter");
+    __shared__ __attribute__((aligned(1024))) char st0[2 * TB];
+    __shared__ __attribute__((aligned(1024))) char st1[2 * TB];
+    __shared__ __attribute__((aligned(1024))) char st2[2 * TB];
+    __shared__ __attribute__((aligned(1024))) char st3[2 * TB];
+    __shared__ __attribute__((aligned(1024))) char st4[2 * TB];
+    __shared__ __attribute__((aligned(1024))) char st5[2 * TB];
+    __shared__ __attribute__((aligned(1024))) char st6[2 * TB];
+    __shared__ __attribute__((aligned(1024))) char st7[2 * TB];
+    auto stage = [&](auto I) __attribute__((always_inline)) -> char * {
+        constexpr int i = decltype(I)::value % NS;
+        if constexpr (i == 0) return st0;
+        else if constexpr (i == 1) return st1;
+        else if constexpr (i == 2) return st2;
+        else if constexpr (i == 3) return st3;
+        else if constexpr (i == 4) return st4;
+        else if constexpr (i == 5) return st5;
+        else if constexpr (i == 6) return st6;
+        else return st7;
+    };
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int ln = lane & 31, h = lane >> 5;
@@ -58,33 +117,46 @@ __global__ void __launch_bounds__(kDecThreads) decode_kernel(const DecParams prm
     L = L < Nq ? Nq : L;
     if (!prm.rolling && L > S) L = S;
 
-    // this lane's query row
-    const int r = rg * kDecRows + wave * 32 + ln;
+    // this lane's query row (rows past R compute nothing and store nothing)
+    const int rw = KS2 ? wave >> 1 : wave;   // which 32 rows
+    const int kb = KS2 ? wave & 1 : 0;       // first key block taken
+    const int r = rg * kDecRows + rw * 32 + ln;
     const bool valid = r < prm.R;
+    const bool active = rg * kDecRows + rw * 32 < prm.R;   // wave-uniform
     const int hq = kvh * prm.group + (valid ? r / Nq : 0);
     const int t = valid ? r % Nq : 0;
     const int pos = L - Nq + t;
+    const int lo = prm.win < 0 ? 0 : imax(0, pos - prm.win);   // oldest visible position
     const long long grow = ((long long)b * prm.H + hq) * Nq + t;   // row of out / lse
     const uint16_t *qrow = static_cast<const uint16_t *>(prm.q) + grow * D;
-    // the waves whose 32 rows are all past the last query row still share
-    // the tile copies and barriers but skip the arithmetic
-    const bool active = rg * kDecRows + wave * 32 < prm.R;
-    // slots >= min(S, L) hold no position of this sequence (a cache that
-    // is not yet full may hold anything there, NaN included): the copies
-    // treat them as past the end of the buffer, which reads zeros
+    // slots >= min(S, L) hold no position of this sequence (a cache that is
+    // not yet full may hold anything there, NaN included): the copies treat
+    // them as past the end of the buffer, which reads zeros
     const int Nb = imin(S, L);
     const uint16_t *kh = static_cast<const uint16_t *>(prm.kc) + (long long)bkv * S * D;
     const uint16_t *vh = static_cast<const uint16_t *>(prm.vc) + (long long)bkv * S * D;
 
-    // slots this chunk must visit: a contiguous cache holds positions
-    // 0..L-1 in slots 0..L-1, of which the rows see at most the last
-    // Nq + win; a rolling cache may hold a visible position in any slot
-    int s_lo = 0, s_hi = prm.rolling ? imin(S, L) - 1 : L - 1;
-    if (!prm.rolling && prm.win >= 0) s_lo = imax(0, L - Nq - prm.win);
-    const int c0 = c * prm.chunk_tiles * BN;
-    s_lo = imax(s_lo, c0);
-    s_hi = imin(s_hi, imin(S - 1, c0 + prm.chunk_tiles * BN - 1));
-    const int t_lo = s_lo / BN, t_hi = s_hi >= s_lo ? s_hi / BN : t_lo - 1;
+    SlotMap map;
+    if (prm.rolling) {
+        map.sl = (L - 1) % S;
+        map.off = L - 1 - map.sl;
+    } else {
+        map.sl = INT_MAX;
+        map.off = 0;
+    }
+    map.S = S;
+    // every row of the workgroup sees positions [wlo, whi] at least
+    const int whi = L - Nq;
+    const int wlo = prm.win < 0 ? 0 : imax(0, L - 1 - prm.win);
+
+    // tiles this chunk visits: a contiguous cache holds positions 0..L-1
+    // in slots 0..L-1, of which the rows see at most the last Nq + win; a
+    // rolling cache may hold a visible position in any of its min(S, L)
+    // filled slots. The chunks split this sequence's tiles evenly.
+    const int s_lo = (!prm.rolling && prm.win >= 0) ? imax(0, L - Nq - prm.win) : 0;
+    const int f_lo = s_lo / BN, f_n = (Nb - 1) / BN - f_lo + 1;
+    const int per = (f_n + prm.chunks - 1) / prm.chunks;
+    const int t_lo = f_lo + c * per, t_hi = imin(f_lo + f_n, t_lo + per) - 1;
 
     typename P::Lane Ln;
     P::init_lane(Ln, lane, wave);
@@ -97,64 +169,132 @@ __global__ void __launch_bounds__(kDecThreads) decode_kernel(const DecParams prm
 #pragma unroll
     for (int db = 0; db < DB; ++db) o[db] = f32x16{};
 
-    auto step = [&](int tile, const char *kr, const char *vr, char *kw, char *vw) __attribute__((always_inline)) {
-        if (tile < t_hi) {
-            P::issue_k(Ln, kh, Nb, kw, (tile + 1) * BN);
-            P::issue_v(Ln, vh, Nb, vw, (tile + 1) * BN);
-        }
-        if (active) {
-            f32x16 s[MB];
-            P::scores(s, qf, Ln, kr);
-            float mx = EEA_NEG_INF;
+    auto issue = [&](int tile, char *buf) __attribute__((always_inline)) {
+        P::issue_k(Ln, kh, Nb, buf, tile * BN);
+        P::issue_v(Ln, vh, Nb, buf + TB, tile * BN);
+    };
+
+    auto compute = [&](int tile, const char *kr, const char *vr) __attribute__((always_inline)) {
+        f32x16 s[NB];
+        if constexpr (KS2) {
+            s[0] = f32x16{};
 #pragma unroll
-            for (int mb = 0; mb < MB; ++mb)
+            for (int ks = 0; ks < P::KS; ++ks) {
+                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(kr + Ln.krd[ks] + kb * 32 * P::ROWB);
+                s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf.x[ks], s[0], 0, 0, 0);
+            }
+        } else {
+            P::scores(s, qf, Ln, kr);
+        }
+        // interior tile: one run of positions (no wrap inside), all of them
+        // seen by every row of the workgroup
+        const int s0 = tile * BN, p0 = map.pos(s0);
+        const bool interior = s0 + BN <= S && !(s0 <= map.sl && map.sl < s0 + BN - 1) && p0 >= wlo &&
+                              p0 + BN - 1 <= whi;
+        float mx = EEA_NEG_INF;
+        if (interior) {   // rows past R score zeros here: finite, never stored
+#pragma unroll
+            for (int mb = 0; mb < NB; ++mb)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[mb][e]);
+        } else {
+#pragma unroll
+            for (int mb = 0; mb < NB; ++mb)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
-                    const int slot = tile * BN + mb * 32 + acc_row(e, h);
-                    const int p = slot_position(slot, L, S, prm.rolling);
-                    const bool vis = valid & (p >= 0) & (p <= pos) & ((prm.win < 0) | (p >= pos - prm.win));
+                    const int slot = s0 + (kb + mb) * 32 + acc_row(e, h);
+                    const int p = map.pos(slot);
+                    const bool vis = valid & (slot < S) & (p >= lo) & (p <= pos);
                     s[mb][e] = vis ? s[mb][e] : EEA_NEG_INF;
                     mx = fmaxf(mx, s[mb][e]);
                 }
-            mx = max_across_halves(mx);
-            const float mnew = fmaxf(m, mx * cl2);
-            const float alpha = (mnew == EEA_NEG_INF) ? 1.f : fast_exp2(m - mnew);   // m = -inf gives 0
-            m = mnew;
-            const float mu = (m == EEA_NEG_INF) ? 0.f : m;
-            float sum = 0.f;
+        }
+        mx = max_across_halves(mx);
+        const float mnew = fmaxf(m, mx * cl2);
+        const float alpha = (mnew == EEA_NEG_INF) ? 1.f : fast_exp2(m - mnew);   // m = -inf gives 0
+        m = mnew;
+        const float mu = (m == EEA_NEG_INF) ? 0.f : m;
+        float sum = 0.f;
 #pragma unroll
-            for (int mb = 0; mb < MB; ++mb)
+        for (int mb = 0; mb < NB; ++mb)
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const float pw = fast_exp2(__builtin_fmaf(s[mb][e], cl2, -mu));
-                    s[mb][e] = pw;
-                    sum += pw;
-                }
-            lpart = lpart * alpha + sum;
+            for (int e = 0; e < 16; ++e) {
+                const float pw = fast_exp2(__builtin_fmaf(s[mb][e], cl2, -mu));
+                s[mb][e] = pw;
+                sum += pw;
+            }
+        lpart = lpart * alpha + sum;
 #pragma unroll
-            for (int db = 0; db < DB; ++db) o[db] *= alpha;
+        for (int db = 0; db < DB; ++db) o[db] *= alpha;
+        if constexpr (KS2) {   // the block's two 16-key steps of P V
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                f32x8 x = {s[0][8 * j + 0], s[0][8 * j + 1], s[0][8 * j + 2], s[0][8 * j + 3],
+                           s[0][8 * j + 4], s[0][8 * j + 5], s[0][8 * j + 6], s[0][8 * j + 7]};
+                const bf16x8 pj = __builtin_convertvector(x, bf16x8);
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+                    o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(P::v_operand(Ln, vr, db, 2 * kb + j), pj, o[db],
+                                                                    0, 0, 0);
+            }
+        } else {
             typename P::PFrag pf;
             P::pack_p(pf, s);
             P::pv(o, pf, Ln, vr);
         }
-        wait_vmem();
-        __syncthreads();
     };
 
-    if (t_lo <= t_hi) {
-        P::issue_k(Ln, kh, Nb, kb0, t_lo * BN);
-        P::issue_v(Ln, vh, Nb, vb0, t_lo * BN);
-        wait_vmem();
-        __syncthreads();
-        for (int tile = t_lo; tile <= t_hi; tile += 2) {
-            step(tile, kb0, vb0, kb1, vb1);
-            if (tile + 1 > t_hi) break;
-            step(tile + 1, kb1, vb1, kb0, vb0);
-        }
+    // NS-stage pipeline: tiles t_lo .. t_lo+NS-2 are in flight before the
+    // loop; each iteration waits for its tile, then refills the stage the
+    // previous iteration computed on (every wave has left it: barrier)
+    static_for<NS - 1>([&](auto I) __attribute__((always_inline)) {
+        if (t_lo + I <= t_hi) issue(t_lo + I, stage(I));
+    });
+    for (int tile0 = t_lo; tile0 <= t_hi; tile0 += NS) {
+        static_for<NS>([&](auto I) __attribute__((always_inline)) {
+            const int tile = tile0 + I;
+            if (tile <= t_hi) {
+                wait_tiles<LPT, NS - 2>(imin(NS - 2, t_hi - tile));
+                __syncthreads();
+                if (tile + NS - 1 <= t_hi)
+                    issue(tile + NS - 1, stage(std::integral_constant<int, I + NS - 1>{}));
+                if (active) compute(tile, stage(I), stage(I) + TB);
+            }
+        });
     }
 
-    const float l = sum_across_halves(lpart);
+    float l = sum_across_halves(lpart);
+    if constexpr (KS2) {   // fold the second key block's state into the first's
+        __syncthreads();   // every wave is done with the stages
+        float *xs = reinterpret_cast<float *>(rw == 0 ? st0 : st1);
+        constexpr int NO = DB * 16;
+        if (kb == 1 && active) {
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) xs[(db * 16 + e) * 64 + lane] = o[db][e];
+            xs[NO * 64 + lane] = m;
+            xs[(NO + 1) * 64 + lane] = l;
+        }
+        __syncthreads();
+        if (kb == 1 || !active) return;
+        const float m1 = xs[NO * 64 + lane], l1 = xs[(NO + 1) * 64 + lane];
+        const float M = fmaxf(m, m1);
+        const float a0 = m == EEA_NEG_INF ? 0.f : fast_exp2(m - M);
+        const float a1 = m1 == EEA_NEG_INF ? 0.f : fast_exp2(m1 - M);
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) o[db][e] = o[db][e] * a0 + xs[(db * 16 + e) * 64 + lane] * a1;
+        l = l * a0 + l1 * a1;
+        m = M;
+    }
     if (!valid) return;
+    if (prm.chunks == 1) {   // the only chunk: finish the row here
+        P::store_out(static_cast<uint16_t *>(prm.out) + grow * D, 0, o, l > 0.f ? 1.f / l : 0.f, h);
+        if (h == 0) prm.lse[grow] = l > 0.f ? (m + __log2f(l)) * kLn2 : EEA_NEG_INF;
+        return;
+    }
     float *dst = prm.part + (grow * prm.chunks + c) * (D + 2);
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -172,48 +312,78 @@ __global__ void __launch_bounds__(kDecThreads) decode_kernel(const DecParams prm
     }
 }
 
-// One wave per output row: combine the chunks' partials.
+// One wave per output row: weight each chunk's partial by exp2(m_c - M)
+// (M the largest m_c), sum, and divide by the weighted normalisers.
 template <int D>
 __global__ void __launch_bounds__(64) decode_merge(const DecParams prm) {
+    __shared__ float wsh[kDecMaxChunks];
+    const int lane = threadIdx.x;
     const long long grow = blockIdx.x;   // over B * H * Nq
-    const float *src = prm.part + grow * prm.chunks * (D + 2);
+    const int C = prm.chunks;
+    const float *src = prm.part + grow * C * (D + 2);
     float M = EEA_NEG_INF;
-    for (int ci = 0; ci < prm.chunks; ++ci) M = fmaxf(M, src[ci * (D + 2) + D]);
-    float Lsum = 0.f;
-    for (int ci = 0; ci < prm.chunks; ++ci) {
+    for (int ci = lane; ci < C; ci += 64) M = fmaxf(M, src[ci * (D + 2) + D]);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    float Ls = 0.f;
+    for (int ci = lane; ci < C; ci += 64) {
         const float mc = src[ci * (D + 2) + D];
-        if (mc != EEA_NEG_INF) Lsum += src[ci * (D + 2) + D + 1] * fast_exp2(mc - M);
+        const float w = mc == EEA_NEG_INF ? 0.f : fast_exp2(mc - M);
+        wsh[ci] = w;
+        Ls += w * src[ci * (D + 2) + D + 1];
     }
-    const float inv = Lsum > 0.f ? 1.f / Lsum : 0.f;
-    for (int dd = threadIdx.x; dd < D; dd += 64) {
-        float acc = 0.f;
-        for (int ci = 0; ci < prm.chunks; ++ci) {
-            const float mc = src[ci * (D + 2) + D];
-            if (mc != EEA_NEG_INF) acc += src[ci * (D + 2) + dd] * fast_exp2(mc - M);
-        }
-        static_cast<__bf16 *>(prm.out)[grow * D + dd] = (__bf16)(acc * inv);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) Ls += __shfl_xor(Ls, off);
+    __syncthreads();
+    const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
+    constexpr int PER = D / 64;
+    float acc[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) acc[j] = 0.f;
+#pragma unroll 4
+    for (int ci = 0; ci < C; ++ci) {
+        const float w = wsh[ci];
+#pragma unroll
+        for (int j = 0; j < PER; ++j) acc[j] += src[ci * (D + 2) + lane + 64 * j] * w;
     }
-    if (threadIdx.x == 0) prm.lse[grow] = Lsum > 0.f ? (M + __log2f(Lsum)) * kLn2 : EEA_NEG_INF;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) static_cast<__bf16 *>(prm.out)[grow * D + lane + 64 * j] = (__bf16)(acc[j] * inv);
+    if (lane == 0) prm.lse[grow] = Ls > 0.f ? (M + __log2f(Ls)) * kLn2 : EEA_NEG_INF;
 }
 
-int decode_chunks(int B, int H_kv, int nrg, int S, int *chunk_tiles) {
-    const int tiles = (S + 63) / 64;
+// Chunks per row group. Each CU runs one workgroup at a time, so the cost
+// of a split is (rounds of kDecCUs workgroups) x (tiles per chunk + a
+// pipeline fill of about kFillTiles tiles); take the cheapest split.
+int decode_chunks(int B, int H_kv, int nrg, int S, int Nq, int win, int rolling) {
+    constexpr int kFillTiles = 3;
+    long long tiles = (S + 63) / 64;
+    if (!rolling && win >= 0) {
+        const long long span = ((long long)Nq + win + 63) / 64 + 1;   // window slots, any alignment
+        tiles = tiles < span ? tiles : span;
+    }
     const long long units = (long long)B * H_kv * nrg;
-    long long target = (2048 + units - 1) / units;   // a few thousand workgroups
-    if (target < 1) target = 1;
-    if (target > tiles) target = tiles;
-    int ct = (int)((tiles + target - 1) / target);
-    if (ct < 1) ct = 1;
-    if (chunk_tiles) *chunk_tiles = ct;
-    return (tiles + ct - 1) / ct;
+    const long long cmax = tiles < kDecMaxChunks ? tiles : kDecMaxChunks;
+    long long best = 1, best_cost = -1;
+    for (long long c = 1; c <= cmax; ++c) {
+        const long long rounds = (units * c + kDecCUs - 1) / kDecCUs;
+        const long long cost = rounds * ((tiles + c - 1) / c + kFillTiles);
+        if (best_cost < 0 || cost < best_cost) {
+            best = c;
+            best_cost = cost;
+        }
+    }
+    return (int)best;
 }
 
 template <int D>
 static hipError_t launch_dec_impl(const DecParams &p, hipStream_t stream) {
     const long long grid = (long long)p.B * p.H_kv * p.nrg * p.chunks;
-    hipLaunchKernelGGL((decode_kernel<D>), dim3((unsigned)grid), dim3(kDecThreads), 0, stream, p);
+    if (p.R <= 64)
+        hipLaunchKernelGGL((decode_kernel<D, true>), dim3((unsigned)grid), dim3(kDecThreads), 0, stream, p);
+    else
+        hipLaunchKernelGGL((decode_kernel<D, false>), dim3((unsigned)grid), dim3(kDecThreads), 0, stream, p);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess || p.chunks == 1) return e;
     hipLaunchKernelGGL((decode_merge<D>), dim3((unsigned)((long long)p.B * p.H * p.Nq)), dim3(64), 0, stream, p);
     return hipGetLastError();
 }

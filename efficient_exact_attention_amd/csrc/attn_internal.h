@@ -78,14 +78,14 @@ struct DecParams {
     int rolling;            // 1: position p lives in slot p % S
     int R;                  // query rows per K/V head: group * Nq
     int nrg;                // row groups of kDecRows per K/V head
-    int chunks;             // key chunks per row group
-    int chunk_tiles;        // 64-slot tiles per chunk
+    int chunks;             // cache chunks per row group (each sequence's tiles split evenly)
     float scale_log2;
 };
 
-constexpr int kDecRows = 64;   // query rows per decode workgroup (two waves)
+constexpr int kDecRows = 128;        // query rows per decode workgroup (four waves)
+constexpr int kDecMaxChunks = 256;   // most chunks one row is split into
 hipError_t launch_decode(const DecParams &p, int d, hipStream_t stream);
-int decode_chunks(int B, int H_kv, int nrg, int S, int *chunk_tiles);
+int decode_chunks(int B, int H_kv, int nrg, int S, int Nq, int win, int rolling);
 int bwd_tile_q(int d);      // query rows per dQ workgroup
 int bwd_tile_k(int d);      // keys per dK/dV workgroup
 

@@ -242,10 +242,12 @@ int attn_decode(const void *q, const void *k_cache, const void *v_cache, const i
 
 /*
  * attn_decode_workspace_bytes - device scratch attn_decode needs for its
- * per-chunk partial results (B*H*Nq*chunks*(d+2)*4 bytes, chunks <= S/64);
- * 0 for invalid sizes.
+ * per-chunk partial results: B*H*Nq*chunks*(d+2)*4 bytes, where the cache
+ * is split into 1 <= chunks <= 256 parts; 0 when one chunk suffices (the
+ * partials are not used) and for invalid sizes.
  */
-size_t attn_decode_workspace_bytes(int B, int H, int H_kv, int Nq, int S, int d);
+size_t attn_decode_workspace_bytes(int B, int H, int H_kv, int Nq, int S, int d, int win_left,
+                                   int rolling);
 
 /*
  * attn_workspace_bytes - device scratch a call with these sizes needs for the

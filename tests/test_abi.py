@@ -409,10 +409,16 @@ def test_decode_validation(over, status, text):
 
 
 def test_decode_workspace_bytes():
-    for (B, H, Hkv, Nq, S, d) in [(1, 32, 8, 1, 32768, 128), (4, 8, 8, 4, 100, 64), (2, 64, 1, 1, 4096, 128)]:
-        n = ea.attn_decode_workspace_bytes(B, H, Hkv, Nq, S, d)
-        per_row = n // (B * H * Nq * (d + 2) * 4)
-        assert n == B * H * Nq * (d + 2) * 4 * per_row
-        assert 1 <= per_row <= max(1, (S + 63) // 64)      # one partial per key chunk
+    for (B, H, Hkv, Nq, S, d, wl, roll) in [(1, 32, 8, 1, 32768, 128, -1, 0), (4, 8, 8, 4, 1000, 64, -1, 0),
+                                            (2, 64, 1, 1, 4096, 128, -1, 0), (1, 8, 8, 1, 32768, 128, 4095, 0),
+                                            (1, 8, 2, 1, 4096, 128, 4095, 1)]:
+        n = ea.attn_decode_workspace_bytes(B, H, Hkv, Nq, S, d, wl, roll)
+        chunks = n // (B * H * Nq * (d + 2) * 4)
+        assert n == B * H * Nq * (d + 2) * 4 * chunks
+        assert 2 <= chunks <= min(256, (S + 63) // 64)      # one partial per chunk
+    # a window bounds the chunks of a contiguous cache by the window's tiles
+    assert ea.attn_decode_workspace_bytes(1, 8, 8, 1, 32768, 128, 127, 0) // (8 * 130 * 4) <= 4
+    # thousands of sequences: one chunk each, no partials
+    assert ea.attn_decode_workspace_bytes(512, 64, 8, 1, 4096, 128, 4095, 1) == 0
     assert ea.attn_decode_workspace_bytes(1, 6, 4, 1, 100, 128) == 0
     assert ea.attn_decode_workspace_bytes(1, 8, 8, 1, 100, 96) == 0
