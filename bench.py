@@ -46,12 +46,15 @@ def mask_name(w):
     return "causal" if w.causal else "full"
 
 
-def source_hash():
-    with open(KERNEL_SRC, "rb") as f:
+DECODE_SRC = os.path.join(ROOT, "efficient_exact_attention_amd", "csrc", "attn_decode.hip")
+
+
+def source_hash(path=KERNEL_SRC):
+    with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def traffic_for(config):
+def traffic_for(config, src=KERNEL_SRC):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if the
     kernel source has not changed since the counters were taken."""
     path = os.path.join(ROOT, "profiles", f"traffic_{config}.json")
@@ -59,9 +62,21 @@ def traffic_for(config):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("kernel_source_sha256") != source_hash():
+    if t.get("kernel_source_sha256") != source_hash(src):
         return None
     return t.get("hbm_bytes_per_launch")
+
+
+def calibration_copy(nbytes):
+    """One plain device copy of nbytes (the dispatch the HBM byte counters are
+    scaled by)."""
+    import torch
+    src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"[bench] calibration copy of {nbytes} bytes done", file=sys.stderr, flush=True)
 
 
 def blas_build():
@@ -238,13 +253,7 @@ def main():
           flush=True)
 
     if args.copy_bytes > 0:
-        src = torch.ones(args.copy_bytes, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        print(f"[bench] calibration copy of {args.copy_bytes} bytes done", file=sys.stderr, flush=True)
-        del src, dst
+        calibration_copy(args.copy_bytes)
 
     result = {
         "metric": METRIC,
@@ -375,6 +384,8 @@ def bench_decode(args):
     avg = sum(ms) / len(ms)
     gbs = nbytes / (avg * 1e-3) / 1e9
     steps_s = 1e3 / avg
+    if args.copy_bytes > 0:
+        calibration_copy(args.copy_bytes)
     print(json.dumps({"metric": "decode steps/s (one new token per sequence, all heads)",
                       "value": round(steps_s, 2), "unit": "steps/s", "n_gpus": 1, "steps": args.steps,
                       "warmup": args.warmup, "ms_per_step": round(t0.elapsed_time(t1) / args.steps, 4),
@@ -383,7 +394,8 @@ def bench_decode(args):
                       "config": {"workload": f"decode {w.desc}: B={w.B} H={w.H} H_kv={w.H_kv} Nq={w.Nq} "
                                              f"S={w.S} d={w.d}", "algorithmic_bytes_per_step": nbytes},
                       "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
-                                   "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}}),
+                                   "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                                   "traffic": traffic_for(w.name, DECODE_SRC)}}),
           flush=True)
     return 0
 

@@ -38,5 +38,40 @@ def build(verbose: bool = False, extra_flags=()) -> str:
     return LIB
 
 
+def kernel_resources(sources=None) -> dict:
+    """Per-kernel register and scratch use of the device code, read from the
+    code-object metadata of a device-only assembly build:
+    {kernel symbol: {"vgpr": n, "agpr": n, "vgpr_spill": n, "sgpr_spill": n,
+    "scratch_bytes": n, "lds_bytes": n}}."""
+    import re
+    import tempfile
+    from concurrent.futures import ThreadPoolExecutor
+    srcs = sources or [s for s in SOURCES if s.endswith(".hip")]
+
+    def one(src):
+        with tempfile.TemporaryDirectory() as tmp:
+            out = os.path.join(tmp, "k.s")
+            cmd = [HIPCC, *DEVICE_FLAGS, "--cuda-device-only", "-S", f"-I{INCLUDE}", f"-I{CSRC}",
+                   os.path.join(CSRC, src), "-o", out]
+            r = subprocess.run(cmd, capture_output=True, text=True)
+            if r.returncode != 0:
+                raise RuntimeError(f"hipcc -S {src} failed:\n{r.stderr[-2000:]}")
+            return open(out).read()
+
+    res = {}
+    with ThreadPoolExecutor(len(srcs)) as ex:
+        for text in ex.map(one, srcs):
+            for block in text.split("\n  - "):
+                kv = dict(re.findall(r"\.(\w+):\s+([^\n]+)", block))
+                if "name" in kv and "vgpr_count" in kv and "private_segment_fixed_size" in kv:
+                    res[kv["name"].strip()] = {
+                        "vgpr": int(kv["vgpr_count"]), "agpr": int(kv.get("agpr_count", 0)),
+                        "vgpr_spill": int(kv.get("vgpr_spill_count", 0)),
+                        "sgpr_spill": int(kv.get("sgpr_spill_count", 0)),
+                        "scratch_bytes": int(kv["private_segment_fixed_size"]),
+                        "lds_bytes": int(kv.get("group_segment_fixed_size", 0))}
+    return res
+
+
 if __name__ == "__main__":
     print(build(verbose=True))

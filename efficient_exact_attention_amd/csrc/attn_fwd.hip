@@ -623,9 +623,14 @@ __device__ __forceinline__ void raise_max(RowState<P> &rs, float mx, float c) {
     }
 }
 
-template <int D>
-__global__ void __launch_bounds__(512) fwd_band_bf16(const FwdParams prm) {
-    typedef Bf16Path<D, 512> P;
+// DIL: dilation is live; BLK: the block-sparse rule is live. Each is folded
+// to a constant where off, since at 512 threads (two waves per SIMD, 256
+// registers each) the kernel has almost no registers to spare; the
+// block-rule instance runs 256 threads (one wave per SIMD) for that reason.
+template <int D, bool DIL, bool BLK>
+__global__ void __launch_bounds__(BLK ? 256 : 512) fwd_band_bf16(const FwdParams prm) {
+    constexpr bool GEN = BLK;
+    typedef Bf16Path<D, BLK ? 256 : 512> P;
     typedef BandPipe<P> BP;
     constexpr int BN = P::BN, BM = 32 * P::NW, MB = P::MB;
 
@@ -650,7 +655,7 @@ __global__ void __launch_bounds__(512) fwd_band_bf16(const FwdParams prm) {
     const int G = gridDim.x;
     const int bid = blockIdx.x;
     const int Lw = prm.xcd_remap ? (bid & 7) * (G >> 3) + (bid >> 3) : bid;
-    const int dil = prm.dil;
+    const int dil = DIL ? prm.dil : 1;
     const int per_head = dil * prm.num_qt;
     const int bh = Lw / per_head;
     const int rcls = (Lw - bh * per_head) / prm.num_qt;
@@ -658,7 +663,7 @@ __global__ void __launch_bounds__(512) fwd_band_bf16(const FwdParams prm) {
     const int unit = prm.causal ? prm.num_qt - 1 - qi : qi;
     const int N = (prm.N - rcls + dil - 1) / dil;   // rows of this residue class
     if (unit * BM >= N) return;                      // whole workgroup: a shorter class
-    const Band band{N, prm.wl, prm.wr, prm.block, prm.cap};
+    const Band band{N, prm.wl, prm.wr, BLK ? prm.block : 0, BLK ? prm.cap : 0};
 
     if (tid < kMaxGlobal) s_gidx[tid] = tid < ng ? prm.gidx[tid] : -1;
 
@@ -726,7 +731,16 @@ __global__ void __launch_bounds__(512) fwd_band_bf16(const FwdParams prm) {
 
     // --- band tiles
     auto in_w = [&](int kt) { return kt >= w_lo && kt <= w_hi; };
-    auto is_edge = [&](int kt) { return classify(band, wr0, wr1, kt * BN, kt * BN + BN - 1) != TILE_FULL; };
+    // a tile of the wave's range needs the mask unless every key of it lies
+    // in every row's interval: [row_lo(last row), row_hi(first row)]. Under
+    // the block rule these bounds take divisions, so they are computed once
+    // (wave-uniform, scalar registers); the window form is cheap inline.
+    const int full_lo = GEN ? __builtin_amdgcn_readfirstlane(row_lo(band, wr1)) : 0;
+    const int full_hi = GEN ? __builtin_amdgcn_readfirstlane(row_hi(band, wr0)) : 0;
+    auto is_edge = [&](int kt) {
+        if constexpr (GEN) return !(kt * BN >= full_lo && kt * BN + BN - 1 <= full_hi);
+        else return classify(band, wr0, wr1, kt * BN, kt * BN + BN - 1) != TILE_FULL;
+    };
 
     P::issue_k(L, kh, N, kb0, kt_lo * BN, dil);
     P::issue_v(L, vh, N, vb0, kt_lo * BN, dil);
@@ -837,8 +851,12 @@ __global__ void __launch_bounds__(64) merge_kernel(const FwdParams prm) {
 // ---------------------------------------------------------------------------
 constexpr int kBandThreadsBf16 = 512;   // 8 waves, 256 query rows
 constexpr int kBandThreadsF32 = 256;    // 4 waves, 128 query rows
+constexpr int kBandThreadsBlock = 256;  // bf16 under the block rule: 4 waves, 128 query rows
 
 int tile_bm(int d, int f32) { (void)d; return 32 * ((f32 ? kBandThreadsF32 : kBandThreadsBf16) / 64); }
+int band_tile_bm(int d, int f32, int block) {
+    return (!f32 && block > 0) ? 32 * (kBandThreadsBlock / 64) : tile_bm(d, f32);
+}
 int tile_bn(int d, int f32) { (void)d; return f32 ? 32 : 64; }
 
 int global_chunks(int BH, int N, int d, int f32, int *chunk_tiles) {
@@ -861,8 +879,12 @@ static hipError_t launch_impl(const FwdParams &p0, hipStream_t stream) {
     p.xcd_remap = (grid % 8 == 0) ? 1 : 0;
     if constexpr (F32)
         hipLaunchKernelGGL((fwd_kernel<PB, MODE_BAND>), dim3(grid), dim3(PB::NT), 0, stream, p);
+    else if (p.block > 0)
+        hipLaunchKernelGGL((fwd_band_bf16<D, false, true>), dim3(grid), dim3(kBandThreadsBlock), 0, stream, p);
+    else if (p.dil > 1)
+        hipLaunchKernelGGL((fwd_band_bf16<D, true, false>), dim3(grid), dim3(PB::NT), 0, stream, p);
     else
-        hipLaunchKernelGGL((fwd_band_bf16<D>), dim3(grid), dim3(PB::NT), 0, stream, p);
+        hipLaunchKernelGGL((fwd_band_bf16<D, false, false>), dim3(grid), dim3(PB::NT), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.n_global == 0) return e;
     const int ggrid = p.BH * p.chunks;

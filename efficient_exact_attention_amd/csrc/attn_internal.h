@@ -91,6 +91,7 @@ int bwd_tile_k(int d);      // keys per dK/dV workgroup
 
 // Tile shapes chosen per (d, dtype).
 int tile_bm(int d, int f32);
+int band_tile_bm(int d, int f32, int block);   // query rows per band workgroup for this mask
 int tile_bn(int d, int f32);
 
 // Enqueue the band pass (every query tile), then, when n_global > 0, the
