@@ -411,13 +411,14 @@ int bwd_impl(const void *q, const void *k, const void *v, const void *out, const
     if (rc != ATTN_OK) return rc;
     if (d != 64 && d != 128) return fail(ATTN_ERR_UNSUPPORTED, "head size d=%d is not supported (64 or 128)", d);
     if (m.ng > 0) return fail(ATTN_ERR_UNSUPPORTED, "the backward pass does not support global tokens");
-    if (m.dil > 1) return fail(ATTN_ERR_UNSUPPORTED, "the backward pass does not support dilated masks");
     const eea::Band band = m.band;
 
     const long long BH = (long long)B * H;
     const int bq = eea::bwd_tile_q(d), bk = eea::bwd_tile_k(d);
-    const long long nqt = (N + (long long)bq - 1) / bq, nkt = (N + (long long)bk - 1) / bk;
-    if (BH > INT_MAX || BH * nqt > INT_MAX || (long long)B * H_kv * nkt > INT_MAX)
+    // tiles per residue class (the longest class: ceil(N / dil) rows)
+    const long long Nc = (N + (long long)m.dil - 1) / m.dil;
+    const long long nqt = (Nc + bq - 1) / bq, nkt = (Nc + bk - 1) / bk;
+    if (BH > INT_MAX || BH * m.dil * nqt > INT_MAX || (long long)B * H_kv * m.dil * nkt > INT_MAX)
         return fail(ATTN_ERR_INVALID_ARG, "B*H=%lld with N=%d exceeds the launch grid", BH, N);
     if ((long long)N * d * 2 > INT_MAX)
         return fail(ATTN_ERR_UNSUPPORTED, "one head's K of N=%d x d=%d elements exceeds 2 GiB", N, d);
@@ -479,6 +480,7 @@ int bwd_impl(const void *q, const void *k, const void *v, const void *out, const
     p.wr = band.wr;
     p.block = band.block;
     p.cap = band.cap;
+    p.dil = m.dil;
     p.causal = causal;
     p.num_qt = (int)nqt;
     p.num_kt = (int)nkt;

@@ -70,7 +70,9 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_delta(const BwdParams prm) {
 // ---------------------------------------------------------------------------
 // dK, dV: keys stationary, query tiles streamed.
 // ---------------------------------------------------------------------------
-template <int D>
+// DIL: a dilated mask, run as one band attention per residue class of rows
+// (the forward's decomposition); folded to 1 otherwise.
+template <int D, bool DIL>
 __global__ void __launch_bounds__(kBwdThreads) bwd_dkdv(const BwdParams prm) {
     typedef Bf16Path<D, kBwdThreads> P;
     constexpr int BQ = P::BN;               // query rows per streamed tile
@@ -92,20 +94,26 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_dkdv(const BwdParams prm) {
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int ln = lane & 31, h = lane >> 5;
-    const int N = prm.N;
-    const Band band{N, prm.wl, prm.wr, prm.block, prm.cap};
     const int H_kv = prm.H / prm.group;
 
+    // work item: (K/V head, residue class, key tile)
     const int G = gridDim.x, bid = blockIdx.x;
     const int Lw = prm.xcd_remap_k ? (bid & 7) * (G >> 3) + (bid >> 3) : bid;
-    const int bkv = Lw / prm.num_kt;
-    const int kt = Lw - bkv * prm.num_kt;
+    const int dil = DIL ? prm.dil : 1;
+    const int per_kv = dil * prm.num_kt;
+    const int bkv = Lw / per_kv;
+    const int rcls = (Lw - bkv * per_kv) / prm.num_kt;
+    const int kt = Lw - bkv * per_kv - rcls * prm.num_kt;
+    const int N = DIL ? (prm.N - rcls + dil - 1) / dil : prm.N;   // rows of this residue class
+    if (kt * BK >= N) return;                                      // whole workgroup: a shorter class
+    const Band band{N, prm.wl, prm.wr, prm.block, prm.cap};
     const int b = bkv / H_kv, kvh = bkv - b * H_kv;
-    const uint16_t *kh = static_cast<const uint16_t *>(prm.k) + (long long)bkv * prm.head_stride;
-    const uint16_t *vh = static_cast<const uint16_t *>(prm.v) + (long long)bkv * prm.head_stride;
+    const long long cls_off = (long long)rcls * D;   // first row of the class
+    const uint16_t *kh = static_cast<const uint16_t *>(prm.k) + (long long)bkv * prm.head_stride + cls_off;
+    const uint16_t *vh = static_cast<const uint16_t *>(prm.v) + (long long)bkv * prm.head_stride + cls_off;
 
     typename P::Lane L;
-    P::init_lane(L, lane, wave);
+    P::init_lane(L, lane, wave, dil);
 
     const int K0 = kt * BK;
     const int key = K0 + wave * 32 + ln;
@@ -121,8 +129,8 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_dkdv(const BwdParams prm) {
 
     // this wave's keys as the B operands of S = Q K^T and dP = dO V^T
     typename P::QFrag kf, vf;
-    P::load_q(kf, kh, key, kvalid, h);
-    P::load_q(vf, vh, key, kvalid, h);
+    P::load_q(kf, kh, key * dil, kvalid, h);
+    P::load_q(vf, vh, key * dil, kvalid, h);
 
     f32x16 dk[DB], dv[DB];
 #pragma unroll
@@ -134,12 +142,12 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_dkdv(const BwdParams prm) {
     auto issue = [&](int t, char *qk, char *qv, char *ok, char *ov) __attribute__((always_inline)) {
         const long long bh = head_of(t);
         const int q0 = tile_of(t) * BQ;
-        const uint16_t *qh = static_cast<const uint16_t *>(prm.q) + bh * prm.head_stride;
-        const uint16_t *gh = static_cast<const uint16_t *>(prm.dout) + bh * prm.head_stride;
-        P::issue_k(L, qh, N, qk, q0);
-        P::issue_v(L, qh, N, qv, q0);
-        P::issue_k(L, gh, N, ok, q0);
-        P::issue_v(L, gh, N, ov, q0);
+        const uint16_t *qh = static_cast<const uint16_t *>(prm.q) + bh * prm.head_stride + cls_off;
+        const uint16_t *gh = static_cast<const uint16_t *>(prm.dout) + bh * prm.head_stride + cls_off;
+        P::issue_k(L, qh, N, qk, q0, dil);
+        P::issue_v(L, qh, N, qv, q0, dil);
+        P::issue_k(L, gh, N, ok, q0, dil);
+        P::issue_v(L, gh, N, ov, q0, dil);
     };
     // per-row terms of tile t, loaded into registers now and stored to LDS later
     auto row_terms = [&](int t, float &l2, float &dl) __attribute__((always_inline)) {
@@ -149,8 +157,9 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_dkdv(const BwdParams prm) {
             const long long bh = head_of(t);
             const int i = tile_of(t) * BQ + tid;
             if (i < N) {
-                l2 = prm.lse[bh * N + i] * kLog2e;
-                dl = prm.delta[bh * N + i];
+                const long long gi = bh * prm.N + rcls + (long long)i * dil;   // row in the stored sequence
+                l2 = prm.lse[gi] * kLog2e;
+                dl = prm.delta[gi];
             }
         }
     };
@@ -221,16 +230,16 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_dkdv(const BwdParams prm) {
     }
 
     if (!kvalid) return;
-    uint16_t *dkh = static_cast<uint16_t *>(prm.dk) + (long long)bkv * prm.head_stride;
-    uint16_t *dvh = static_cast<uint16_t *>(prm.dv) + (long long)bkv * prm.head_stride;
-    P::store_out(dkh, key, dk, prm.scale, h);
-    P::store_out(dvh, key, dv, 1.f, h);
+    uint16_t *dkh = static_cast<uint16_t *>(prm.dk) + (long long)bkv * prm.head_stride + cls_off;
+    uint16_t *dvh = static_cast<uint16_t *>(prm.dv) + (long long)bkv * prm.head_stride + cls_off;
+    P::store_out(dkh, key * dil, dk, prm.scale, h);
+    P::store_out(dvh, key * dil, dv, 1.f, h);
 }
 
 // ---------------------------------------------------------------------------
 // dQ: query rows stationary, key tiles streamed.
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, bool DIL>
 __global__ void __launch_bounds__(kBwdThreads) bwd_dq(const BwdParams prm) {
     typedef Bf16Path<D, kBwdThreads> P;
     constexpr int BN = P::BN;                 // keys per streamed tile
@@ -246,22 +255,27 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_dq(const BwdParams prm) {
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int ln = lane & 31, h = lane >> 5;
-    const int N = prm.N;
-    const Band band{N, prm.wl, prm.wr, prm.block, prm.cap};
-
+    // work item: (query head, residue class, query tile)
     const int G = gridDim.x, bid = blockIdx.x;
     const int Lw = prm.xcd_remap_q ? (bid & 7) * (G >> 3) + (bid >> 3) : bid;
-    const int bh = Lw / prm.num_qt;
-    const int qi = Lw - bh * prm.num_qt;
+    const int dil = DIL ? prm.dil : 1;
+    const int per_head = dil * prm.num_qt;
+    const int bh = Lw / per_head;
+    const int rcls = (Lw - bh * per_head) / prm.num_qt;
+    const int qi = Lw - bh * per_head - rcls * prm.num_qt;
     const int unit = prm.causal ? prm.num_qt - 1 - qi : qi;
+    const int N = DIL ? (prm.N - rcls + dil - 1) / dil : prm.N;   // rows of this residue class
+    if (unit * BM >= N) return;                                    // whole workgroup: a shorter class
+    const Band band{N, prm.wl, prm.wr, prm.block, prm.cap};
+    const long long cls_off = (long long)rcls * D;
     const long long kvb = (long long)(bh / prm.H) * (prm.H / prm.group) + (bh % prm.H) / prm.group;
-    const uint16_t *qh = static_cast<const uint16_t *>(prm.q) + (long long)bh * prm.head_stride;
-    const uint16_t *gh = static_cast<const uint16_t *>(prm.dout) + (long long)bh * prm.head_stride;
-    const uint16_t *kh = static_cast<const uint16_t *>(prm.k) + kvb * prm.head_stride;
-    const uint16_t *vh = static_cast<const uint16_t *>(prm.v) + kvb * prm.head_stride;
+    const uint16_t *qh = static_cast<const uint16_t *>(prm.q) + (long long)bh * prm.head_stride + cls_off;
+    const uint16_t *gh = static_cast<const uint16_t *>(prm.dout) + (long long)bh * prm.head_stride + cls_off;
+    const uint16_t *kh = static_cast<const uint16_t *>(prm.k) + kvb * prm.head_stride + cls_off;
+    const uint16_t *vh = static_cast<const uint16_t *>(prm.v) + kvb * prm.head_stride + cls_off;
 
     typename P::Lane L;
-    P::init_lane(L, lane, wave);
+    P::init_lane(L, lane, wave, dil);
 
     const int q0 = unit * BM;
     const int row = q0 + wave * 32 + ln;
@@ -273,10 +287,11 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_dq(const BwdParams prm) {
     key_tile_range(band, q0, imin(N - 1, q0 + BM - 1), BN, &kt_lo, &kt_hi);
 
     typename P::QFrag qf, gf;   // this wave's Q and dO rows: B operands of S^T and dP^T
-    P::load_q(qf, qh, row, valid, h);
-    P::load_q(gf, gh, row, valid, h);
-    const float l2 = valid ? prm.lse[(long long)bh * N + row] * kLog2e : 0.f;
-    const float dl = valid ? prm.delta[(long long)bh * N + row] : 0.f;
+    P::load_q(qf, qh, row * dil, valid, h);
+    P::load_q(gf, gh, row * dil, valid, h);
+    const long long grow = (long long)bh * prm.N + rcls + (long long)row * dil;   // row in the stored sequence
+    const float l2 = valid ? prm.lse[grow] * kLog2e : 0.f;
+    const float dl = valid ? prm.delta[grow] : 0.f;
     const float c = prm.scale_log2;
 
     f32x16 dq[DB];
@@ -284,9 +299,9 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_dq(const BwdParams prm) {
     for (int db = 0; db < DB; ++db) dq[db] = f32x16{};
 
     auto issue = [&](int kt, char *kk, char *kv, char *vk) __attribute__((always_inline)) {
-        P::issue_k(L, kh, N, kk, kt * BN);
-        P::issue_v(L, kh, N, kv, kt * BN);
-        P::issue_k(L, vh, N, vk, kt * BN);
+        P::issue_k(L, kh, N, kk, kt * BN, dil);
+        P::issue_v(L, kh, N, kv, kt * BN, dil);
+        P::issue_k(L, vh, N, vk, kt * BN, dil);
     };
     auto step = [&](int kt, const char *kk, const char *kv, const char *vk, char *nkk, char *nkv, char *nvk)
         __attribute__((always_inline)) {
@@ -327,8 +342,8 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_dq(const BwdParams prm) {
         }
     }
     if (!valid) return;
-    uint16_t *dqh = static_cast<uint16_t *>(prm.dq) + (long long)bh * prm.head_stride;
-    P::store_out(dqh, row, dq, prm.scale, h);
+    uint16_t *dqh = static_cast<uint16_t *>(prm.dq) + (long long)bh * prm.head_stride + cls_off;
+    P::store_out(dqh, row * dil, dq, prm.scale, h);
 }
 
 int bwd_tile_q(int d) { (void)d; return 32 * (kBwdThreads / 64); }
@@ -341,14 +356,20 @@ static hipError_t launch_bwd_impl(const BwdParams &p0, hipStream_t stream) {
     hipLaunchKernelGGL((bwd_delta<D>), dim3((unsigned)((rows + 31) / 32)), dim3(kBwdThreads), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int kgrid = (p.BH / p.group) * p.num_kt;
+    const int kgrid = (p.BH / p.group) * p.dil * p.num_kt;
     p.xcd_remap_k = kgrid % 8 == 0;
-    hipLaunchKernelGGL((bwd_dkdv<D>), dim3(kgrid), dim3(kBwdThreads), 0, stream, p);
+    if (p.dil > 1)
+        hipLaunchKernelGGL((bwd_dkdv<D, true>), dim3(kgrid), dim3(kBwdThreads), 0, stream, p);
+    else
+        hipLaunchKernelGGL((bwd_dkdv<D, false>), dim3(kgrid), dim3(kBwdThreads), 0, stream, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int qgrid = p.BH * p.num_qt;
+    const int qgrid = p.BH * p.dil * p.num_qt;
     p.xcd_remap_q = qgrid % 8 == 0;
-    hipLaunchKernelGGL((bwd_dq<D>), dim3(qgrid), dim3(kBwdThreads), 0, stream, p);
+    if (p.dil > 1)
+        hipLaunchKernelGGL((bwd_dq<D, true>), dim3(qgrid), dim3(kBwdThreads), 0, stream, p);
+    else
+        hipLaunchKernelGGL((bwd_dq<D, false>), dim3(qgrid), dim3(kBwdThreads), 0, stream, p);
     return hipGetLastError();
 }
 

@@ -55,9 +55,10 @@ struct BwdParams {
     int N;
     int wl, wr;             // normalised band
     int block, cap;         // block-sparse rule (0: window rule)
+    int dil;                // dilation: rows r, r+dil, ... form one sequence (1: plain)
     int causal;
-    int num_qt;             // query tiles of the dQ pass
-    int num_kt;             // key tiles of the dK/dV pass
+    int num_qt;             // query tiles of the dQ pass (per residue class when dil > 1)
+    int num_kt;             // key tiles of the dK/dV pass (per residue class when dil > 1)
     int xcd_remap_q, xcd_remap_k;
     float scale;            // score scale
     float scale_log2;       // scale * log2(e)

@@ -207,9 +207,11 @@ def test_masked_null_mask():
     assert err.status == ea.ATTN_ERR_INVALID_ARG and "mask" in err.message
 
 
-def test_bwd_rejects_dilation():
-    err = _call_bwd_masked(dilation=2)
-    assert err.status == ea.ATTN_ERR_UNSUPPORTED and "dilated" in err.message
+def test_bwd_accepts_dilation():
+    """A dilated mask passes validation (the call then stops on the invalid
+    scale, before the device)."""
+    err = _call_bwd_masked(dilation=2, causal=1, scale=-1.0)
+    assert err.status == ea.ATTN_ERR_INVALID_ARG and "scale" in err.message
 
 
 def _call_bwd_masked(**m):

@@ -96,3 +96,35 @@ def test_block_bwd(m):
     torch.cuda.synchronize()
     check_bwd((q, k, v, do), grads, dict(causal=m.get("causal", 0), win_left=-1, win_right=-1, global_idx=(),
                                           block=m["block"]))
+
+
+@pytest.mark.parametrize("m", DIL, ids=str)
+@pytest.mark.parametrize("N,d,H,H_kv", [(700, 128, 4, 2), (333, 64, 2, 2), (3, 64, 2, 1)])
+def test_dilated_bwd(m, N, d, H, H_kv):
+    """Backward of a dilated mask: every residue class is a band attention
+    of its own (strided rows), GQA heads summed."""
+    import efficient_exact_attention_amd as ea
+    from test_bwd_gpu import check_bwd
+    B = 1
+    q, k, v = _inputs(B, H, H_kv, N, d, "bf16", 21 + N)
+    do = W.make_tensor(W.random_workload("pdo", B, H, N, d, seed=22 + N), 0)
+    qd, kd, vd, dod = (to_device(x, "bf16") for x in (q, k, v, do))
+    say(f"  launch dilated bwd: B={B} H={H} H_kv={H_kv} N={N} d={d} mask={m}")
+    out, lse = ea.fwd(qd, kd, vd, **m)
+    grads = ea.bwd(qd, kd, vd, out, dod, lse, **m)
+    torch.cuda.synchronize()
+    check_bwd((q, k, v, do), grads, dict(causal=m.get("causal", 0), win_left=m.get("win_left", -1),
+                                          win_right=m.get("win_right", -1), global_idx=(),
+                                          dilation=m["dilation"]))
+
+
+def test_dilation_one_bwd_is_the_window_bitwise():
+    import efficient_exact_attention_amd as ea
+    q, k, v, do = (to_device(x, "bf16") for x in (*_inputs(1, 4, 2, 900, 128, "bf16", 31),
+                                                   W.make_tensor(W.random_workload("pdo", 1, 4, 900, 128, seed=32), 0)))
+    out, lse = ea.fwd(q, k, v, causal=1, win_left=77)
+    g1 = ea.bwd(q, k, v, out, do, lse, causal=1, win_left=77)
+    g2 = ea.bwd(q, k, v, out, do, lse, causal=1, win_left=77, dilation=1)
+    torch.cuda.synchronize()
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
