@@ -85,7 +85,7 @@ def lib():
     L.attn_decode.restype = ci
     L.attn_decode_workspace_bytes.argtypes = [ci, ci, ci, ci, ci, ci, ci, ci]
     L.attn_decode_workspace_bytes.restype = ctypes.c_size_t
-    L.attn_bwd_workspace_bytes.argtypes = [ci, ci, ci, ci]
+    L.attn_bwd_workspace_bytes.argtypes = [ci, ci, ci, ci, ci, ci]
     L.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
     L.attn_workspace_bytes.argtypes = [ci, ci, ci, ci, ci]
     L.attn_workspace_bytes.restype = ctypes.c_size_t
@@ -198,8 +198,8 @@ def attn_decode_workspace_bytes(B, H, H_kv, Nq, S, d, win_left=-1, rolling=0) ->
     return int(lib().attn_decode_workspace_bytes(B, H, H_kv, Nq, S, d, win_left, int(bool(rolling))))
 
 
-def attn_bwd_workspace_bytes(B, H, N, d) -> int:
-    return int(lib().attn_bwd_workspace_bytes(B, H, N, d))
+def attn_bwd_workspace_bytes(B, H, N, d, *, H_kv=None, n_global=0) -> int:
+    return int(lib().attn_bwd_workspace_bytes(B, H, H if H_kv is None else H_kv, N, d, n_global))
 
 
 def attn_workspace_bytes(B, H, N, d, n_global) -> int:

@@ -388,9 +388,29 @@ int device_and_scratch(size_t need, void **buf, bool backward) {
     return ATTN_OK;
 }
 
-size_t bwd_workspace(long long BH, int N) {
-    const size_t raw = (size_t)BH * N * sizeof(float);
-    return (raw + 255) & ~(size_t)255;
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Backward workspace: the row terms rowsum(dO * O) [B*H][N], then, with
+// global tokens, the split passes' partials (dQ of the global rows per key
+// chunk, dK and dV of the global columns per row chunk).
+struct BwdLayout {
+    size_t delta = 0, part_q = 0, part_k = 0, total = 0;
+    int gchunks_q = 0, gct_q = 0, gchunks_k = 0, gct_k = 0;
+};
+
+BwdLayout bwd_layout(long long BH, long long BKV, int N, int d, int ng) {
+    BwdLayout w;
+    w.delta = 0;
+    w.total = align256((size_t)BH * N * sizeof(float));
+    if (ng > 0) {
+        eea::bwd_global_chunks((int)BH, N, &w.gchunks_q, &w.gct_q);
+        eea::bwd_global_chunks((int)BKV, N, &w.gchunks_k, &w.gct_k);
+        w.part_q = w.total;
+        w.total += align256((size_t)BH * ng * w.gchunks_q * d * sizeof(float));
+        w.part_k = w.total;
+        w.total += align256((size_t)BKV * ng * w.gchunks_k * 2 * d * sizeof(float));
+    }
+    return w;
 }
 
 int bwd_impl(const void *q, const void *k, const void *v, const void *out, const void *dout, const float *lse,
@@ -410,7 +430,6 @@ int bwd_impl(const void *q, const void *k, const void *v, const void *out, const
     int rc = resolve_mask(N, causal, win_left, win_right, block, dilation, global_idx, n_global, m);
     if (rc != ATTN_OK) return rc;
     if (d != 64 && d != 128) return fail(ATTN_ERR_UNSUPPORTED, "head size d=%d is not supported (64 or 128)", d);
-    if (m.ng > 0) return fail(ATTN_ERR_UNSUPPORTED, "the backward pass does not support global tokens");
     const eea::Band band = m.band;
 
     const long long BH = (long long)B * H;
@@ -445,7 +464,8 @@ int bwd_impl(const void *q, const void *k, const void *v, const void *out, const
     if (!(scale > 0.f) || !std::isfinite(scale))
         return fail(ATTN_ERR_INVALID_ARG, "scale must be positive and finite");
 
-    const size_t need = bwd_workspace(BH, N);
+    const BwdLayout lay = bwd_layout(BH, (long long)B * H_kv, N, d, m.ng);
+    const size_t need = lay.total;
     void *ws = nullptr;
     if (opts && opts->workspace) {
         if (opts->workspace_bytes < need)
@@ -486,11 +506,21 @@ int bwd_impl(const void *q, const void *k, const void *v, const void *out, const
     p.num_kt = (int)nkt;
     p.scale = scale;
     p.scale_log2 = scale * 1.4426950408889634f;
+    p.n_global = m.ng;
+    for (int t = 0; t < m.ng; ++t) p.gidx[t] = m.G[t];
+    p.gchunks_q = lay.gchunks_q;
+    p.gct_q = lay.gct_q;
+    p.gchunks_k = lay.gchunks_k;
+    p.gct_k = lay.gct_k;
 
     // ---- first HIP call
     rc = device_and_scratch(need, &ws, true);
     if (rc != ATTN_OK) return rc;
     p.delta = static_cast<float *>(ws);
+    if (m.ng > 0) {
+        p.part_q = reinterpret_cast<float *>(static_cast<char *>(ws) + lay.part_q);
+        p.part_k = reinterpret_cast<float *>(static_cast<char *>(ws) + lay.part_k);
+    }
     hipStream_t stream = opts ? static_cast<hipStream_t>(opts->stream) : nullptr;
     hipError_t e = eea::launch_backward(p, d, stream);
     if (e != hipSuccess) return fail(ATTN_ERR_DEVICE, "kernel launch: %s", hipGetErrorString(e));
@@ -621,10 +651,11 @@ int attn_bwd_masked(const void *q, const void *k, const void *v, const void *out
                     mask->win_right, mask->block, mask->dilation, mask->global_idx, mask->n_global, opts);
 }
 
-size_t attn_bwd_workspace_bytes(int B, int H, int N, int d) {
+size_t attn_bwd_workspace_bytes(int B, int H, int H_kv, int N, int d, int n_global) {
     if (B <= 0 || H <= 0 || N <= 0 || (d != 64 && d != 128)) return 0;
+    if (H_kv <= 0 || H % H_kv != 0 || n_global < 0 || n_global > eea::kMaxGlobal) return 0;
     if ((long long)B * H > INT_MAX) return 0;
-    return bwd_workspace((long long)B * H, N);
+    return bwd_layout((long long)B * H, (long long)B * H_kv, N, d, n_global).total;
 }
 
 int attn_fwd_ex(const void *q, const void *k, const void *v, void *out, float *lse, int B, int H, int N, int d,

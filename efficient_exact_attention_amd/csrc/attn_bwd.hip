@@ -23,8 +23,8 @@
 // forward pass, so each of them is one of the bf16 tile path's two operand
 // patterns (row reads with the K swizzle, transpose reads with the V
 // swizzle); a tile needed in both forms is copied into LDS in both layouts.
-// Only band masks (causal, sliding and symmetric windows) are handled;
-// the C ABI rejects global tokens for the backward pass.
+// Band masks (causal, windows, block-sparse), dilated masks (one band per
+// residue class of rows) and global tokens (below) are handled.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -68,16 +68,45 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_delta(const BwdParams prm) {
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV: keys stationary, query tiles streamed.
+// Global tokens. The visible pairs split into three disjoint sets:
+//   S1  key in the row's band (every row, every column): the band loops,
+//       unchanged;
+//   S2  a global column outside a non-global row's band (causal cut): in
+//       bwd_dq a gathered key tile of the global columns, in the dK/dV of the
+//       global columns a split pass over query rows (BWD_GSET of bwd_dkdv);
+//   S3  a global row's keys outside its band (causal cut): in bwd_dkdv a
+//       gathered query tile of the global rows, in the dQ of the global rows
+//       a split pass over keys (BWD_GSET of bwd_dq).
+// The split passes leave fp32 partials that merge kernels add to the band
+// kernels' outputs for those (at most 64) rows.
 // ---------------------------------------------------------------------------
-// DIL: a dilated mask, run as one band attention per residue class of rows
-// (the forward's decomposition); folded to 1 otherwise.
-template <int D, bool DIL>
+enum { BWD_BAND = 0, BWD_BAND_GL = 1, BWD_GSET = 2 };
+
+// Bit r set when row q0 + r (r < 64) is a global position.
+__device__ __forceinline__ unsigned long long global_rows_in(const int *g, int ng, int q0) {
+    unsigned long long m = 0;
+    for (int t = 0; t < ng; ++t) {
+        const int r = g[t] - q0;
+        if (r >= 0 && r < 64) m |= 1ull << r;
+    }
+    return m;
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV: keys stationary, query tiles streamed.
+// BWD_BAND / BWD_BAND_GL: one workgroup per (K/V head, [residue class,] key
+//   tile); BWD_BAND_GL adds, per query head, the gathered tile of global rows
+//   (set S3).
+// BWD_GSET: the global columns as the keys (one workgroup per (K/V head,
+//   chunk of query tiles)), rows of set S2, fp32 partials out.
+// ---------------------------------------------------------------------------
+template <int D, bool DIL, int MODE>
 __global__ void __launch_bounds__(kBwdThreads) bwd_dkdv(const BwdParams prm) {
     typedef Bf16Path<D, kBwdThreads> P;
     constexpr int BQ = P::BN;               // query rows per streamed tile
     constexpr int BK = 32 * P::NW;          // keys per workgroup
     constexpr int MB = P::MB, DB = P::DB;
+    static_assert(!(DIL && MODE != BWD_BAND), "dilation is not combined with global tokens");
 
     // Q and dO of one query tile, each in both layouts, double-buffered; the
     // eight buffers are distinct objects and the loop is unrolled by two.
@@ -91,21 +120,33 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_dkdv(const BwdParams prm) {
     __shared__ __attribute__((aligned(1024))) char ov1[P::TILE_BYTES];
     __shared__ __attribute__((aligned(16))) float s_lse[2][BQ];   // LSE * log2(e)
     __shared__ __attribute__((aligned(16))) float s_dl[2][BQ];    // rowsum(dO * O)
+    __shared__ int s_g[kMaxGlobal];                               // sorted global positions
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int ln = lane & 31, h = lane >> 5;
     const int H_kv = prm.H / prm.group;
+    const int ng = MODE == BWD_BAND ? 0 : prm.n_global;
+    if constexpr (MODE != BWD_BAND) {
+        if (tid < kMaxGlobal) s_g[tid] = tid < ng ? prm.gidx[tid] : -1;
+        __syncthreads();
+    }
 
-    // work item: (K/V head, residue class, key tile)
+    // work item
     const int G = gridDim.x, bid = blockIdx.x;
     const int Lw = prm.xcd_remap_k ? (bid & 7) * (G >> 3) + (bid >> 3) : bid;
     const int dil = DIL ? prm.dil : 1;
-    const int per_kv = dil * prm.num_kt;
-    const int bkv = Lw / per_kv;
-    const int rcls = (Lw - bkv * per_kv) / prm.num_kt;
-    const int kt = Lw - bkv * per_kv - rcls * prm.num_kt;
+    int bkv, rcls = 0, kt = 0, chunk = 0;
+    if constexpr (MODE == BWD_GSET) {
+        bkv = Lw / prm.gchunks_k;
+        chunk = Lw - bkv * prm.gchunks_k;
+    } else {
+        const int per_kv = dil * prm.num_kt;
+        bkv = Lw / per_kv;
+        rcls = (Lw - bkv * per_kv) / prm.num_kt;
+        kt = Lw - bkv * per_kv - rcls * prm.num_kt;
+    }
     const int N = DIL ? (prm.N - rcls + dil - 1) / dil : prm.N;   // rows of this residue class
-    if (kt * BK >= N) return;                                      // whole workgroup: a shorter class
+    if (MODE != BWD_GSET && kt * BK >= N) return;                  // whole workgroup: a shorter class
     const Band band{N, prm.wl, prm.wr, prm.block, prm.cap};
     const int b = bkv / H_kv, kvh = bkv - b * H_kv;
     const long long cls_off = (long long)rcls * D;   // first row of the class
@@ -115,16 +156,37 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_dkdv(const BwdParams prm) {
     typename P::Lane L;
     P::init_lane(L, lane, wave, dil);
 
+    // this lane's key: a band key, or (BWD_GSET) a global column
     const int K0 = kt * BK;
-    const int key = K0 + wave * 32 + ln;
-    const bool kvalid = key < N;
-    const int k0w = K0 + wave * 32, k1w = imin(N - 1, k0w + 31);
-    const bool wave_active = k0w < N;
+    int key, k0w, k1w;
+    bool kvalid, wave_active;
+    if constexpr (MODE == BWD_GSET) {
+        const int r = wave * 32 + ln;
+        kvalid = r < ng;
+        key = kvalid ? s_g[r] : 0;
+        wave_active = wave * 32 < ng;
+        k0w = 0;
+        k1w = N - 1;
+    } else {
+        key = K0 + wave * 32 + ln;
+        kvalid = key < N;
+        k0w = K0 + wave * 32;
+        k1w = imin(N - 1, k0w + 31);
+        wave_active = k0w < N;
+    }
     // rows whose local interval holds this lane's key, and the query tiles
-    // of the workgroup's keys (both bounds never decrease with the key)
+    // this workgroup streams
     const int qlo = col_lo(band, key), qhi = col_hi(band, key);
-    const int glo = col_lo(band, K0), ghi = col_hi(band, imin(N - 1, K0 + BK - 1));
-    const int qt_lo = glo / BQ, nqt = ghi / BQ - qt_lo + 1;
+    int qt_lo, nqt;
+    if constexpr (MODE == BWD_GSET) {
+        const int ntot = (N + BQ - 1) / BQ;
+        qt_lo = chunk * prm.gct_k;
+        nqt = imax(0, imin(prm.gct_k, ntot - qt_lo));
+    } else {
+        const int glo = col_lo(band, K0), ghi = col_hi(band, imin(N - 1, K0 + BK - 1));
+        qt_lo = glo / BQ;
+        nqt = ghi / BQ - qt_lo + 1;
+    }
     const int T = prm.group * nqt;   // (query head, query tile) pairs
 
     // this wave's keys as the B operands of S = Q K^T and dP = dO V^T
@@ -164,6 +226,35 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_dkdv(const BwdParams prm) {
         }
     };
 
+    // the four products of one staged query tile; row(r) gives the sequence
+    // row of tile slot r (or -1), vis(i) the extra test of an edge tile
+    auto tile_products = [&](const char *qk, const char *qv, const char *ok, const char *ov, int sb, int cl,
+                             auto row, auto vis) __attribute__((always_inline)) {
+        f32x16 s[MB], dp[MB];
+        P::scores(s, kf, L, qk);    // S  = Q K^T : lane = key, registers = query rows
+        P::scores(dp, vf, L, ok);   // dP = dO V^T
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const f32x4 l4 = *reinterpret_cast<const f32x4 *>(&s_lse[sb][32 * mb + 8 * g + 4 * h]);
+                const f32x4 d4 = *reinterpret_cast<const f32x4 *>(&s_dl[sb][32 * mb + 8 * g + 4 * h]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 4 * g + e;
+                    float p = fast_exp2(__builtin_fmaf(s[mb][r], c, -l4[e]));
+                    if (cl == TILE_EDGE) p = vis(row(32 * mb + acc_row(r, h))) ? p : 0.f;
+                    s[mb][r] = p;
+                    dp[mb][r] = p * (dp[mb][r] - d4[e]);
+                }
+            }
+        typename P::PFrag pp, pd;
+        P::pack_p(pp, s);
+        P::pack_p(pd, dp);
+        P::pv(dv, pp, L, ov);   // dV^T += dO^T P
+        P::pv(dk, pd, L, qv);   // dK^T += Q^T dS
+    };
+
     auto step = [&](int t, const char *qk, const char *qv, const char *ok, const char *ov, char *nqk, char *nqv,
                     char *nok, char *nov, int sb) __attribute__((always_inline)) {
         const bool more = t + 1 < T;
@@ -174,35 +265,22 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_dkdv(const BwdParams prm) {
         }
         const int q0 = tile_of(t) * BQ;
         const int q1 = imin(N - 1, q0 + BQ - 1);
-        int cl = wave_active ? classify(band, q0, q1, k0w, k1w) : TILE_SKIP;
-        if (cl == TILE_FULL && q0 + BQ - 1 >= N) cl = TILE_EDGE;
-        if (cl != TILE_SKIP) {
-            f32x16 s[MB], dp[MB];
-            P::scores(s, kf, L, qk);    // S  = Q K^T : lane = key, registers = query rows
-            P::scores(dp, vf, L, ok);   // dP = dO V^T
-#pragma unroll
-            for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const f32x4 l4 = *reinterpret_cast<const f32x4 *>(&s_lse[sb][32 * mb + 8 * g + 4 * h]);
-                    const f32x4 d4 = *reinterpret_cast<const f32x4 *>(&s_dl[sb][32 * mb + 8 * g + 4 * h]);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int r = 4 * g + e;
-                        float p = fast_exp2(__builtin_fmaf(s[mb][r], c, -l4[e]));
-                        if (cl == TILE_EDGE) {
-                            const int i = q0 + 32 * mb + acc_row(r, h);
-                            p = ((i >= qlo) & (i <= qhi)) ? p : 0.f;
-                        }
-                        s[mb][r] = p;
-                        dp[mb][r] = p * (dp[mb][r] - d4[e]);
-                    }
-                }
-            typename P::PFrag pp, pd;
-            P::pack_p(pp, s);
-            P::pack_p(pd, dp);
-            P::pv(dv, pp, L, ov);   // dV^T += dO^T P
-            P::pv(dk, pd, L, qv);   // dK^T += Q^T dS
+        if constexpr (MODE == BWD_GSET) {
+            // set S2: rows outside the key's band, not global, causal cut
+            if (wave_active) {
+                const unsigned long long gm = global_rows_in(s_g, ng, q0);
+                tile_products(qk, qv, ok, ov, sb, TILE_EDGE, [&](int r) { return q0 + r; },
+                              [&](int i) {
+                                  return kvalid & (i < N) & ((i < qlo) | (i > qhi)) &
+                                         ((prm.causal == 0) | (i >= key)) & !((gm >> (i - q0)) & 1ull);
+                              });
+            }
+        } else {
+            int cl = wave_active ? classify(band, q0, q1, k0w, k1w) : TILE_SKIP;
+            if (cl == TILE_FULL && q0 + BQ - 1 >= N) cl = TILE_EDGE;
+            if (cl != TILE_SKIP)
+                tile_products(qk, qv, ok, ov, sb, cl, [&](int r) { return q0 + r; },
+                              [&](int i) { return (i >= qlo) & (i <= qhi); });
         }
         if (more && tid < BQ) {
             s_lse[sb ^ 1][tid] = nl2;
@@ -212,7 +290,7 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_dkdv(const BwdParams prm) {
         __syncthreads();
     };
 
-    {
+    if (T > 0) {
         issue(0, qk0, qv0, ok0, ov0);
         float l2, dl;
         row_terms(0, l2, dl);
@@ -229,7 +307,47 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_dkdv(const BwdParams prm) {
         step(t + 1, qk1, qv1, ok1, ov1, qk0, qv0, ok0, ov0, 1);
     }
 
+    if constexpr (MODE == BWD_BAND_GL) {
+        // set S3: per query head, the gathered tile of the global rows; a
+        // global row counts here for the keys outside its own band
+        for (int hq = 0; hq < prm.group; ++hq) {
+            const long long bh = (long long)b * prm.H + kvh * prm.group + hq;
+            const uint16_t *qh = static_cast<const uint16_t *>(prm.q) + bh * prm.head_stride;
+            const uint16_t *gh = static_cast<const uint16_t *>(prm.dout) + bh * prm.head_stride;
+            const TileSrc src{0, 1, N, ng, s_g};
+            typename P::Stage st;
+            P::issue(st, L, qh, qh, qk0, qv0, src, s_g[0]);
+            P::issue(st, L, gh, gh, ok0, ov0, src, s_g[0]);
+            if (tid < BQ) {
+                const bool gv = tid < ng;
+                s_lse[0][tid] = gv ? prm.lse[bh * N + s_g[tid]] * kLog2e : 0.f;
+                s_dl[0][tid] = gv ? prm.delta[bh * N + s_g[tid]] : 0.f;
+            }
+            wait_vmem();
+            __syncthreads();
+            if (wave_active)
+                tile_products(qk0, qv0, ok0, ov0, 0, TILE_EDGE, [&](int r) { return r < ng ? s_g[r] : -1; },
+                              [&](int i) {   // row i's band holds the key iff qlo <= i <= qhi
+                                  return kvalid & (i >= 0) & ((prm.causal == 0) | (key <= i)) &
+                                         ((i < qlo) | (i > qhi));
+                              });
+            __syncthreads();
+        }
+    }
+
     if (!kvalid) return;
+    if constexpr (MODE == BWD_GSET) {   // fp32 partials: [B*H_kv][ng][chunks][2 D] (dK^T unscaled, dV^T)
+        float *dst = prm.part_k + (((long long)bkv * ng + (wave * 32 + ln)) * prm.gchunks_k + chunk) * (2 * D);
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int d = db * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
+                dst[d] = dk[db][e];
+                dst[D + d] = dv[db][e];
+            }
+        return;
+    }
     uint16_t *dkh = static_cast<uint16_t *>(prm.dk) + (long long)bkv * prm.head_stride + cls_off;
     uint16_t *dvh = static_cast<uint16_t *>(prm.dv) + (long long)bkv * prm.head_stride + cls_off;
     P::store_out(dkh, key * dil, dk, prm.scale, h);
@@ -238,13 +356,18 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_dkdv(const BwdParams prm) {
 
 // ---------------------------------------------------------------------------
 // dQ: query rows stationary, key tiles streamed.
+// BWD_BAND / BWD_BAND_GL: one workgroup per (query head, [residue class,]
+//   query tile); BWD_BAND_GL adds the gathered tile of global columns (set S2).
+// BWD_GSET: the global rows as the query rows (one workgroup per (query head,
+//   chunk of key tiles)), keys of set S3, fp32 partials out.
 // ---------------------------------------------------------------------------
-template <int D, bool DIL>
+template <int D, bool DIL, int MODE>
 __global__ void __launch_bounds__(kBwdThreads) bwd_dq(const BwdParams prm) {
     typedef Bf16Path<D, kBwdThreads> P;
     constexpr int BN = P::BN;                 // keys per streamed tile
     constexpr int BM = 32 * P::NW;            // query rows per workgroup
     constexpr int MB = P::MB, DB = P::DB;
+    static_assert(!(DIL && MODE != BWD_BAND), "dilation is not combined with global tokens");
 
     __shared__ __attribute__((aligned(1024))) char kk0[P::TILE_BYTES];   // K, row-read layout
     __shared__ __attribute__((aligned(1024))) char kv0[P::TILE_BYTES];   // K, transpose-read layout
@@ -252,20 +375,33 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_dq(const BwdParams prm) {
     __shared__ __attribute__((aligned(1024))) char kk1[P::TILE_BYTES];
     __shared__ __attribute__((aligned(1024))) char kv1[P::TILE_BYTES];
     __shared__ __attribute__((aligned(1024))) char vk1[P::TILE_BYTES];
+    __shared__ int s_g[kMaxGlobal];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int ln = lane & 31, h = lane >> 5;
-    // work item: (query head, residue class, query tile)
+    const int ng = MODE == BWD_BAND ? 0 : prm.n_global;
+    if constexpr (MODE != BWD_BAND) {
+        if (tid < kMaxGlobal) s_g[tid] = tid < ng ? prm.gidx[tid] : -1;
+        __syncthreads();
+    }
+
+    // work item
     const int G = gridDim.x, bid = blockIdx.x;
     const int Lw = prm.xcd_remap_q ? (bid & 7) * (G >> 3) + (bid >> 3) : bid;
     const int dil = DIL ? prm.dil : 1;
-    const int per_head = dil * prm.num_qt;
-    const int bh = Lw / per_head;
-    const int rcls = (Lw - bh * per_head) / prm.num_qt;
-    const int qi = Lw - bh * per_head - rcls * prm.num_qt;
-    const int unit = prm.causal ? prm.num_qt - 1 - qi : qi;
+    int bh, rcls = 0, unit = 0, chunk = 0;
+    if constexpr (MODE == BWD_GSET) {
+        bh = Lw / prm.gchunks_q;
+        chunk = Lw - bh * prm.gchunks_q;
+    } else {
+        const int per_head = dil * prm.num_qt;
+        bh = Lw / per_head;
+        rcls = (Lw - bh * per_head) / prm.num_qt;
+        const int qi = Lw - bh * per_head - rcls * prm.num_qt;
+        unit = prm.causal ? prm.num_qt - 1 - qi : qi;
+    }
     const int N = DIL ? (prm.N - rcls + dil - 1) / dil : prm.N;   // rows of this residue class
-    if (unit * BM >= N) return;                                    // whole workgroup: a shorter class
+    if (MODE != BWD_GSET && unit * BM >= N) return;                // whole workgroup: a shorter class
     const Band band{N, prm.wl, prm.wr, prm.block, prm.cap};
     const long long cls_off = (long long)rcls * D;
     const long long kvb = (long long)(bh / prm.H) * (prm.H / prm.group) + (bh % prm.H) / prm.group;
@@ -277,14 +413,29 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_dq(const BwdParams prm) {
     typename P::Lane L;
     P::init_lane(L, lane, wave, dil);
 
+    // this lane's row: a band row, or (BWD_GSET) a global row
     const int q0 = unit * BM;
-    const int row = q0 + wave * 32 + ln;
-    const bool valid = row < N;
+    int row, wr0, wr1, kt_lo, kt_hi;
+    bool valid, wave_active;
+    if constexpr (MODE == BWD_GSET) {
+        const int r = wave * 32 + ln;
+        valid = r < ng;
+        row = valid ? s_g[r] : 0;
+        wave_active = wave * 32 < ng;
+        wr0 = 0;
+        wr1 = N - 1;
+        const int ntot = (N + BN - 1) / BN;
+        kt_lo = chunk * prm.gct_q;
+        kt_hi = imin(ntot, kt_lo + prm.gct_q) - 1;
+    } else {
+        row = q0 + wave * 32 + ln;
+        valid = row < N;
+        wr0 = q0 + wave * 32;
+        wr1 = imin(N - 1, wr0 + 31);
+        wave_active = wr0 < N;
+        key_tile_range(band, q0, imin(N - 1, q0 + BM - 1), BN, &kt_lo, &kt_hi);
+    }
     const int lo = row_lo(band, row), hi = row_hi(band, row);
-    const int wr0 = q0 + wave * 32, wr1 = imin(N - 1, wr0 + 31);
-    const bool wave_active = wr0 < N;
-    int kt_lo, kt_hi;
-    key_tile_range(band, q0, imin(N - 1, q0 + BM - 1), BN, &kt_lo, &kt_hi);
 
     typename P::QFrag qf, gf;   // this wave's Q and dO rows: B operands of S^T and dP^T
     P::load_q(qf, qh, row * dil, valid, h);
@@ -298,6 +449,26 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_dq(const BwdParams prm) {
 #pragma unroll
     for (int db = 0; db < DB; ++db) dq[db] = f32x16{};
 
+    // dS^T of one staged key tile into dQ^T; col(r) gives the key of tile
+    // slot r (or -1), vis(j) the extra test of an edge tile
+    auto tile_products = [&](const char *kk, const char *kv, const char *vk, int cl, auto col, auto vis)
+        __attribute__((always_inline)) {
+        f32x16 s[MB], dp[MB];
+        P::scores(s, qf, L, kk);    // S^T  = K Q^T  : lane = query row, registers = keys
+        P::scores(dp, gf, L, vk);   // dP^T = V dO^T
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float p = fast_exp2(__builtin_fmaf(s[mb][r], c, -l2));
+                if (cl == TILE_EDGE) p = vis(col(mb * 32 + acc_row(r, h))) ? p : 0.f;
+                dp[mb][r] = p * (dp[mb][r] - dl);
+            }
+        typename P::PFrag pd;
+        P::pack_p(pd, dp);
+        P::pv(dq, pd, L, kv);       // dQ^T += K^T dS^T
+    };
+
     auto issue = [&](int kt, char *kk, char *kv, char *vk) __attribute__((always_inline)) {
         P::issue_k(L, kh, N, kk, kt * BN, dil);
         P::issue_v(L, kh, N, kv, kt * BN, dil);
@@ -307,25 +478,17 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_dq(const BwdParams prm) {
         __attribute__((always_inline)) {
         if (kt < kt_hi) issue(kt + 1, nkk, nkv, nvk);
         const int k0 = kt * BN;
-        const int cl = wave_active ? classify(band, wr0, wr1, k0, k0 + BN - 1) : TILE_SKIP;
-        if (cl != TILE_SKIP) {
-            f32x16 s[MB], dp[MB];
-            P::scores(s, qf, L, kk);    // S^T  = K Q^T  : lane = query row, registers = keys
-            P::scores(dp, gf, L, vk);   // dP^T = V dO^T
-#pragma unroll
-            for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    float p = fast_exp2(__builtin_fmaf(s[mb][r], c, -l2));
-                    if (cl == TILE_EDGE) {
-                        const int j = k0 + mb * 32 + acc_row(r, h);
-                        p = ((j >= lo) & (j <= hi)) ? p : 0.f;
-                    }
-                    dp[mb][r] = p * (dp[mb][r] - dl);
-                }
-            typename P::PFrag pd;
-            P::pack_p(pd, dp);
-            P::pv(dq, pd, L, kv);       // dQ^T += K^T dS^T
+        if constexpr (MODE == BWD_GSET) {
+            // set S3: keys outside the global row's band, causal cut
+            if (wave_active)
+                tile_products(kk, kv, vk, TILE_EDGE, [&](int r) { return k0 + r; }, [&](int j) {
+                    return valid & (j < N) & ((j < lo) | (j > hi)) & ((prm.causal == 0) | (j <= row));
+                });
+        } else {
+            const int cl = wave_active ? classify(band, wr0, wr1, k0, k0 + BN - 1) : TILE_SKIP;
+            if (cl != TILE_SKIP)
+                tile_products(kk, kv, vk, cl, [&](int r) { return k0 + r; },
+                              [&](int j) { return (j >= lo) & (j <= hi); });
         }
         wait_vmem();
         __syncthreads();
@@ -341,13 +504,85 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_dq(const BwdParams prm) {
             step(kt + 1, kk1, kv1, vk1, kk0, kv0, vk0);
         }
     }
+
+    if constexpr (MODE == BWD_BAND_GL) {
+        // set S2: the gathered tile of the global columns; a global column
+        // counts here for non-global rows outside whose band it lies
+        bool row_is_g = false;
+        for (int t = 0; t < ng; ++t) row_is_g |= s_g[t] == row;
+        const TileSrc src{0, 1, N, ng, s_g};
+        typename P::Stage st;
+        P::issue(st, L, kh, kh, kk0, kv0, src, s_g[0]);
+        P::issue(st, L, vh, vh, vk0, kv1, src, s_g[0]);
+        wait_vmem();
+        __syncthreads();
+        if (wave_active)
+            tile_products(kk0, kv0, vk0, TILE_EDGE, [&](int r) { return r < ng ? s_g[r] : -1; }, [&](int j) {
+                return valid & !row_is_g & (j >= 0) & ((prm.causal == 0) | (j <= row)) & ((j < lo) | (j > hi));
+            });
+    }
+
     if (!valid) return;
+    if constexpr (MODE == BWD_GSET) {   // fp32 partials: [B*H][ng][chunks][D] (dQ^T unscaled)
+        float *dst = prm.part_q + (((long long)bh * ng + (wave * 32 + ln)) * prm.gchunks_q + chunk) * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) dst[db * 32 + 8 * (e >> 2) + 4 * h + (e & 3)] = dq[db][e];
+        return;
+    }
     uint16_t *dqh = static_cast<uint16_t *>(prm.dq) + (long long)bh * prm.head_stride + cls_off;
     P::store_out(dqh, row * dil, dq, prm.scale, h);
 }
 
+// Add the split passes' partials to the band kernels' outputs for the global
+// rows (dQ) and global columns (dK, dV): one workgroup of 64 lanes per row.
+template <int D>
+__global__ void __launch_bounds__(64) bwd_merge_dq(const BwdParams prm) {
+    const int ng = prm.n_global;
+    const long long bh = blockIdx.x / ng;
+    const int r = blockIdx.x - (int)(bh * ng);
+    const float *src = prm.part_q + ((long long)bh * ng + r) * prm.gchunks_q * D;
+    __bf16 *dst = static_cast<__bf16 *>(prm.dq) + bh * prm.head_stride + (long long)prm.gidx[r] * D;
+    for (int d = threadIdx.x; d < D; d += 64) {
+        float acc = 0.f;
+        for (int ci = 0; ci < prm.gchunks_q; ++ci) acc += src[ci * D + d];
+        dst[d] = (__bf16)((float)dst[d] + acc * prm.scale);
+    }
+}
+
+template <int D>
+__global__ void __launch_bounds__(64) bwd_merge_dkdv(const BwdParams prm) {
+    const int ng = prm.n_global;
+    const long long bkv = blockIdx.x / ng;
+    const int r = blockIdx.x - (int)(bkv * ng);
+    const float *src = prm.part_k + ((long long)bkv * ng + r) * prm.gchunks_k * (2 * D);
+    __bf16 *dk = static_cast<__bf16 *>(prm.dk) + bkv * prm.head_stride + (long long)prm.gidx[r] * D;
+    __bf16 *dv = static_cast<__bf16 *>(prm.dv) + bkv * prm.head_stride + (long long)prm.gidx[r] * D;
+    for (int d = threadIdx.x; d < D; d += 64) {
+        float ak = 0.f, av = 0.f;
+        for (int ci = 0; ci < prm.gchunks_k; ++ci) {
+            ak += src[ci * 2 * D + d];
+            av += src[ci * 2 * D + D + d];
+        }
+        dk[d] = (__bf16)((float)dk[d] + ak * prm.scale);
+        dv[d] = (__bf16)((float)dv[d] + av);
+    }
+}
+
 int bwd_tile_q(int d) { (void)d; return 32 * (kBwdThreads / 64); }
 int bwd_tile_k(int d) { (void)d; return 32 * (kBwdThreads / 64); }
+
+// Chunks of the split passes: a few hundred workgroups in all.
+void bwd_global_chunks(int units, int N, int *chunks, int *tiles_per_chunk) {
+    const int tiles = (N + 63) / 64;
+    int target = (512 + units - 1) / units;
+    if (target < 1) target = 1;
+    if (target > tiles) target = tiles;
+    const int ct = (tiles + target - 1) / target;
+    *tiles_per_chunk = ct;
+    *chunks = (tiles + ct - 1) / ct;
+}
 
 template <int D>
 static hipError_t launch_bwd_impl(const BwdParams &p0, hipStream_t stream) {
@@ -356,20 +591,42 @@ static hipError_t launch_bwd_impl(const BwdParams &p0, hipStream_t stream) {
     hipLaunchKernelGGL((bwd_delta<D>), dim3((unsigned)((rows + 31) / 32)), dim3(kBwdThreads), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int kgrid = (p.BH / p.group) * p.dil * p.num_kt;
+    const int BKV = p.BH / p.group;
+    const int kgrid = BKV * p.dil * p.num_kt;
     p.xcd_remap_k = kgrid % 8 == 0;
-    if (p.dil > 1)
-        hipLaunchKernelGGL((bwd_dkdv<D, true>), dim3(kgrid), dim3(kBwdThreads), 0, stream, p);
+    if (p.n_global > 0)
+        hipLaunchKernelGGL((bwd_dkdv<D, false, BWD_BAND_GL>), dim3(kgrid), dim3(kBwdThreads), 0, stream, p);
+    else if (p.dil > 1)
+        hipLaunchKernelGGL((bwd_dkdv<D, true, BWD_BAND>), dim3(kgrid), dim3(kBwdThreads), 0, stream, p);
     else
-        hipLaunchKernelGGL((bwd_dkdv<D, false>), dim3(kgrid), dim3(kBwdThreads), 0, stream, p);
+        hipLaunchKernelGGL((bwd_dkdv<D, false, BWD_BAND>), dim3(kgrid), dim3(kBwdThreads), 0, stream, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int qgrid = p.BH * p.dil * p.num_qt;
     p.xcd_remap_q = qgrid % 8 == 0;
-    if (p.dil > 1)
-        hipLaunchKernelGGL((bwd_dq<D, true>), dim3(qgrid), dim3(kBwdThreads), 0, stream, p);
+    if (p.n_global > 0)
+        hipLaunchKernelGGL((bwd_dq<D, false, BWD_BAND_GL>), dim3(qgrid), dim3(kBwdThreads), 0, stream, p);
+    else if (p.dil > 1)
+        hipLaunchKernelGGL((bwd_dq<D, true, BWD_BAND>), dim3(qgrid), dim3(kBwdThreads), 0, stream, p);
     else
-        hipLaunchKernelGGL((bwd_dq<D, false>), dim3(qgrid), dim3(kBwdThreads), 0, stream, p);
+        hipLaunchKernelGGL((bwd_dq<D, false, BWD_BAND>), dim3(qgrid), dim3(kBwdThreads), 0, stream, p);
+    e = hipGetLastError();
+    if (e != hipSuccess || p.n_global == 0) return e;
+    // split passes over the global rows and columns, then their merges
+    const int g1 = p.BH * p.gchunks_q;
+    p.xcd_remap_q = g1 % 8 == 0;
+    hipLaunchKernelGGL((bwd_dq<D, false, BWD_GSET>), dim3(g1), dim3(kBwdThreads), 0, stream, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int g2 = BKV * p.gchunks_k;
+    p.xcd_remap_k = g2 % 8 == 0;
+    hipLaunchKernelGGL((bwd_dkdv<D, false, BWD_GSET>), dim3(g2), dim3(kBwdThreads), 0, stream, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_merge_dq<D>), dim3(p.BH * p.n_global), dim3(64), 0, stream, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_merge_dkdv<D>), dim3(BKV * p.n_global), dim3(64), 0, stream, p);
     return hipGetLastError();
 }
 

@@ -62,9 +62,18 @@ struct BwdParams {
     int xcd_remap_q, xcd_remap_k;
     float scale;            // score scale
     float scale_log2;       // scale * log2(e)
+    // global tokens (n_global == 0: none)
+    int n_global;
+    int gchunks_q, gct_q;   // split pass over keys for the global rows: chunks, key tiles per chunk
+    int gchunks_k, gct_k;   // split pass over query rows for the global columns
+    float *part_q;          // workspace: [B*H][n_global][gchunks_q][d] fp32
+    float *part_k;          // workspace: [B*H_kv][n_global][gchunks_k][2d] fp32
+    int gidx[kMaxGlobal];   // sorted global positions
 };
 
 hipError_t launch_backward(const BwdParams &p, int d, hipStream_t stream);
+// Chunks of a split pass over N positions shared by `units` workgroup rows.
+void bwd_global_chunks(int units, int N, int *chunks, int *tiles_per_chunk);
 
 // Decode arguments: the newest Nq queries of each sequence against a cache.
 struct DecParams {

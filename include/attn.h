@@ -179,9 +179,9 @@ int attn_fwd_gqa(const void *q, const void *k, const void *v, void *out, float *
  *                 input or another output.
  *   B, H, H_kv, N, d, causal, win_left, win_right: as in attn_fwd_gqa, and
  *                 they must be the forward call's values.
- *   global_idx, n_global: global tokens are not supported by the backward
- *                 pass: n_global > 0 gives ATTN_ERR_UNSUPPORTED unless the
- *                 window already covers every visible key.
+ *   global_idx, n_global: global tokens, as in attn_fwd (host array, at
+ *                 most 64). Their pairs outside the band are handled by two
+ *                 split passes whose fp32 partials live in the workspace.
  *   opts          as in attn_fwd_ex: only ATTN_BF16 (ATTN_F32 gives
  *                 ATTN_ERR_UNSUPPORTED), scale (must be the forward's),
  *                 stream, and a workspace of at least attn_bwd_workspace_bytes
@@ -194,9 +194,9 @@ int attn_bwd(const void *q, const void *k, const void *v, const void *out, const
              const int *global_idx, int n_global, const attn_opts *opts);
 
 /*
- * attn_bwd_masked - attn_bwd with the mask given as an attn_mask: window and
- * block-sparse rules (dilated masks and global tokens give
- * ATTN_ERR_UNSUPPORTED).
+ * attn_bwd_masked - attn_bwd with the mask given as an attn_mask: window,
+ * block-sparse and dilated rules, global tokens (the combinations attn_fwd_masked
+ * accepts).
  */
 int attn_bwd_masked(const void *q, const void *k, const void *v, const void *out, const void *dout,
                     const float *lse, void *dq, void *dk, void *dv,
@@ -204,9 +204,11 @@ int attn_bwd_masked(const void *q, const void *k, const void *v, const void *out
 
 /*
  * attn_bwd_workspace_bytes - device scratch attn_bwd needs: one fp32 row term
- * per query row (B*H*N*4 bytes, rounded up to 256). 0 for invalid sizes.
+ * per query row (B*H*N*4 bytes, rounded up to 256), plus, when n_global > 0,
+ * the split passes' fp32 partials (O(n_global * d * N / 64) per head, never
+ * O(N^2)). 0 for invalid sizes.
  */
-size_t attn_bwd_workspace_bytes(int B, int H, int N, int d);
+size_t attn_bwd_workspace_bytes(int B, int H, int H_kv, int N, int d, int n_global);
 
 /*
  * attn_decode - one decoding step over a key/value cache: the Nq newest

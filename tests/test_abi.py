@@ -145,7 +145,8 @@ def _call_bwd(**over):
     (dict(H_kv=3), ea.ATTN_ERR_INVALID_ARG, "H_kv"),
     (dict(d=96), ea.ATTN_ERR_UNSUPPORTED, "head size"),
     (dict(dtype=ea.ATTN_F32), ea.ATTN_ERR_UNSUPPORTED, "bf16"),
-    (dict(global_idx=[0, 50], win_left=4, causal=0, win_right=4), ea.ATTN_ERR_UNSUPPORTED, "global"),
+    (dict(global_idx=[0, 50, 50], win_left=4, causal=0, win_right=4), ea.ATTN_ERR_INVALID_ARG, "twice"),
+    (dict(global_idx=list(range(65)), win_left=4), ea.ATTN_ERR_UNSUPPORTED, "maximum"),
     (dict(dq=FAKE + (1 << 32) + 64), ea.ATTN_ERR_INVALID_ARG, "overlaps an input"),
     (dict(dk=FAKE + (6 << 32) + 1024), ea.ATTN_ERR_INVALID_ARG, "overlap"),
     (dict(dk=FAKE + (7 << 32) + 8), ea.ATTN_ERR_INVALID_ARG, "aligned"),
@@ -157,6 +158,13 @@ def test_bwd_validation(over, status, text):
     err = _call_bwd(**over)
     assert err.status == status, err.message
     assert text in err.message, err.message
+
+
+def test_bwd_globals_are_accepted():
+    """Global tokens with a window pass validation (the call then stops on
+    the invalid scale, before the device)."""
+    err = _call_bwd(global_idx=[0, 50], win_left=4, causal=0, win_right=4, scale=-1.0)
+    assert err.status == ea.ATTN_ERR_INVALID_ARG and "scale" in err.message
 
 
 def test_bwd_globals_covered_by_window_are_accepted():
@@ -171,6 +179,12 @@ def test_bwd_workspace_bytes():
     assert ea.attn_bwd_workspace_bytes(2, 8, 1000, 128) == (2 * 8 * 1000 * 4 + 255) // 256 * 256
     assert ea.attn_bwd_workspace_bytes(0, 8, 1000, 128) == 0
     assert ea.attn_bwd_workspace_bytes(1, 1, 16, 96) == 0
+    # global tokens add the split passes' partials: O(n_global d N / 64) per head
+    base = ea.attn_bwd_workspace_bytes(2, 12, 16384, 64)
+    with_g = ea.attn_bwd_workspace_bytes(2, 12, 16384, 64, H_kv=4, n_global=9)
+    assert base < with_g < base + 2 * 12 * 9 * 64 * 4 * (16384 // 64) * 3
+    assert ea.attn_bwd_workspace_bytes(2, 12, 16384, 64, H_kv=5, n_global=9) == 0
+    assert ea.attn_bwd_workspace_bytes(2, 12, 16384, 64, n_global=65) == 0
 
 
 def _call_masked(mask=None, dtype=ea.ATTN_BF16, **m):
@@ -205,6 +219,11 @@ def test_masked_validation(m, status, text):
 def test_masked_null_mask():
     err = _call_masked(mask=False)
     assert err.status == ea.ATTN_ERR_INVALID_ARG and "mask" in err.message
+
+
+def test_bwd_rejects_dilation_with_globals():
+    err = _call_bwd_masked(dilation=2, global_idx=[0, 50])
+    assert err.status == ea.ATTN_ERR_UNSUPPORTED and "dilated" in err.message
 
 
 def test_bwd_accepts_dilation():

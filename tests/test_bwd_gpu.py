@@ -133,3 +133,54 @@ def test_bwd_workspace_and_stream():
     s.synchronize()
     for a, b in zip(g1, g2):
         assert torch.equal(a, b)
+
+
+# ---- global tokens ------------------------------------------------------------
+
+GMASKS = {
+    "band_g": dict(causal=0, win_left=20, win_right=20, global_idx=(0, 1, 100, 511, 700, 999)),
+    "swa_g": dict(causal=1, win_left=50, win_right=0, global_idx=(0, 3, 64, 500, 999)),
+    "diag_g63": dict(causal=0, win_left=0, win_right=0, global_idx=tuple(range(0, 1000, 16))),
+    "block_g": dict(causal=1, block=64, global_idx=(0, 130, 777)),
+    "left_only_g": dict(causal=0, win_left=7, win_right=0, global_idx=(5, 998)),
+}
+
+
+@pytest.mark.parametrize("mask", list(GMASKS))
+@pytest.mark.parametrize("N,d,H,H_kv", [(1000, 128, 4, 2), (1000, 64, 2, 2), (77, 64, 3, 1)])
+def test_bwd_globals(mask, N, d, H, H_kv):
+    """Global rows and columns: the band loops plus the gathered tiles and
+    the split passes over the global rows and columns."""
+    m = dict(GMASKS[mask])
+    m["global_idx"] = tuple(g for g in m["global_idx"] if g < N)
+    inputs, grads = run_bwd(1, H, H_kv, N, d, m, seed=N + d + H)
+    check_bwd(inputs, grads, dict(dict(win_left=-1, win_right=-1), **m))
+
+
+def test_bwd_globals_max_count():
+    m = dict(causal=1, win_left=30, win_right=0, global_idx=tuple(range(3, 3 + 64 * 37, 37)))
+    inputs, grads = run_bwd(1, 2, 1, 2500, 128, m, seed=41)
+    check_bwd(inputs, grads, m)
+
+
+def test_bwd_globals_band256_every_2048th():
+    """The non-causal band +-256 with global tokens {0, 1} and every 2048th
+    position, at N = 4096 (the oracle's fp64 backward is O(N^2) per head)."""
+    N = 4096
+    m = dict(causal=0, win_left=256, win_right=256, global_idx=W.every_2048th(N))
+    inputs, grads = run_bwd(2, 2, 2, N, 64, m, seed=42)
+    check_bwd(inputs, grads, m)
+
+
+def test_bwd_globals_deterministic_and_workspace():
+    import efficient_exact_attention_amd as ea
+    m = GMASKS["band_g"]
+    (q, k, v, do), g1 = run_bwd(1, 4, 2, 1000, 128, m, seed=43)
+    qd, kd, vd, dod = (to_device(x, "bf16") for x in (q, k, v, do))
+    out, lse = ea.fwd(qd, kd, vd, **m)
+    nbytes = ea.attn_bwd_workspace_bytes(1, 4, 1000, 128, H_kv=2, n_global=len(m["global_idx"]))
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    g2 = ea.bwd(qd, kd, vd, out, dod, lse, workspace=ws, **m)
+    torch.cuda.synchronize()
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
