@@ -24,13 +24,24 @@ What it computes (plain definition, no tiling, no fusion):
       "Sparse & sub-quadratic attention", section "Escape 1");
     - global tokens that see every position and are seen by every position
       (week-17 notes, global-token passage; "Efficient Transformers",
-      "Family 1"; "Sparse & sub-quadratic attention", "Escape 1").
+      "Family 1"; "Sparse & sub-quadratic attention", "Escape 1");
+    - log-spaced strides: row i also sees the positions at distance s, 2s,
+      4s, ... ("Module 9", table in "Sparse and windowed attention": the
+      strided / dilated family at strides s, 2s, 4s with O(n log n) cost);
+    - random blocks: row i also sees every key of the key blocks listed for
+      its query block (week-17 notes, BigBird passage: global tokens + local
+      window + random attention; "Efficient Transformers", "Family 1"). The
+      random draw is an input (the list), so the definition is deterministic.
   Readings used where the pages leave a choice open:
     - ``win_left``/``win_right`` count keys strictly left/right of the
       diagonal; -1 means unbounded on that side;
     - ``causal`` is combined with everything else by AND;
     - a pair is visible if it is in the window band OR its row is global OR
-      its column is global (each pair counted once);
+      its column is global OR (with a stride s) the distance |i - j| is s
+      times a power of two OR (with random blocks of size b) block j // b is
+      in the list of block i // b; each pair counted once. Random-list
+      entries outside the block range are ignored and repeated entries count
+      once;
     - LSE is the natural log of the sum over visible keys of exp(scaled
       score), one value per query row;
     - a row with no visible key (impossible under the argument rules, since
@@ -48,8 +59,19 @@ import math
 import numpy as np
 
 
+def _is_log_stride(dist: int, stride: int) -> bool:
+    """dist = stride * 2^m for some whole m >= 0 (scalar form)."""
+    if stride <= 0 or dist <= 0 or dist % stride:
+        return False
+    m = dist // stride
+    while m % 2 == 0:
+        m //= 2
+    return m == 1
+
+
 def visible(i: int, j: int, N: int, causal: int, win_left: int, win_right: int,
-            global_set, block: int = 0, dilation: int = 1) -> bool:
+            global_set, block: int = 0, dilation: int = 1, stride: int = 0,
+            rand_block: int = 0, rand_idx=None) -> bool:
     """Scalar visibility predicate: may query row i attend to key j?
 
     The local part of the mask is one of
@@ -61,8 +83,8 @@ def visible(i: int, j: int, N: int, causal: int, win_left: int, win_right: int,
       * dilated (dilation k > 1): j = i - m*k for whole m ("Week 17 lecture
         notes", dilated passage: i, i-k, i-2k, ...), with the window counted
         in dilated steps: -win_right <= m <= win_left.
-    Causal (j <= i) is ANDed with everything; global rows and columns are
-    ORed with the local part."""
+    Causal (j <= i) is ANDed with everything; global rows and columns, the
+    log-spaced strides and the random blocks are ORed with the local part."""
     if not (0 <= i < N and 0 <= j < N):
         return False
     if causal and j > i:
@@ -75,13 +97,19 @@ def visible(i: int, j: int, N: int, causal: int, win_left: int, win_right: int,
                  and (win_right < 0 or -diff <= win_right * dilation))
     else:
         local = (win_left < 0 or j >= i - win_left) and (win_right < 0 or j <= i + win_right)
-    return bool(local or (i in global_set) or (j in global_set))
+    strided = _is_log_stride(abs(i - j), stride)
+    rand = False
+    if rand_block > 0 and rand_idx is not None:
+        rand = (j // rand_block) in set(int(x) for x in rand_idx[i // rand_block])
+    return bool(local or (i in global_set) or (j in global_set) or strided or rand)
 
 
 def mask_rows(rows, N: int, causal: int, win_left: int, win_right: int,
-              global_idx=(), block: int = 0, dilation: int = 1) -> np.ndarray:
+              global_idx=(), block: int = 0, dilation: int = 1, stride: int = 0,
+              rand_block: int = 0, rand_idx=None) -> np.ndarray:
     """Boolean visibility matrix [len(rows), N]: the predicate of `visible`
-    evaluated for every (row, key) pair."""
+    evaluated for every (row, key) pair. rand_idx: [ceil(N / rand_block), r]
+    key-block lists, one row per query block."""
     i = np.asarray(rows, dtype=np.int64)[:, None]
     j = np.arange(N, dtype=np.int64)[None, :]
     if block > 0:
@@ -97,6 +125,16 @@ def mask_rows(rows, N: int, causal: int, win_left: int, win_right: int,
     if len(global_idx):
         is_global[np.asarray(global_idx, dtype=np.int64)] = True
     vis = band | is_global[i] | is_global[j]
+    if stride > 0:   # |i - j| in {s, 2s, 4s, ...}
+        dist = np.abs(i - j)
+        m = np.where(dist % stride == 0, dist // stride, 0)
+        vis = vis | ((m > 0) & ((m & (m - 1)) == 0))
+    if rand_block > 0 and rand_idx is not None:
+        lists = np.asarray(rand_idx, dtype=np.int64)
+        qb = (i[:, 0] // rand_block)
+        kb = j[0] // rand_block
+        for e in range(lists.shape[1]):
+            vis = vis | (kb[None, :] == lists[qb, e][:, None])
     if causal:
         vis &= j <= i
     return vis
@@ -104,7 +142,8 @@ def mask_rows(rows, N: int, causal: int, win_left: int, win_right: int,
 
 def attention(q, k, v, *, causal: int, win_left: int = -1, win_right: int = -1,
               global_idx=(), rows=None, scale: float | None = None,
-              row_block: int = 256, block: int = 0, dilation: int = 1):
+              row_block: int = 256, block: int = 0, dilation: int = 1, stride: int = 0,
+              rand_block: int = 0, rand_idx=None):
     """Masked softmax attention in fp64.
 
     q:       [B, H, N, d]; k, v: [B, H_kv, N, d] with H_kv dividing H (any
@@ -132,7 +171,8 @@ def attention(q, k, v, *, causal: int, win_left: int = -1, win_right: int = -1,
     lse = np.full((B, H, R), -np.inf, dtype=np.float64)
     for r0 in range(0, R, row_block):
         rb = rows[r0:r0 + row_block]
-        vis = mask_rows(rb, N, causal, win_left, win_right, global_idx, block, dilation)
+        vis = mask_rows(rb, N, causal, win_left, win_right, global_idx, block, dilation, stride,
+                        rand_block, rand_idx)
         any_vis = vis.any(axis=1)
         for b in range(B):
             for h in range(H):
@@ -151,7 +191,7 @@ def attention(q, k, v, *, causal: int, win_left: int = -1, win_right: int = -1,
 
 def probabilities(q, k, *, causal: int, win_left: int = -1, win_right: int = -1,
                   global_idx=(), rows=None, scale: float | None = None, block: int = 0,
-                  dilation: int = 1):
+                  dilation: int = 1, stride: int = 0, rand_block: int = 0, rand_idx=None):
     """Softmax weights [B, H, R, N] (fp64) of the same definition; used to
     check that visible weights sum to one and masked weights are zero."""
     q = np.asarray(q, dtype=np.float64)
@@ -160,7 +200,8 @@ def probabilities(q, k, *, causal: int, win_left: int = -1, win_right: int = -1,
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     rows = np.arange(N) if rows is None else np.asarray(rows, dtype=np.int64)
-    vis = mask_rows(rows, N, causal, win_left, win_right, global_idx, block, dilation)
+    vis = mask_rows(rows, N, causal, win_left, win_right, global_idx, block, dilation, stride,
+                    rand_block, rand_idx)
     s = np.einsum("bhrd,bhnd->bhrn", q[:, :, rows], k) * scale
     s = np.where(vis[None, None], s, -np.inf)
     m = s.max(axis=-1, keepdims=True)
@@ -215,12 +256,14 @@ def online_softmax_rows(q_rows, k, v, vis, block: int, scale: float | None = Non
 
 def visible_pairs_bruteforce(N: int, causal: int, win_left: int, win_right: int,
                              global_idx=(), row_block: int = 4096, block: int = 0,
-                             dilation: int = 1) -> int:
+                             dilation: int = 1, stride: int = 0, rand_block: int = 0,
+                             rand_idx=None) -> int:
     """Count of visible (i, j) pairs of one head by evaluating the mask."""
     total = 0
     for r0 in range(0, N, row_block):
         rows = np.arange(r0, min(N, r0 + row_block))
-        total += int(mask_rows(rows, N, causal, win_left, win_right, global_idx, block, dilation).sum())
+        total += int(mask_rows(rows, N, causal, win_left, win_right, global_idx, block, dilation, stride,
+                               rand_block, rand_idx).sum())
     return total
 
 

@@ -36,7 +36,8 @@ from .masked_attention import mask_rows
 
 
 def attention_backward(q, k, v, dout, *, causal: int, win_left: int = -1, win_right: int = -1,
-                       global_idx=(), scale: float | None = None, block: int = 0, dilation: int = 1):
+                       global_idx=(), scale: float | None = None, block: int = 0, dilation: int = 1,
+                       stride: int = 0, rand_block: int = 0, rand_idx=None):
     """(dQ [B, H, N, d], dK [B, H_kv, N, d], dV [B, H_kv, N, d]) in fp64 for
     O = attention(q, k, v) and upstream gradient dout [B, H, N, d]."""
     q = np.asarray(q, dtype=np.float64)
@@ -50,7 +51,8 @@ def attention_backward(q, k, v, dout, *, causal: int, win_left: int = -1, win_ri
     group = H // H_kv
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    vis = mask_rows(np.arange(N), N, causal, win_left, win_right, global_idx, block, dilation)
+    vis = mask_rows(np.arange(N), N, causal, win_left, win_right, global_idx, block, dilation, stride,
+                    rand_block, rand_idx)
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)

@@ -90,7 +90,7 @@ def test_mutant_is_caught(mutant):
     assert _fails(mutant), f"no pin caught {mutant.__name__}"
 
 
-def _mask_global_rows_only(rows, N, causal, win_left, win_right, global_idx=(), block=0, dilation=1):
+def _mask_global_rows_only(rows, N, causal, win_left, win_right, global_idx=(), block=0, dilation=1, *extra):
     """Mask with the global-column term dropped (globals see all, but are not seen)."""
     i = np.asarray(rows, dtype=np.int64)[:, None]
     j = np.arange(N, dtype=np.int64)[None, :]
@@ -108,7 +108,7 @@ def _mask_global_rows_only(rows, N, causal, win_left, win_right, global_idx=(), 
     return vis
 
 
-def _mask_strict_window(rows, N, causal, win_left, win_right, global_idx=(), block=0, dilation=1):
+def _mask_strict_window(rows, N, causal, win_left, win_right, global_idx=(), block=0, dilation=1, *extra):
     """Window bounds taken as strict (off by one on both sides)."""
     i = np.asarray(rows, dtype=np.int64)[:, None]
     j = np.arange(N, dtype=np.int64)[None, :]
