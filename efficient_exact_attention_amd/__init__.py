@@ -39,13 +39,18 @@ class _Opts(ctypes.Structure):
 class _Mask(ctypes.Structure):
     _fields_ = [("causal", ctypes.c_int), ("win_left", ctypes.c_int), ("win_right", ctypes.c_int),
                 ("block", ctypes.c_int), ("dilation", ctypes.c_int),
-                ("global_idx", ctypes.POINTER(ctypes.c_int)), ("n_global", ctypes.c_int)]
+                ("global_idx", ctypes.POINTER(ctypes.c_int)), ("n_global", ctypes.c_int),
+                ("stride", ctypes.c_int), ("rand_block", ctypes.c_int), ("n_rand", ctypes.c_int),
+                ("rand_idx", ctypes.c_void_p)]
 
 
-def _mask(causal, win_left, win_right, block, dilation, global_idx):
+def _mask(causal, win_left, win_right, block, dilation, global_idx, stride=0, rand_block=0, n_rand=0,
+          rand_idx=None):
+    """rand_idx: device address (int) of the int32 key-block lists, or None."""
     g, ng = _gidx(global_idx)
     m = _Mask(int(bool(causal)), int(win_left), int(win_right), int(block), int(dilation),
-              ctypes.cast(g, ctypes.POINTER(ctypes.c_int)) if g is not None else None, ng)
+              ctypes.cast(g, ctypes.POINTER(ctypes.c_int)) if g is not None else None, ng,
+              int(stride), int(rand_block), int(n_rand), rand_idx)
     m._keep = g   # the index array must outlive the call
     return m
 
@@ -159,27 +164,27 @@ def attn_bwd(q, k, v, out, dout, lse, dq, dk, dv, B, H, H_kv, N, d, causal, win_
 
 def attn_fwd_masked(q, k, v, out, lse, B, H, H_kv, N, d, *, causal=0, win_left=-1, win_right=-1, block=0,
                     dilation=1, global_idx=None, dtype=ATTN_BF16, scale=0.0, stream=None, workspace=None,
-                    workspace_bytes=0):
-    """Raw forward entry point with an attn_mask descriptor."""
-    m = _mask(causal, win_left, win_right, block, dilation, global_idx)
+                    workspace_bytes=0, stride=0, rand_block=0, n_rand=0, rand_idx=None):
+    """Raw forward entry point with an attn_mask descriptor (rand_idx: device address)."""
+    m = _mask(causal, win_left, win_right, block, dilation, global_idx, stride, rand_block, n_rand, rand_idx)
     opts = _Opts(dtype, float(scale), stream, workspace, workspace_bytes)
     _check(lib().attn_fwd_masked(q, k, v, out, lse, B, H, H_kv, N, d, ctypes.byref(m), ctypes.byref(opts)))
 
 
 def attn_bwd_masked(q, k, v, out, dout, lse, dq, dk, dv, B, H, H_kv, N, d, *, causal=0, win_left=-1,
                     win_right=-1, block=0, dilation=1, global_idx=None, dtype=ATTN_BF16, scale=0.0, stream=None,
-                    workspace=None, workspace_bytes=0):
+                    workspace=None, workspace_bytes=0, stride=0, rand_block=0, n_rand=0, rand_idx=None):
     """Raw backward entry point with an attn_mask descriptor."""
-    m = _mask(causal, win_left, win_right, block, dilation, global_idx)
+    m = _mask(causal, win_left, win_right, block, dilation, global_idx, stride, rand_block, n_rand, rand_idx)
     opts = _Opts(dtype, float(scale), stream, workspace, workspace_bytes)
     _check(lib().attn_bwd_masked(q, k, v, out, dout, lse, dq, dk, dv, B, H, H_kv, N, d, ctypes.byref(m),
                                  ctypes.byref(opts)))
 
 
 def attn_plan_stats_masked(N, bm, bn, *, causal=0, win_left=-1, win_right=-1, block=0, dilation=1,
-                           global_idx=None):
+                           global_idx=None, stride=0, rand_block=0, n_rand=0, rand_idx=None):
     """(visible_pairs, tiles_full, tiles_edge) of one head for an attn_mask."""
-    m = _mask(causal, win_left, win_right, block, dilation, global_idx)
+    m = _mask(causal, win_left, win_right, block, dilation, global_idx, stride, rand_block, n_rand, rand_idx)
     a, b, c = ctypes.c_longlong(), ctypes.c_longlong(), ctypes.c_longlong()
     _check(lib().attn_plan_stats_masked(N, ctypes.byref(m), bm, bn, ctypes.byref(a), ctypes.byref(b),
                                         ctypes.byref(c)))
@@ -222,10 +227,13 @@ def attn_tile_shape(d, dtype=ATTN_BF16):
 
 
 def fwd(q, k, v, *, causal=False, win_left=-1, win_right=-1, global_idx=None, scale=None,
-        out=None, lse=None, workspace=None, stream=None, block=0, dilation=1):
+        out=None, lse=None, workspace=None, stream=None, block=0, dilation=1, stride=0, rand_block=0,
+        rand_idx=None):
     """Attention forward on torch CUDA tensors: q [B, H, N, d], k and v
     [B, H_kv, N, d] with H_kv dividing H (H_kv = H: multi-head; H_kv < H:
-    grouped-query; H_kv = 1: multi-query), bf16 or fp32.
+    grouped-query; H_kv = 1: multi-query), bf16 or fp32. ``rand_idx`` (with
+    ``rand_block``) is a contiguous int32 device tensor [ceil(N / rand_block),
+    r] of key-block lists.
 
     Allocates ``out`` (input dtype) and ``lse`` (fp32 [B, H, N]) with torch
     unless given, enqueues the kernels on torch's current stream (or
@@ -259,12 +267,19 @@ def fwd(q, k, v, *, causal=False, win_left=-1, win_right=-1, global_idx=None, sc
         stream = stream.cuda_stream
     ws, wsb = (workspace.data_ptr(), workspace.numel() * workspace.element_size()) \
         if workspace is not None else (None, 0)
+    n_rand, rptr = 0, None
+    if rand_block:
+        if rand_idx is None or rand_idx.dtype != torch.int32 or not rand_idx.is_cuda or rand_idx.dim() != 2 \
+                or not rand_idx.is_contiguous() or rand_idx.shape[0] != (N + rand_block - 1) // rand_block:
+            raise ValueError("rand_idx must be a contiguous int32 device tensor [ceil(N / rand_block), r]")
+        n_rand, rptr = rand_idx.shape[1], rand_idx.data_ptr()
     attn_fwd_masked(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                     B, H, H_kv, N, d, causal=causal, win_left=win_left, win_right=win_right, block=block,
                     dilation=dilation, global_idx=global_idx,
                     dtype=ATTN_F32 if q.dtype == torch.float32 else ATTN_BF16,
                     scale=0.0 if scale is None else float(scale), stream=stream,
-                    workspace=ws, workspace_bytes=wsb)
+                    workspace=ws, workspace_bytes=wsb, stride=stride, rand_block=rand_block, n_rand=n_rand,
+                    rand_idx=rptr)
     return out, lse
 
 

@@ -119,7 +119,44 @@ struct MaskSpec {
     eea::Band band{};     // window or block rule; with dil > 1 the window counts steps
     std::vector<int> G;   // sorted global positions
     int ng = 0;           // globals in use (0 when the band already holds every visible key)
+    int stride = 0;       // log-spaced strided rule (0: off)
+    int rand_block = 0;   // random-block rule (0: off)
+    int n_rand = 0;
+    const int *rand_idx = nullptr;   // device key-block lists
+    bool extra() const { return stride > 0 || rand_block > 0; }
 };
+
+constexpr int kMaxRand = 16;   // key blocks listed per query block
+
+// The strided and random-block fields of an attn_mask, validated against the
+// already resolved local rule.
+int resolve_extras(int N, const attn_mask *mask, MaskSpec &m) {
+    if (!mask) return ATTN_OK;
+    if (mask->stride < 0) return fail(ATTN_ERR_INVALID_ARG, "stride=%d must be >= 0", mask->stride);
+    if (mask->rand_block < 0) return fail(ATTN_ERR_INVALID_ARG, "rand_block=%d must be >= 0", mask->rand_block);
+    if (mask->stride == 0 && mask->rand_block == 0) return ATTN_OK;
+    if (mask->stride > 0 && mask->rand_block > 0)
+        return fail(ATTN_ERR_UNSUPPORTED, "the strided and random-block rules cannot be combined");
+    if (m.band.block > 0 || m.dil > 1)
+        return fail(ATTN_ERR_UNSUPPORTED, "the strided and random-block rules combine with a window only");
+    if (mask->rand_block > 0) {
+        if (mask->rand_block % 32 != 0)
+            return fail(ATTN_ERR_UNSUPPORTED, "rand_block=%d must be a multiple of 32", mask->rand_block);
+        if (mask->n_rand < 1 || mask->n_rand > kMaxRand)
+            return fail(ATTN_ERR_INVALID_ARG, "n_rand=%d must be in [1, %d]", mask->n_rand, kMaxRand);
+        if (!mask->rand_idx) return fail(ATTN_ERR_INVALID_ARG, "rand_idx is NULL");
+        if ((uintptr_t)mask->rand_idx & 3) return fail(ATTN_ERR_INVALID_ARG, "rand_idx must be 4-byte aligned");
+    }
+    // a band that already holds every visible key leaves nothing to add
+    if (eea::band_is_everything(m.band, m.causal)) return ATTN_OK;
+    if (mask->stride > 0 && mask->stride < N) m.stride = mask->stride;
+    if (mask->rand_block > 0) {
+        m.rand_block = mask->rand_block;
+        m.n_rand = mask->n_rand;
+        m.rand_idx = mask->rand_idx;
+    }
+    return ATTN_OK;
+}
 
 int resolve_mask(int N, int causal, int win_left, int win_right, int block, int dilation, const int *global_idx,
                  int n_global, MaskSpec &m) {
@@ -167,6 +204,15 @@ int plan_impl(int N, const MaskSpec &m, int bm, int bn, long long *visible_pairs
             if (use_g)
                 for (int g : m.G)
                     if ((g < lo || g > hi) && (!causal || g <= i)) ++pairs;
+            if (m.stride > 0)   // positions at distance stride * 2^k outside the band, off the globals
+                for (long long o = m.stride; o < Nr; o *= 2)
+                    for (int sgn = -1; sgn <= 1; sgn += 2) {
+                        if (sgn > 0 && causal) continue;
+                        const long long j = i + sgn * o;
+                        if (j < 0 || j >= Nr || (j >= lo && j <= hi)) continue;
+                        if (use_g && is_g[j]) continue;
+                        ++pairs;
+                    }
         }
         const int nqt = (Nr + bm - 1) / bm;
         for (int qt = 0; qt < nqt; ++qt) {
@@ -179,6 +225,22 @@ int plan_impl(int N, const MaskSpec &m, int bm, int bn, long long *visible_pairs
                 else if (cl == eea::TILE_EDGE) ++edge;
             }
             if (use_g) edge += (m.ng + bn - 1) / bn;   // gathered tiles of global columns
+            if (m.stride > 0) {   // the strided rule's extra tiles, each visited once
+                long long next = 0;
+                auto visit = [&](long long klo, long long khi) {
+                    klo = std::max(klo, 0LL);
+                    khi = std::min(khi, (long long)Nr - 1);
+                    if (klo > khi) return;
+                    const long long t1 = khi / bn, t0 = std::max(klo / bn, next);
+                    if (t1 >= t0) edge += t1 - t0 + 1;
+                    next = std::max(next, t1 + 1);
+                };
+                std::vector<long long> offs;
+                for (long long o = m.stride; o < Nr; o *= 2) offs.push_back(o);
+                for (int a = (int)offs.size() - 1; a >= 0; --a) visit(r0 - offs[a], r1 - offs[a]);
+                if (!causal)
+                    for (long long o : offs) visit(r0 + o, r1 + o);
+            }
         }
     }
     if (use_g)
@@ -215,6 +277,10 @@ int attn_plan_stats_masked(int N, const attn_mask *mask, int bm, int bn, long lo
     int rc = resolve_mask(N, mask->causal, mask->win_left, mask->win_right, mask->block, mask->dilation,
                           mask->global_idx, mask->n_global, m);
     if (rc != ATTN_OK) return rc;
+    rc = resolve_extras(N, mask, m);
+    if (rc != ATTN_OK) return rc;
+    if (m.rand_block > 0)
+        return fail(ATTN_ERR_UNSUPPORTED, "plan statistics of the random-block rule need its device lists");
     return plan_impl(N, m, bm, bn, visible_pairs, tiles_full, tiles_edge);
 }
 
@@ -226,7 +292,7 @@ namespace {
 // multi-head attention).
 int fwd_impl(const void *q, const void *k, const void *v, void *out, float *lse, int B, int H, int H_kv, int N,
              int d, int causal, int win_left, int win_right, int block, int dilation, const int *global_idx,
-             int n_global, const attn_opts *opts) {
+             int n_global, const attn_opts *opts, const attn_mask *extras = nullptr) {
     g_err.clear();
     const int dtype = opts ? opts->dtype : ATTN_BF16;
     if (!q || !k || !v || !out || !lse) return fail(ATTN_ERR_INVALID_ARG, "a tensor pointer is NULL");
@@ -241,10 +307,14 @@ int fwd_impl(const void *q, const void *k, const void *v, void *out, float *lse,
     if (d != 64 && d != 128) return fail(ATTN_ERR_UNSUPPORTED, "head size d=%d is not supported (64 or 128)", d);
     if (m.dil > 1 && dtype == ATTN_F32)
         return fail(ATTN_ERR_UNSUPPORTED, "dilated masks are supported for bf16 tensors only");
+    rc = resolve_extras(N, extras, m);
+    if (rc != ATTN_OK) return rc;
+    if (m.extra() && dtype == ATTN_F32)
+        return fail(ATTN_ERR_UNSUPPORTED, "the strided and random-block rules are supported for bf16 tensors only");
     const std::vector<int> &G = m.G;
 
     const long long BH = (long long)B * H;
-    const int bm = eea::band_tile_bm(d, dtype == ATTN_F32, m.band.block);
+    const int bm = eea::band_tile_bm(d, dtype == ATTN_F32, m.band.block, m.extra());
     // query tiles per residue class (the longest class: ceil(N / dil) rows)
     const long long nqt = ((N + (long long)m.dil - 1) / m.dil + bm - 1) / bm;
     if (BH > INT_MAX || BH * m.dil * nqt > INT_MAX)
@@ -293,6 +363,10 @@ int fwd_impl(const void *q, const void *k, const void *v, void *out, float *lse,
     p.n_global = ng;
     p.num_qt = (int)nqt;
     p.scale_log2 = scale * 1.4426950408889634f;
+    p.stride = m.stride;
+    p.rand_block = m.rand_block;
+    p.n_rand = m.n_rand;
+    p.rand_idx = m.rand_idx;
     for (int t = 0; t < ng; ++t) p.gidx[t] = G[t];
 
     size_t need = 0;
@@ -647,6 +721,10 @@ int attn_bwd_masked(const void *q, const void *k, const void *v, const void *out
         g_err.clear();
         return fail(ATTN_ERR_INVALID_ARG, "mask is NULL");
     }
+    if (mask->stride != 0 || mask->rand_block != 0) {
+        g_err.clear();
+        return fail(ATTN_ERR_UNSUPPORTED, "the backward pass does not support the strided or random-block rules");
+    }
     return bwd_impl(q, k, v, out, dout, lse, dq, dk, dv, B, H, H_kv, N, d, mask->causal, mask->win_left,
                     mask->win_right, mask->block, mask->dilation, mask->global_idx, mask->n_global, opts);
 }
@@ -679,7 +757,7 @@ int attn_fwd_masked(const void *q, const void *k, const void *v, void *out, floa
         return fail(ATTN_ERR_INVALID_ARG, "mask is NULL");
     }
     return fwd_impl(q, k, v, out, lse, B, H, H_kv, N, d, mask->causal, mask->win_left, mask->win_right,
-                    mask->block, mask->dilation, mask->global_idx, mask->n_global, opts);
+                    mask->block, mask->dilation, mask->global_idx, mask->n_global, opts, mask);
 }
 
 int attn_fwd(const void *q, const void *k, const void *v, void *out, float *lse, int B, int H, int N, int d,

@@ -623,14 +623,16 @@ __device__ __forceinline__ void raise_max(RowState<P> &rs, float mx, float c) {
     }
 }
 
-// DIL: dilation is live; BLK: the block-sparse rule is live. Each is folded
-// to a constant where off, since at 512 threads (two waves per SIMD, 256
-// registers each) the kernel has almost no registers to spare; the
-// block-rule instance runs 256 threads (one wave per SIMD) for that reason.
-template <int D, bool DIL, bool BLK>
-__global__ void __launch_bounds__(BLK ? 256 : 512) fwd_band_bf16(const FwdParams prm) {
+// DIL: dilation is live; BLK: the block-sparse rule is live; XT: the extra
+// tiles of the log-spaced strided and random-block rules follow the band.
+// Each is folded to a constant where off, since at 512 threads (two waves
+// per SIMD, 256 registers each) the kernel has almost no registers to spare;
+// the block-rule and extra-tile instances run 256 threads (one wave per
+// SIMD) for that reason.
+template <int D, bool DIL, bool BLK, bool XT = false>
+__global__ void __launch_bounds__((BLK || XT) ? 256 : 512) fwd_band_bf16(const FwdParams prm) {
     constexpr bool GEN = BLK;
-    typedef Bf16Path<D, BLK ? 256 : 512> P;
+    typedef Bf16Path<D, (BLK || XT) ? 256 : 512> P;
     typedef BandPipe<P> BP;
     constexpr int BN = P::BN, BM = 32 * P::NW, MB = P::MB;
 
@@ -796,6 +798,85 @@ __global__ void __launch_bounds__(BLK ? 256 : 512) fwd_band_bf16(const FwdParams
         iter(j + 1, sb, sa, kb0, vb1, kb1, vb0);
     }
 
+    if constexpr (XT) {
+        // --- extra key tiles of the strided and random-block rules,
+        // unpipelined. A pair counts here only outside the row's band, off
+        // the global columns (the gathered tile has those) and within the
+        // causal limit; every tile is visited once per pattern entry.
+        const int q1 = imin(N - 1, q0 + BM - 1);
+        auto extra_tile = [&](int k0, bool take, auto vis) __attribute__((always_inline)) {
+            P::issue_k(L, kh, N, kb0, k0);
+            P::issue_v(L, vh, N, vb0, k0);
+            wait_vmem();
+            __syncthreads();
+            if (take) {
+                unsigned long long gm = 0;   // global columns of this tile
+                for (int t = 0; t < ng; ++t) {
+                    const int r = s_gidx[t] - k0;
+                    if (r >= 0 && r < BN) gm |= 1ull << r;
+                }
+                f32x16 s[MB];
+                P::scores(s, qf, L, kb0);
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int jr = mb * 32 + acc_row(r, h), j = k0 + jr;
+                        const bool ok = valid & (j < N) & ((j < lo) | (j > hi)) & ((prm.causal == 0) | (j <= row)) &
+                                        !((gm >> jr) & 1ull) && vis(j);
+                        s[mb][r] = ok ? s[mb][r] : EEA_NEG_INF;
+                    }
+                softmax_pv_step<P>(rs, s, c, L, vb0);
+            }
+            __syncthreads();
+        };
+        if (prm.stride > 0) {
+            // offsets o = stride * 2^m < N; the key ranges [q0 - o, q1 - o]
+            // (farthest first) then [q0 + o, q1 + o] (nearest first) come in
+            // increasing order, so a running bound visits each tile once
+            const int st = prm.stride;
+            int mtop = -1;
+            while (mtop < 30 && ((long long)st << (mtop + 1)) < N) ++mtop;
+            int next = 0;
+            auto strided = [&](int j) {
+                const int dist = j > row ? j - row : row - j;
+                if (dist == 0 || dist % st) return false;
+                const int m = dist / st;
+                return (m & (m - 1)) == 0;
+            };
+            auto visit = [&](int klo, int khi) __attribute__((always_inline)) {
+                klo = imax(klo, 0);
+                khi = imin(khi, N - 1);
+                if (klo > khi) return;
+                const int t1 = khi / BN;
+                for (int t = imax(klo / BN, next); t <= t1; ++t) extra_tile(t * BN, wave_active, strided);
+                next = imax(next, t1 + 1);
+            };
+            for (int m = mtop; m >= 0; --m) visit(q0 - (st << m), q1 - (st << m));
+            if (!prm.causal)
+                for (int m = 0; m <= mtop; ++m) visit(q0 + (st << m), q1 + (st << m));
+        }
+        if (prm.rand_block > 0) {
+            // each query block's listed key blocks (out-of-range entries
+            // skipped, repeats taken once); rows of one wave share a block
+            const int b = prm.rand_block, nr = prm.n_rand, nkb = (N + b - 1) / b;
+            const int my_qb = wr0 / b;
+            for (int qb = q0 / b; qb <= q1 / b; ++qb) {
+                const int *lst = prm.rand_idx + (long long)qb * nr;
+                for (int e = 0; e < nr; ++e) {
+                    const int kb = lst[e];
+                    bool skip = kb < 0 || kb >= nkb;
+                    for (int e2 = 0; e2 < e; ++e2) skip |= lst[e2] == kb;
+                    if (skip) continue;
+                    const int klo = kb * b, khi = imin(N - 1, klo + b - 1);
+                    if (prm.causal && klo > imin(q1, qb * b + b - 1)) continue;
+                    for (int t = klo / BN; t <= khi / BN; ++t)
+                        extra_tile(t * BN, wave_active && my_qb == qb, [&](int j) { return j >= klo && j <= khi; });
+                }
+            }
+        }
+    }
+
     // --- epilogue
     if (!valid) return;
     const int orow = rcls + row * dil;   // row index in the stored sequence
@@ -851,11 +932,11 @@ __global__ void __launch_bounds__(64) merge_kernel(const FwdParams prm) {
 // ---------------------------------------------------------------------------
 constexpr int kBandThreadsBf16 = 512;   // 8 waves, 256 query rows
 constexpr int kBandThreadsF32 = 256;    // 4 waves, 128 query rows
-constexpr int kBandThreadsBlock = 256;  // bf16 under the block rule: 4 waves, 128 query rows
+constexpr int kBandThreadsBlock = 256;  // bf16 with the block rule or extra tiles: 4 waves, 128 query rows
 
 int tile_bm(int d, int f32) { (void)d; return 32 * ((f32 ? kBandThreadsF32 : kBandThreadsBf16) / 64); }
-int band_tile_bm(int d, int f32, int block) {
-    return (!f32 && block > 0) ? 32 * (kBandThreadsBlock / 64) : tile_bm(d, f32);
+int band_tile_bm(int d, int f32, int block, int extra) {
+    return (!f32 && (block > 0 || extra)) ? 32 * (kBandThreadsBlock / 64) : tile_bm(d, f32);
 }
 int tile_bn(int d, int f32) { (void)d; return f32 ? 32 : 64; }
 
@@ -879,6 +960,8 @@ static hipError_t launch_impl(const FwdParams &p0, hipStream_t stream) {
     p.xcd_remap = (grid % 8 == 0) ? 1 : 0;
     if constexpr (F32)
         hipLaunchKernelGGL((fwd_kernel<PB, MODE_BAND>), dim3(grid), dim3(PB::NT), 0, stream, p);
+    else if (p.stride > 0 || p.rand_block > 0)
+        hipLaunchKernelGGL((fwd_band_bf16<D, false, false, true>), dim3(grid), dim3(kBandThreadsBlock), 0, stream, p);
     else if (p.block > 0)
         hipLaunchKernelGGL((fwd_band_bf16<D, false, true>), dim3(grid), dim3(kBandThreadsBlock), 0, stream, p);
     else if (p.dil > 1)

@@ -33,6 +33,10 @@ struct FwdParams {
     int chunk_tiles;      // key tiles per chunk
     int xcd_remap;        // 1: group consecutive work items on one XCD
     float scale_log2;     // score scale * log2(e)
+    int stride;           // > 0: also the positions at distance stride * 2^m
+    int rand_block;       // > 0: random-block rule, blocks of rand_block positions
+    int n_rand;           // key blocks listed per query block
+    const int *rand_idx;  // device [ceil(N / rand_block)][n_rand] key-block lists
     int gidx[kMaxGlobal]; // sorted global positions
 };
 
@@ -101,7 +105,7 @@ int bwd_tile_k(int d);      // keys per dK/dV workgroup
 
 // Tile shapes chosen per (d, dtype).
 int tile_bm(int d, int f32);
-int band_tile_bm(int d, int f32, int block);   // query rows per band workgroup for this mask
+int band_tile_bm(int d, int f32, int block, int extra);   // query rows per band workgroup for this mask
 int tile_bn(int d, int f32);
 
 // Enqueue the band pass (every query tile), then, when n_global > 0, the

@@ -116,7 +116,18 @@ int attn_fwd_ex(const void *q, const void *k, const void *v, void *out, float *l
  *       in those steps: -win_right <= m <= win_left. bf16 forward only, and
  *       not combined with global tokens.
  * causal (j <= i) is ANDed with the result, global tokens (rows that see
- * everything and columns seen by everyone) ORed with the local rule.
+ * everything and columns seen by everyone) ORed with the local rule, and so
+ * is at most one of two extra rules (window local rule only; bf16 forward
+ * only: the backward pass gives ATTN_ERR_UNSUPPORTED):
+ *   strided (stride = s > 0): j is at distance s, 2s, 4s, ... from i ("Module
+ *       9 - Quadratic cost and efficient attention", table in "Sparse and
+ *       windowed attention": strides s, 2s, 4s with O(n log n) cost);
+ *   random blocks (rand_block = b > 0): j lies in one of the key blocks listed
+ *       for i's query block, blocks being runs of b positions (week-17 lecture
+ *       notes, BigBird passage: global tokens + local window + random
+ *       attention). The caller draws the lists: rand_idx is read on the
+ *       device, row q of it lists the key blocks of query block q; entries
+ *       outside [0, ceil(N / b)) are ignored and repeated entries count once.
  */
 typedef struct attn_mask {
     int causal;             /* 0 or 1 */
@@ -126,6 +137,10 @@ typedef struct attn_mask {
     int dilation;           /* >= 0; 0 or 1 = no dilation */
     const int *global_idx;  /* host array of distinct positions in [0, N), or NULL */
     int n_global;           /* 0..64 */
+    int stride;             /* >= 0; > 0: also the positions at distance stride * 2^m */
+    int rand_block;         /* >= 0; > 0: random-block rule, blocks of rand_block positions (a multiple of 32) */
+    int n_rand;             /* key blocks listed per query block: 1..16 (with rand_block > 0) */
+    const int *rand_idx;    /* DEVICE int32 array [ceil(N / rand_block)][n_rand] of key-block indices */
 } attn_mask;
 
 /*

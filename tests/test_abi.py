@@ -443,3 +443,53 @@ def test_decode_workspace_bytes():
     assert ea.attn_decode_workspace_bytes(512, 64, 8, 1, 4096, 128, 4095, 1) == 0
     assert ea.attn_decode_workspace_bytes(1, 6, 4, 1, 100, 128) == 0
     assert ea.attn_decode_workspace_bytes(1, 8, 8, 1, 100, 96) == 0
+
+
+# ---- strided and random-block rules: validation and planning ---------------------
+
+@pytest.mark.parametrize("m,dtype,status,text", [
+    (dict(stride=-1), ea.ATTN_BF16, ea.ATTN_ERR_INVALID_ARG, "stride"),
+    (dict(rand_block=-1), ea.ATTN_BF16, ea.ATTN_ERR_INVALID_ARG, "rand_block"),
+    (dict(stride=2, rand_block=64, n_rand=1, rand_idx=FAKE), ea.ATTN_BF16, ea.ATTN_ERR_UNSUPPORTED, "combined"),
+    (dict(stride=2, block=16), ea.ATTN_BF16, ea.ATTN_ERR_UNSUPPORTED, "window only"),
+    (dict(stride=2, dilation=2), ea.ATTN_BF16, ea.ATTN_ERR_UNSUPPORTED, "window only"),
+    (dict(rand_block=48, n_rand=1, rand_idx=FAKE), ea.ATTN_BF16, ea.ATTN_ERR_UNSUPPORTED, "multiple of 32"),
+    (dict(rand_block=64, n_rand=0, rand_idx=FAKE), ea.ATTN_BF16, ea.ATTN_ERR_INVALID_ARG, "n_rand"),
+    (dict(rand_block=64, n_rand=17, rand_idx=FAKE), ea.ATTN_BF16, ea.ATTN_ERR_INVALID_ARG, "n_rand"),
+    (dict(rand_block=64, n_rand=2, rand_idx=None), ea.ATTN_BF16, ea.ATTN_ERR_INVALID_ARG, "NULL"),
+    (dict(rand_block=64, n_rand=2, rand_idx=FAKE + 2), ea.ATTN_BF16, ea.ATTN_ERR_INVALID_ARG, "aligned"),
+    (dict(stride=3, win_left=2, win_right=2), ea.ATTN_F32, ea.ATTN_ERR_UNSUPPORTED, "bf16"),
+    # valid configurations pass every check and stop at the scale
+    (dict(stride=3, win_left=2, win_right=2, scale=-1.0), ea.ATTN_BF16, ea.ATTN_ERR_INVALID_ARG, "scale"),
+    (dict(rand_block=32, n_rand=3, rand_idx=FAKE, causal=1, win_left=31, scale=-1.0), ea.ATTN_BF16,
+     ea.ATTN_ERR_INVALID_ARG, "scale"),
+])
+def test_extra_rule_validation(m, dtype, status, text):
+    err = _call_masked(dtype=dtype, **m)
+    assert err.status == status, err.message
+    assert text in err.message, err.message
+
+
+def test_extra_rules_rejected_by_backward():
+    err = _call_bwd_masked(stride=2, win_left=3, win_right=3)
+    assert err.status == ea.ATTN_ERR_UNSUPPORTED and "strided" in err.message
+
+
+def test_random_plan_stats_unsupported():
+    with pytest.raises(ea.AttnError) as ei:
+        ea.attn_plan_stats_masked(100, 128, 64, rand_block=32, n_rand=1, rand_idx=FAKE, win_left=2, win_right=2)
+    assert ei.value.status == ea.ATTN_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("N", [1, 63, 300, 1000, 4097])
+@pytest.mark.parametrize("m", [dict(stride=1, causal=1, win_left=0, win_right=0),
+                               dict(stride=3, causal=0, win_left=5, win_right=5),
+                               dict(stride=16, causal=1, win_left=40, win_right=0, global_idx=[0, 7, 999]),
+                               dict(stride=2, causal=0, win_left=0, win_right=0, global_idx=[10]),
+                               dict(stride=5000, causal=1, win_left=3, win_right=0)])
+def test_strided_plan_pairs_match_oracle(N, m):
+    G = [g for g in m.get("global_idx", []) if g < N]
+    mm = dict(m, global_idx=G)
+    pairs = ea.attn_plan_stats_masked(N, 128, 64, **mm)[0]
+    ref = oracle.visible_pairs_bruteforce(N, m["causal"], m["win_left"], m["win_right"], tuple(G), stride=m["stride"])
+    assert pairs == ref

@@ -37,5 +37,5 @@ def test_band_kernel_fits_two_waves_per_simd(resources):
     """The 512-thread band instances (plain and dilated) keep within 256
     registers, the budget of two waves per SIMD."""
     for k, v in resources.items():
-        if "fwd_band_bf16" in k and "Lb0EEE" in k:   # BLK = false: the 512-thread instances
+        if "fwd_band_bf16" in k and "Lb0ELb0EEE" in k:   # BLK = XT = false: the 512-thread instances
             assert v["vgpr"] + v["agpr"] <= 256, (k, v)
