@@ -162,6 +162,8 @@ def main():
     ap.add_argument("--decode", default=None, choices=sorted(W.DECODE_WORKLOADS),
                     help="time one decoding step (attn_decode) of this cache workload instead; "
                          "HBM-bound, reported in GB/s of K/V cache read")
+    ap.add_argument("--pattern", default=None, choices=sorted(W.PATTERN_WORKLOADS),
+                    help="time the forward of a strided or random-block (BigBird-style) workload instead")
     ap.add_argument("--cold", action="store_true",
                     help="write a 1 GiB scratch buffer before every timed call (cold MALL)")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -189,6 +191,8 @@ def main():
         return bench_bwd(args)
     if args.decode:
         return bench_decode(args)
+    if args.pattern:
+        return bench_pattern(args)
 
     w = W.WORKLOADS[args.config]
     print(f"[bench] generating {w.name}: B={w.B} H={w.H} N={w.N} d={w.d} {w.dtype}", file=sys.stderr,
@@ -334,6 +338,57 @@ def bench_bwd(args):
                       "config": {"workload": f"{mask_name(w)} attention backward B={w.B} H={w.H} N={w.N} d={w.d}",
                                  "useful_flop_per_step": flops},
                       "pct_bf16_peak": round(100 * value / PEAK_BF16, 2)}), flush=True)
+    return 0
+
+
+def bench_pattern(args):
+    """Forward of a strided or random-block workload: one attn_fwd_masked call
+    per step; useful FLOP = 4*d per visible pair (from the planner, which
+    reads the random lists back from the device)."""
+    import torch
+    import efficient_exact_attention_amd as ea
+    from efficient_exact_attention_amd import workloads as W
+    pw = W.PATTERN_WORKLOADS[args.pattern]
+    w = pw["workload"]
+    print(f"[bench] generating {w.name}: {w.desc}", file=sys.stderr, flush=True)
+    q, k, v = (torch.from_numpy(x.view("int16")).view(torch.bfloat16).cuda() for x in W.make_qkv(w))
+    kw = dict(causal=w.causal, win_left=w.win_left, win_right=w.win_right, global_idx=w.global_idx or None,
+              stride=pw["stride"], rand_block=pw["rand_block"])
+    lists = None
+    if pw["rand_block"]:
+        lists = torch.from_numpy(W.random_block_lists(w.N, pw["rand_block"], pw["n_rand"], w.seed + 9)).cuda()
+        kw["rand_idx"] = lists
+    pairs = ea.attn_plan_stats_masked(w.N, 128, 64, causal=w.causal, win_left=w.win_left, win_right=w.win_right,
+                                      global_idx=list(w.global_idx), stride=pw["stride"],
+                                      rand_block=pw["rand_block"], n_rand=pw["n_rand"],
+                                      rand_idx=lists.data_ptr() if lists is not None else None)[0]
+    flops = 4 * w.d * pairs * w.B * w.H
+    out = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        ea.fwd(q, k, v, out=out, lse=lse, stream=stream, **kw)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for s_, e_ in ev:
+        s_.record(stream)
+        step()
+        e_.record(stream)
+    torch.cuda.synchronize()
+    ms = sorted(s_.elapsed_time(e_) for s_, e_ in ev)
+    avg = sum(ms) / len(ms)
+    value = flops / (avg * 1e-3) / 1e12
+    print(json.dumps({"metric": "fwd attention TFLOP/s (unmasked FLOPs only)", "value": round(value, 2),
+                      "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+                      "ms_per_step": round(avg, 4), "median_launch_ms": round(ms[len(ms) // 2], 4),
+                      "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
+                      "config": {"workload": f"{w.desc}: B={w.B} H={w.H} N={w.N} d={w.d}",
+                                 "visible_pairs_per_head": pairs, "useful_flop_per_step": flops},
+                      "roofline": {"bound": "mfma", "achieved": round(value, 2), "peak": PEAK_BF16, "unit": "TFLOP/s",
+                                   "frac": round(value / PEAK_BF16, 4), "traffic": None}}), flush=True)
     return 0
 
 

@@ -188,6 +188,14 @@ int plan_impl(int N, const MaskSpec &m, int bm, int bn, long long *visible_pairs
     std::vector<char> is_g(N, 0);
     if (use_g)
         for (int g : m.G) is_g[g] = 1;
+    // the random-block lists live on the device: one blocking copy
+    std::vector<int> lists;
+    const int rb = m.rand_block, nkb = rb > 0 ? (N + rb - 1) / rb : 0;
+    if (rb > 0) {
+        lists.resize((size_t)nkb * m.n_rand);
+        hipError_t e = hipMemcpy(lists.data(), m.rand_idx, lists.size() * sizeof(int), hipMemcpyDeviceToHost);
+        if (e != hipSuccess) return fail(ATTN_ERR_DEVICE, "reading rand_idx: %s", hipGetErrorString(e));
+    }
     long long pairs = 0, full = 0, edge = 0;
     // every residue class (one class unless dilated) is a band of its own
     for (int r = 0; r < m.dil && r < N; ++r) {
@@ -204,6 +212,20 @@ int plan_impl(int N, const MaskSpec &m, int bm, int bn, long long *visible_pairs
             if (use_g)
                 for (int g : m.G)
                     if ((g < lo || g > hi) && (!causal || g <= i)) ++pairs;
+            if (rb > 0) {   // keys of each distinct listed block outside the band, off the globals
+                const int *lst = &lists[(size_t)(i / rb) * m.n_rand];
+                for (int e = 0; e < m.n_rand; ++e) {
+                    const int kb = lst[e];
+                    bool skip = kb < 0 || kb >= nkb;
+                    for (int e2 = 0; e2 < e && !skip; ++e2) skip = lst[e2] == kb;
+                    if (skip) continue;
+                    const int j1 = std::min(Nr - 1, kb * rb + rb - 1);
+                    for (int j = kb * rb; j <= j1; ++j) {
+                        if ((causal && j > i) || (j >= lo && j <= hi) || (use_g && is_g[j])) continue;
+                        ++pairs;
+                    }
+                }
+            }
             if (m.stride > 0)   // positions at distance stride * 2^k outside the band, off the globals
                 for (long long o = m.stride; o < Nr; o *= 2)
                     for (int sgn = -1; sgn <= 1; sgn += 2) {
@@ -279,8 +301,6 @@ int attn_plan_stats_masked(int N, const attn_mask *mask, int bm, int bn, long lo
     if (rc != ATTN_OK) return rc;
     rc = resolve_extras(N, mask, m);
     if (rc != ATTN_OK) return rc;
-    if (m.rand_block > 0)
-        return fail(ATTN_ERR_UNSUPPORTED, "plan statistics of the random-block rule need its device lists");
     return plan_impl(N, m, bm, bn, visible_pairs, tiles_full, tiles_edge);
 }
 

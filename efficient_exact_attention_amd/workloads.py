@@ -231,3 +231,24 @@ def make_decode(w: DecodeWorkload, b_list=None):
     with ThreadPoolExecutor(min(16, len(os.sched_getaffinity(0)))) as ex:
         list(ex.map(fill, jobs))
     return q, kc, vc, np.asarray(w.seq_len, np.int32)
+
+
+# Workloads of the strided and random-block rules (forward only).
+PATTERN_WORKLOADS = {
+    # BigBird-style: window of one 64-token block each side, the first block
+    # as global tokens, 3 random key blocks of 64 per query block
+    "bigbird": dict(workload=Workload("bigbird", 1, 16, 16384, 64, "bf16", 1.0, 0, 64, 64, tuple(range(64)), 301,
+                                      "BigBird-style: window +-64, 64 global tokens, 3 random blocks of 64"),
+                    rand_block=64, n_rand=3, stride=0),
+    # strided rule with a local window: row i sees i-255..i and i - 256 * 2^m
+    "strided": dict(workload=Workload("strided", 1, 16, 16384, 128, "bf16", 1.0, 1, 255, 0, (), 302,
+                                      "causal window 256 + positions at distance 256, 512, 1024, ..."),
+                    rand_block=0, n_rand=0, stride=256),
+}
+
+
+def random_block_lists(N: int, b: int, r: int, seed: int) -> np.ndarray:
+    """Seeded key-block lists [ceil(N / b), r] (int32): uniform draws over the
+    blocks, repeats allowed (they count once)."""
+    nb = (N + b - 1) // b
+    return np.random.default_rng(seed).integers(0, nb, size=(nb, r)).astype(np.int32)

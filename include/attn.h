@@ -294,6 +294,10 @@ int attn_plan_stats(int N, int causal, int win_left, int win_right,
  * attn_plan_stats_masked - attn_plan_stats for an attn_mask. With a dilated
  * mask the counts are summed over the residue classes, each planned as its
  * own band over its strided rows (the way the forward kernel visits them).
+ * The strided rule's extra tiles are counted in tiles_edge (random blocks'
+ * tiles are not); with the random-block rule the call reads the lists from
+ * device memory with one blocking copy (the only HIP call of the planner)
+ * and fails with ATTN_ERR_DEVICE if it cannot.
  */
 int attn_plan_stats_masked(int N, const attn_mask *mask, int bm, int bn,
                            long long *visible_pairs, long long *tiles_full,

@@ -475,9 +475,11 @@ def test_extra_rules_rejected_by_backward():
     assert err.status == ea.ATTN_ERR_UNSUPPORTED and "strided" in err.message
 
 
-def test_random_plan_stats_unsupported():
+def test_random_plan_stats_validation_before_the_copy():
+    """Invalid random-block fields are reported before the planner reads the
+    device lists."""
     with pytest.raises(ea.AttnError) as ei:
-        ea.attn_plan_stats_masked(100, 128, 64, rand_block=32, n_rand=1, rand_idx=FAKE, win_left=2, win_right=2)
+        ea.attn_plan_stats_masked(100, 128, 64, rand_block=48, n_rand=1, rand_idx=FAKE, win_left=2, win_right=2)
     assert ei.value.status == ea.ATTN_ERR_UNSUPPORTED
 
 

@@ -121,3 +121,21 @@ def test_every_block_listed_is_full_attention():
     torch.cuda.synchronize()
     assert (o1.float() - o2.float()).abs().max().item() <= 1e-2
     assert (l1 - l2).abs().max().item() <= 1e-3
+
+
+@pytest.mark.parametrize("ci", range(len(RANDOM)))
+@pytest.mark.parametrize("N", [40, 700, 1000])
+def test_random_plan_pairs_match_oracle(ci, N):
+    """The planner's visible-pair count for random blocks (lists read from
+    the device) against the oracle's mask."""
+    import efficient_exact_attention_amd as ea
+    m, r, extra = RANDOM[ci]
+    G = tuple(g for g in m.get("global_idx", ()) if g < N)
+    lists = rand_lists(N, m["rand_block"], r, seed=ci + N, extra=extra)
+    dl = torch.from_numpy(lists).cuda()
+    pairs = ea.attn_plan_stats_masked(N, 128, 64, causal=m["causal"], win_left=m["win_left"],
+                                      win_right=m["win_right"], global_idx=list(G), rand_block=m["rand_block"],
+                                      n_rand=r, rand_idx=dl.data_ptr())[0]
+    ref = oracle.visible_pairs_bruteforce(N, m["causal"], m["win_left"], m["win_right"], G,
+                                          rand_block=m["rand_block"], rand_idx=lists)
+    assert pairs == ref
