@@ -546,6 +546,7 @@ __global__ void __launch_bounds__(64) bwd_merge_dq(const BwdParams prm) {
     __bf16 *dst = static_cast<__bf16 *>(prm.dq) + bh * prm.head_stride + (long long)prm.gidx[r] * D;
     for (int d = threadIdx.x; d < D; d += 64) {
         float acc = 0.f;
+#pragma unroll 8
         for (int ci = 0; ci < prm.gchunks_q; ++ci) acc += src[ci * D + d];
         dst[d] = (__bf16)((float)dst[d] + acc * prm.scale);
     }
@@ -561,6 +562,7 @@ __global__ void __launch_bounds__(64) bwd_merge_dkdv(const BwdParams prm) {
     __bf16 *dv = static_cast<__bf16 *>(prm.dv) + bkv * prm.head_stride + (long long)prm.gidx[r] * D;
     for (int d = threadIdx.x; d < D; d += 64) {
         float ak = 0.f, av = 0.f;
+#pragma unroll 8
         for (int ci = 0; ci < prm.gchunks_k; ++ci) {
             ak += src[ci * 2 * D + d];
             av += src[ci * 2 * D + D + d];

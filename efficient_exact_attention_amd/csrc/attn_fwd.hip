@@ -895,36 +895,49 @@ __global__ void __launch_bounds__((BLK || XT) ? 256 : 512) fwd_band_bf16(const F
 // identity as the online softmax, applied across chunks.
 template <int D, bool F32>
 __global__ void __launch_bounds__(64) merge_kernel(const FwdParams prm) {
-    const int ng = prm.n_global;
+    // the chunk maxima are read across lanes (no chain of dependent loads);
+    // each chunk's weight exp2(m_c - M) goes to LDS for the output sum
+    __shared__ float wsh[kMaxGlobalChunks];
+    const int ng = prm.n_global, lane = threadIdx.x;
     const int bh = blockIdx.x / ng, t = blockIdx.x - bh * ng;
-    __shared__ int s_g;
-    if (threadIdx.x == 0) s_g = prm.gidx[t];
-    __syncthreads();
-    const int g = s_g;
-    const float *src = prm.part + ((long long)bh * ng + t) * prm.chunks * (D + 2);
+    const int g = prm.gidx[t];
+    const int C = prm.chunks;
+    const float *src = prm.part + ((long long)bh * ng + t) * C * (D + 2);
     float M = EEA_NEG_INF;
-    for (int ci = 0; ci < prm.chunks; ++ci) M = fmaxf(M, src[ci * (D + 2) + D]);
+    for (int ci = lane; ci < C; ci += 64) M = fmaxf(M, src[ci * (D + 2) + D]);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
     float Lsum = 0.f;
-    for (int ci = 0; ci < prm.chunks; ++ci) {
+    for (int ci = lane; ci < C; ci += 64) {
         const float mc = src[ci * (D + 2) + D];
-        if (mc != EEA_NEG_INF) Lsum += src[ci * (D + 2) + D + 1] * fast_exp2(mc - M);
+        const float w = mc == EEA_NEG_INF ? 0.f : fast_exp2(mc - M);
+        wsh[ci] = w;
+        Lsum += w * src[ci * (D + 2) + D + 1];
     }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) Lsum += __shfl_xor(Lsum, off);
+    __syncthreads();
     const float inv = Lsum > 0.f ? 1.f / Lsum : 0.f;
-    for (int dd = threadIdx.x; dd < D; dd += 64) {
-        float acc = 0.f;
-        for (int ci = 0; ci < prm.chunks; ++ci) {
-            const float mc = src[ci * (D + 2) + D];
-            if (mc != EEA_NEG_INF) acc += src[ci * (D + 2) + dd] * fast_exp2(mc - M);
-        }
-        const long long o = ((long long)bh * prm.N + g) * D + dd;
+    constexpr int PER = D / 64;
+    float acc[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) acc[j] = 0.f;
+#pragma unroll 4
+    for (int ci = 0; ci < C; ++ci) {
+        const float w = wsh[ci];
+#pragma unroll
+        for (int j = 0; j < PER; ++j) acc[j] += src[ci * (D + 2) + lane + 64 * j] * w;
+    }
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        const long long o = ((long long)bh * prm.N + g) * D + lane + 64 * j;
         if (F32) {
-            static_cast<float *>(prm.out)[o] = acc * inv;
+            static_cast<float *>(prm.out)[o] = acc[j] * inv;
         } else {
-            static_cast<__bf16 *>(prm.out)[o] = (__bf16)(acc * inv);
+            static_cast<__bf16 *>(prm.out)[o] = (__bf16)(acc[j] * inv);
         }
     }
-    if (threadIdx.x == 0)
-        prm.lse[(long long)bh * prm.N + g] = Lsum > 0.f ? (M + __log2f(Lsum)) * kLn2 : EEA_NEG_INF;
+    if (lane == 0) prm.lse[(long long)bh * prm.N + g] = Lsum > 0.f ? (M + __log2f(Lsum)) * kLn2 : EEA_NEG_INF;
 }
 
 // ---------------------------------------------------------------------------
@@ -943,8 +956,9 @@ int tile_bn(int d, int f32) { (void)d; return f32 ? 32 : 64; }
 int global_chunks(int BH, int N, int d, int f32, int *chunk_tiles) {
     const int bn = tile_bn(d, f32);
     const int num_kt = (N + bn - 1) / bn;
-    // aim for a few hundred workgroups in the split-key pass
-    int target = (512 + BH - 1) / BH;
+    // aim for a few hundred workgroups in the split-key pass (at most
+    // kMaxGlobalChunks chunks: the merge keeps one weight per chunk in LDS)
+    int target = (kMaxGlobalChunks + BH - 1) / BH;
     if (target < 1) target = 1;
     if (target > num_kt) target = num_kt;
     int ct = (num_kt + target - 1) / target;

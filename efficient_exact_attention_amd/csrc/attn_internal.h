@@ -8,6 +8,7 @@
 namespace eea {
 
 constexpr int kMaxGlobal = 64;       // one gathered key tile holds every global column
+constexpr int kMaxGlobalChunks = 512; // key chunks of the split-key pass over global rows
 
 // Kernel arguments. Offsets are 64-bit throughout: one head at N=131072, d=128
 // is 2^24 elements and B*H*N*d can exceed 2^31.
