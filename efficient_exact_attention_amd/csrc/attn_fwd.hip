@@ -656,12 +656,25 @@ __global__ void __launch_bounds__((BLK || XT) ? 256 : 512) fwd_band_bf16(const F
     // plain sequence.
     const int G = gridDim.x;
     const int bid = blockIdx.x;
-    const int Lw = prm.xcd_remap ? (bid & 7) * (G >> 3) + (bid >> 3) : bid;
     const int dil = DIL ? prm.dil : 1;
-    const int per_head = dil * prm.num_qt;
-    const int bh = Lw / per_head;
-    const int rcls = (Lw - bh * per_head) / prm.num_qt;
-    const int qi = Lw - bh * per_head - rcls * prm.num_qt;
+    int bh, rcls, qi;
+    if (!DIL && prm.xcd_remap == 2) {
+        // workgroups are dispatched round-robin over the 8 XCDs (bid % 8):
+        // each XCD owns BH/8 consecutive heads (their K/V share its L2) and
+        // takes their query tiles heaviest first across all of them, so the
+        // light causal tiles fill the tail
+        const int hx = prm.BH >> 3;
+        const int k = bid >> 3;
+        bh = (bid & 7) * hx + k % hx;
+        rcls = 0;
+        qi = k / hx;
+    } else {
+        const int Lw = prm.xcd_remap ? (bid & 7) * (G >> 3) + (bid >> 3) : bid;
+        const int per_head = dil * prm.num_qt;
+        bh = Lw / per_head;
+        rcls = (Lw - bh * per_head) / prm.num_qt;
+        qi = Lw - bh * per_head - rcls * prm.num_qt;
+    }
     const int unit = prm.causal ? prm.num_qt - 1 - qi : qi;
     const int N = (prm.N - rcls + dil - 1) / dil;   // rows of this residue class
     if (unit * BM >= N) return;                      // whole workgroup: a shorter class
@@ -972,6 +985,12 @@ static hipError_t launch_impl(const FwdParams &p0, hipStream_t stream) {
     FwdParams p = p0;
     const int grid = p.BH * p.dil * p.num_qt;
     p.xcd_remap = (grid % 8 == 0) ? 1 : 0;
+    // short causal sequences: heads per XCD, heaviest tiles first across
+    // them (the tail is a large share of the call). Long ones keep one head
+    // at a time per XCD, whose K/V stream the XCD's L2 then serves to every
+    // workgroup (measured: 872 -> 930 TFLOP/s at N=4096, B*H=128; 1161 ->
+    // 1114 at N=32768, B*H=32 with the head-interleaved order)
+    if (!F32 && p.dil == 1 && p.causal && p.BH % 8 == 0 && p.num_qt <= 32) p.xcd_remap = 2;
     if constexpr (F32)
         hipLaunchKernelGGL((fwd_kernel<PB, MODE_BAND>), dim3(grid), dim3(PB::NT), 0, stream, p);
     else if (p.stride > 0 || p.rand_block > 0)

@@ -32,7 +32,7 @@ struct FwdParams {
     int num_qt;           // query tiles per head (per residue class when dil > 1)
     int chunks;           // key chunks per global row (split-key pass)
     int chunk_tiles;      // key tiles per chunk
-    int xcd_remap;        // 1: group consecutive work items on one XCD
+    int xcd_remap;        // 1: group consecutive work items on one XCD; 2: heads per XCD, heaviest tiles first
     float scale_log2;     // score scale * log2(e)
     int stride;           // > 0: also the positions at distance stride * 2^m
     int rand_block;       // > 0: random-block rule, blocks of rand_block positions
