@@ -284,7 +284,8 @@ def fwd(q, k, v, *, causal=False, win_left=-1, win_right=-1, global_idx=None, sc
 
 
 def bwd(q, k, v, out, dout, lse, *, causal=False, win_left=-1, win_right=-1, global_idx=None, scale=None,
-        dq=None, dk=None, dv=None, workspace=None, stream=None, block=0, dilation=1):
+        dq=None, dk=None, dv=None, workspace=None, stream=None, block=0, dilation=1, stride=0, rand_block=0,
+        rand_idx=None):
     """Gradients (dq, dk, dv) of ``fwd`` on torch CUDA bf16 tensors: q, out,
     dout [B, H, N, d], k, v [B, H_kv, N, d], lse fp32 [B, H, N] from the
     forward call with the same mask and scale. Allocates the gradients with
@@ -311,11 +312,18 @@ def bwd(q, k, v, out, dout, lse, *, causal=False, win_left=-1, win_right=-1, glo
         stream = stream.cuda_stream
     ws, wsb = (workspace.data_ptr(), workspace.numel() * workspace.element_size()) \
         if workspace is not None else (None, 0)
+    n_rand, rptr = 0, None
+    if rand_block:
+        if rand_idx is None or rand_idx.dtype != torch.int32 or not rand_idx.is_cuda or rand_idx.dim() != 2 \
+                or not rand_idx.is_contiguous() or rand_idx.shape[0] != (N + rand_block - 1) // rand_block:
+            raise ValueError("rand_idx must be a contiguous int32 device tensor [ceil(N / rand_block), r]")
+        n_rand, rptr = rand_idx.shape[1], rand_idx.data_ptr()
     attn_bwd_masked(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(), lse.data_ptr(),
                     dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, H_kv, N, d, causal=causal,
                     win_left=win_left, win_right=win_right, block=block, dilation=dilation,
                     global_idx=global_idx, scale=0.0 if scale is None else float(scale), stream=stream,
-                    workspace=ws, workspace_bytes=wsb)
+                    workspace=ws, workspace_bytes=wsb, stride=stride, rand_block=rand_block, n_rand=n_rand,
+                    rand_idx=rptr)
     return dq, dk, dv
 
 

@@ -509,7 +509,8 @@ BwdLayout bwd_layout(long long BH, long long BKV, int N, int d, int ng) {
 
 int bwd_impl(const void *q, const void *k, const void *v, const void *out, const void *dout, const float *lse,
              void *dq, void *dk, void *dv, int B, int H, int H_kv, int N, int d, int causal, int win_left,
-             int win_right, int block, int dilation, const int *global_idx, int n_global, const attn_opts *opts) {
+             int win_right, int block, int dilation, const int *global_idx, int n_global, const attn_opts *opts,
+             const attn_mask *extras = nullptr) {
     g_err.clear();
     const int dtype = opts ? opts->dtype : ATTN_BF16;
     if (!q || !k || !v || !out || !dout || !lse || !dq || !dk || !dv)
@@ -524,6 +525,8 @@ int bwd_impl(const void *q, const void *k, const void *v, const void *out, const
     int rc = resolve_mask(N, causal, win_left, win_right, block, dilation, global_idx, n_global, m);
     if (rc != ATTN_OK) return rc;
     if (d != 64 && d != 128) return fail(ATTN_ERR_UNSUPPORTED, "head size d=%d is not supported (64 or 128)", d);
+    rc = resolve_extras(N, extras, m);
+    if (rc != ATTN_OK) return rc;
     const eea::Band band = m.band;
 
     const long long BH = (long long)B * H;
@@ -606,6 +609,10 @@ int bwd_impl(const void *q, const void *k, const void *v, const void *out, const
     p.gct_q = lay.gct_q;
     p.gchunks_k = lay.gchunks_k;
     p.gct_k = lay.gct_k;
+    p.stride = m.stride;
+    p.rand_block = m.rand_block;
+    p.n_rand = m.n_rand;
+    p.rand_idx = m.rand_idx;
 
     // ---- first HIP call
     rc = device_and_scratch(need, &ws, true);
@@ -741,12 +748,8 @@ int attn_bwd_masked(const void *q, const void *k, const void *v, const void *out
         g_err.clear();
         return fail(ATTN_ERR_INVALID_ARG, "mask is NULL");
     }
-    if (mask->stride != 0 || mask->rand_block != 0) {
-        g_err.clear();
-        return fail(ATTN_ERR_UNSUPPORTED, "the backward pass does not support the strided or random-block rules");
-    }
     return bwd_impl(q, k, v, out, dout, lse, dq, dk, dv, B, H, H_kv, N, d, mask->causal, mask->win_left,
-                    mask->win_right, mask->block, mask->dilation, mask->global_idx, mask->n_global, opts);
+                    mask->win_right, mask->block, mask->dilation, mask->global_idx, mask->n_global, opts, mask);
 }
 
 size_t attn_bwd_workspace_bytes(int B, int H, int H_kv, int N, int d, int n_global) {

@@ -100,7 +100,9 @@ __device__ __forceinline__ unsigned long long global_rows_in(const int *g, int n
 // BWD_GSET: the global columns as the keys (one workgroup per (K/V head,
 //   chunk of query tiles)), rows of set S2, fp32 partials out.
 // ---------------------------------------------------------------------------
-template <int D, bool DIL, int MODE>
+// XT (with BWD_BAND_GL): the rows that see this workgroup's keys by the
+// log-spaced strided or the random-block rule, as extra query tiles.
+template <int D, bool DIL, int MODE, bool XT = false>
 __global__ void __launch_bounds__(kBwdThreads) bwd_dkdv(const BwdParams prm) {
     typedef Bf16Path<D, kBwdThreads> P;
     constexpr int BQ = P::BN;               // query rows per streamed tile
@@ -310,7 +312,7 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_dkdv(const BwdParams prm) {
     if constexpr (MODE == BWD_BAND_GL) {
         // set S3: per query head, the gathered tile of the global rows; a
         // global row counts here for the keys outside its own band
-        for (int hq = 0; hq < prm.group; ++hq) {
+        for (int hq = 0; hq < (ng > 0 ? prm.group : 0); ++hq) {
             const long long bh = (long long)b * prm.H + kvh * prm.group + hq;
             const uint16_t *qh = static_cast<const uint16_t *>(prm.q) + bh * prm.head_stride;
             const uint16_t *gh = static_cast<const uint16_t *>(prm.dout) + bh * prm.head_stride;
@@ -332,6 +334,86 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_dkdv(const BwdParams prm) {
                                          ((i < qlo) | (i > qhi));
                               });
             __syncthreads();
+        }
+    }
+
+    if constexpr (XT) {
+        // extra query tiles of the strided / random-block rules: a pair
+        // counts outside the key's band, off the global rows and columns
+        // (their pairs are in S2 and S3) and within the causal limit
+        bool key_is_g = false;
+        for (int t = 0; t < ng; ++t) key_is_g |= s_g[t] == key;
+        auto extra_qtile = [&](int q0, auto vis) __attribute__((always_inline)) {
+            for (int hq = 0; hq < prm.group; ++hq) {
+                const long long bh = (long long)b * prm.H + kvh * prm.group + hq;
+                const uint16_t *qh = static_cast<const uint16_t *>(prm.q) + bh * prm.head_stride;
+                const uint16_t *gh = static_cast<const uint16_t *>(prm.dout) + bh * prm.head_stride;
+                P::issue_k(L, qh, N, qk0, q0);
+                P::issue_v(L, qh, N, qv0, q0);
+                P::issue_k(L, gh, N, ok0, q0);
+                P::issue_v(L, gh, N, ov0, q0);
+                if (tid < BQ) {
+                    const int i = q0 + tid;
+                    s_lse[0][tid] = i < N ? prm.lse[bh * N + i] * kLog2e : 0.f;
+                    s_dl[0][tid] = i < N ? prm.delta[bh * N + i] : 0.f;
+                }
+                wait_vmem();
+                __syncthreads();
+                if (wave_active) {
+                    const unsigned long long gm = global_rows_in(s_g, ng, q0);
+                    tile_products(qk0, qv0, ok0, ov0, 0, TILE_EDGE, [&](int r) { return q0 + r; }, [&](int i) {
+                        return kvalid & !key_is_g & (i < N) & ((i < qlo) | (i > qhi)) &
+                               ((prm.causal == 0) | (i >= key)) & !((gm >> (i - q0)) & 1ull) && vis(i);
+                    });
+                }
+                __syncthreads();
+            }
+        };
+        const int K1 = imin(N - 1, K0 + BK - 1);
+        if (prm.stride > 0) {
+            // rows at distance o = stride * 2^m from the keys: [K0 - o, K1 - o]
+            // (farthest first, without the causal cut only) then
+            // [K0 + o, K1 + o] (nearest first), visited once each
+            const int st = prm.stride;
+            int mtop = -1;
+            while (mtop < 30 && ((long long)st << (mtop + 1)) < N) ++mtop;
+            int next = 0;
+            auto strided = [&](int i) {
+                const int dist = i > key ? i - key : key - i;
+                if (dist == 0 || dist % st) return false;
+                const int m = dist / st;
+                return (m & (m - 1)) == 0;
+            };
+            auto visit = [&](int rlo, int rhi) __attribute__((always_inline)) {
+                rlo = imax(rlo, 0);
+                rhi = imin(rhi, N - 1);
+                if (rlo > rhi) return;
+                const int t1 = rhi / BQ;
+                for (int t = imax(rlo / BQ, next); t <= t1; ++t) extra_qtile(t * BQ, strided);
+                next = imax(next, t1 + 1);
+            };
+            if (!prm.causal)
+                for (int m = mtop; m >= 0; --m) visit(K0 - (st << m), K1 - (st << m));
+            for (int m = 0; m <= mtop; ++m) visit(K0 + (st << m), K1 + (st << m));
+        }
+        if (prm.rand_block > 0) {
+            // the query blocks whose lists name a key block of this
+            // workgroup (out-of-range entries skipped, repeats once)
+            const int rb = prm.rand_block, nr = prm.n_rand, nb = (N + rb - 1) / rb;
+            for (int qb = 0; qb < nb; ++qb) {
+                const int *lst = prm.rand_idx + (long long)qb * nr;
+                for (int e = 0; e < nr; ++e) {
+                    const int kb = lst[e];
+                    bool skip = kb < 0 || kb >= nb || kb * rb > K1 || kb * rb + rb - 1 < K0;
+                    for (int e2 = 0; e2 < e && !skip; ++e2) skip = lst[e2] == kb;
+                    if (skip) continue;
+                    const int rlo = qb * rb, rhi = imin(N - 1, rlo + rb - 1);
+                    if (prm.causal && rhi < kb * rb) continue;
+                    const int klo = kb * rb, khi = kb * rb + rb - 1;
+                    for (int t = rlo / BQ; t <= rhi / BQ; ++t)
+                        extra_qtile(t * BQ, [&](int i) { return i >= rlo && i <= rhi && key >= klo && key <= khi; });
+                }
+            }
         }
     }
 
@@ -361,7 +443,9 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_dkdv(const BwdParams prm) {
 // BWD_GSET: the global rows as the query rows (one workgroup per (query head,
 //   chunk of key tiles)), keys of set S3, fp32 partials out.
 // ---------------------------------------------------------------------------
-template <int D, bool DIL, int MODE>
+// XT (with BWD_BAND_GL): the keys this workgroup's rows see by the
+// log-spaced strided or the random-block rule, as extra key tiles.
+template <int D, bool DIL, int MODE, bool XT = false>
 __global__ void __launch_bounds__(kBwdThreads) bwd_dq(const BwdParams prm) {
     typedef Bf16Path<D, kBwdThreads> P;
     constexpr int BN = P::BN;                 // keys per streamed tile
@@ -505,11 +589,12 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_dq(const BwdParams prm) {
         }
     }
 
-    if constexpr (MODE == BWD_BAND_GL) {
+    bool row_is_g = false;
+    if constexpr (MODE == BWD_BAND_GL)
+        for (int t = 0; t < ng; ++t) row_is_g |= s_g[t] == row;
+    if (MODE == BWD_BAND_GL && ng > 0) {
         // set S2: the gathered tile of the global columns; a global column
         // counts here for non-global rows outside whose band it lies
-        bool row_is_g = false;
-        for (int t = 0; t < ng; ++t) row_is_g |= s_g[t] == row;
         const TileSrc src{0, 1, N, ng, s_g};
         typename P::Stage st;
         P::issue(st, L, kh, kh, kk0, kv0, src, s_g[0]);
@@ -520,6 +605,69 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_dq(const BwdParams prm) {
             tile_products(kk0, kv0, vk0, TILE_EDGE, [&](int r) { return r < ng ? s_g[r] : -1; }, [&](int j) {
                 return valid & !row_is_g & (j >= 0) & ((prm.causal == 0) | (j <= row)) & ((j < lo) | (j > hi));
             });
+        __syncthreads();
+    }
+
+    if constexpr (XT) {
+        // extra key tiles of the strided / random-block rules (as in the
+        // forward): a pair counts outside the row's band, off the global rows
+        // and columns and within the causal limit
+        const int q1 = imin(N - 1, q0 + BM - 1);
+        auto extra_ktile = [&](int k0, bool take, auto vis) __attribute__((always_inline)) {
+            P::issue_k(L, kh, N, kk0, k0);
+            P::issue_v(L, kh, N, kv0, k0);
+            P::issue_k(L, vh, N, vk0, k0);
+            wait_vmem();
+            __syncthreads();
+            if (take) {
+                const unsigned long long gm = global_rows_in(s_g, ng, k0);   // global columns of the tile
+                tile_products(kk0, kv0, vk0, TILE_EDGE, [&](int r) { return k0 + r; }, [&](int j) {
+                    return valid & !row_is_g & (j < N) & ((j < lo) | (j > hi)) & ((prm.causal == 0) | (j <= row)) &
+                           !((gm >> (j - k0)) & 1ull) && vis(j);
+                });
+            }
+            __syncthreads();
+        };
+        if (prm.stride > 0) {
+            const int st = prm.stride;
+            int mtop = -1;
+            while (mtop < 30 && ((long long)st << (mtop + 1)) < N) ++mtop;
+            int next = 0;
+            auto strided = [&](int j) {
+                const int dist = j > row ? j - row : row - j;
+                if (dist == 0 || dist % st) return false;
+                const int m = dist / st;
+                return (m & (m - 1)) == 0;
+            };
+            auto visit = [&](int klo, int khi) __attribute__((always_inline)) {
+                klo = imax(klo, 0);
+                khi = imin(khi, N - 1);
+                if (klo > khi) return;
+                const int t1 = khi / BN;
+                for (int t = imax(klo / BN, next); t <= t1; ++t) extra_ktile(t * BN, wave_active, strided);
+                next = imax(next, t1 + 1);
+            };
+            for (int m = mtop; m >= 0; --m) visit(q0 - (st << m), q1 - (st << m));
+            if (!prm.causal)
+                for (int m = 0; m <= mtop; ++m) visit(q0 + (st << m), q1 + (st << m));
+        }
+        if (prm.rand_block > 0) {
+            const int rb = prm.rand_block, nr = prm.n_rand, nkb = (N + rb - 1) / rb;
+            const int my_qb = wr0 / rb;
+            for (int qb = q0 / rb; qb <= q1 / rb; ++qb) {
+                const int *lst = prm.rand_idx + (long long)qb * nr;
+                for (int e = 0; e < nr; ++e) {
+                    const int kb = lst[e];
+                    bool skip = kb < 0 || kb >= nkb;
+                    for (int e2 = 0; e2 < e && !skip; ++e2) skip = lst[e2] == kb;
+                    if (skip) continue;
+                    const int klo = kb * rb, khi = imin(N - 1, klo + rb - 1);
+                    if (prm.causal && klo > imin(q1, qb * rb + rb - 1)) continue;
+                    for (int t = klo / BN; t <= khi / BN; ++t)
+                        extra_ktile(t * BN, wave_active && my_qb == qb, [&](int j) { return j >= klo && j <= khi; });
+                }
+            }
+        }
     }
 
     if (!valid) return;
@@ -596,7 +744,9 @@ static hipError_t launch_bwd_impl(const BwdParams &p0, hipStream_t stream) {
     const int BKV = p.BH / p.group;
     const int kgrid = BKV * p.dil * p.num_kt;
     p.xcd_remap_k = kgrid % 8 == 0;
-    if (p.n_global > 0)
+    if (p.stride > 0 || p.rand_block > 0)
+        hipLaunchKernelGGL((bwd_dkdv<D, false, BWD_BAND_GL, true>), dim3(kgrid), dim3(kBwdThreads), 0, stream, p);
+    else if (p.n_global > 0)
         hipLaunchKernelGGL((bwd_dkdv<D, false, BWD_BAND_GL>), dim3(kgrid), dim3(kBwdThreads), 0, stream, p);
     else if (p.dil > 1)
         hipLaunchKernelGGL((bwd_dkdv<D, true, BWD_BAND>), dim3(kgrid), dim3(kBwdThreads), 0, stream, p);
@@ -606,7 +756,9 @@ static hipError_t launch_bwd_impl(const BwdParams &p0, hipStream_t stream) {
     if (e != hipSuccess) return e;
     const int qgrid = p.BH * p.dil * p.num_qt;
     p.xcd_remap_q = qgrid % 8 == 0;
-    if (p.n_global > 0)
+    if (p.stride > 0 || p.rand_block > 0)
+        hipLaunchKernelGGL((bwd_dq<D, false, BWD_BAND_GL, true>), dim3(qgrid), dim3(kBwdThreads), 0, stream, p);
+    else if (p.n_global > 0)
         hipLaunchKernelGGL((bwd_dq<D, false, BWD_BAND_GL>), dim3(qgrid), dim3(kBwdThreads), 0, stream, p);
     else if (p.dil > 1)
         hipLaunchKernelGGL((bwd_dq<D, true, BWD_BAND>), dim3(qgrid), dim3(kBwdThreads), 0, stream, p);

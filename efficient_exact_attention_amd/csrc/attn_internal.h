@@ -73,6 +73,9 @@ struct BwdParams {
     int gchunks_k, gct_k;   // split pass over query rows for the global columns
     float *part_q;          // workspace: [B*H][n_global][gchunks_q][d] fp32
     float *part_k;          // workspace: [B*H_kv][n_global][gchunks_k][2d] fp32
+    int stride;             // > 0: also the positions at distance stride * 2^m
+    int rand_block, n_rand; // random-block rule (rand_block 0: off)
+    const int *rand_idx;    // device [ceil(N / rand_block)][n_rand] key-block lists
     int gidx[kMaxGlobal];   // sorted global positions
 };
 

@@ -117,8 +117,7 @@ int attn_fwd_ex(const void *q, const void *k, const void *v, void *out, float *l
  *       not combined with global tokens.
  * causal (j <= i) is ANDed with the result, global tokens (rows that see
  * everything and columns seen by everyone) ORed with the local rule, and so
- * is at most one of two extra rules (window local rule only; bf16 forward
- * only: the backward pass gives ATTN_ERR_UNSUPPORTED):
+ * is at most one of two extra rules (window local rule only; bf16 only):
  *   strided (stride = s > 0): j is at distance s, 2s, 4s, ... from i ("Module
  *       9 - Quadratic cost and efficient attention", table in "Sparse and
  *       windowed attention": strides s, 2s, 4s with O(n log n) cost);
@@ -210,8 +209,8 @@ int attn_bwd(const void *q, const void *k, const void *v, const void *out, const
 
 /*
  * attn_bwd_masked - attn_bwd with the mask given as an attn_mask: window,
- * block-sparse and dilated rules, global tokens (the combinations attn_fwd_masked
- * accepts).
+ * block-sparse and dilated rules, global tokens, the strided and random-block
+ * rules (the combinations attn_fwd_masked accepts for bf16).
  */
 int attn_bwd_masked(const void *q, const void *k, const void *v, const void *out, const void *dout,
                     const float *lse, void *dq, void *dk, void *dv,

@@ -470,9 +470,13 @@ def test_extra_rule_validation(m, dtype, status, text):
     assert text in err.message, err.message
 
 
-def test_extra_rules_rejected_by_backward():
-    err = _call_bwd_masked(stride=2, win_left=3, win_right=3)
-    assert err.status == ea.ATTN_ERR_UNSUPPORTED and "strided" in err.message
+def test_extra_rules_accepted_by_backward():
+    """The strided and random-block rules pass the backward's validation
+    (the call then stops on the invalid scale, before the device)."""
+    err = _call_bwd_masked(stride=2, win_left=3, win_right=3, scale=-1.0)
+    assert err.status == ea.ATTN_ERR_INVALID_ARG and "scale" in err.message
+    err = _call_bwd_masked(rand_block=48, n_rand=1, rand_idx=FAKE, win_left=3, win_right=3)
+    assert err.status == ea.ATTN_ERR_UNSUPPORTED and "multiple of 32" in err.message
 
 
 def test_random_plan_stats_validation_before_the_copy():

@@ -139,3 +139,40 @@ def test_random_plan_pairs_match_oracle(ci, N):
     ref = oracle.visible_pairs_bruteforce(N, m["causal"], m["win_left"], m["win_right"], G,
                                           rand_block=m["rand_block"], rand_idx=lists)
     assert pairs == ref
+
+
+# ---- backward of the strided and random-block rules ----------------------------
+
+def run_bwd_extra(B, H, H_kv, N, d, m, seed, lists=None):
+    import efficient_exact_attention_amd as ea
+    from test_bwd_gpu import check_bwd
+    q, k, v = _inputs(B, H, H_kv, N, d, seed)
+    do = W.make_tensor(W.random_workload("xdo", B, H, N, d, seed=seed + 5), 0)
+    qd, kd, vd, dod = (to_device(x, "bf16") for x in (q, k, v, do))
+    kw = dict(m)
+    if lists is not None:
+        kw["rand_idx"] = torch.from_numpy(lists).cuda()
+    say(f"  launch extra-rule bwd: B={B} H={H} H_kv={H_kv} N={N} d={d} mask={m} seed={seed}")
+    out, lse = ea.fwd(qd, kd, vd, **kw)
+    grads = ea.bwd(qd, kd, vd, out, dod, lse, **kw)
+    torch.cuda.synchronize()
+    mo = dict(causal=m.get("causal", 0), win_left=m.get("win_left", -1), win_right=m.get("win_right", -1),
+              global_idx=tuple(m.get("global_idx", ()) or ()), stride=m.get("stride", 0),
+              rand_block=m.get("rand_block", 0), rand_idx=lists)
+    check_bwd((q, k, v, do), grads, mo)
+
+
+@pytest.mark.parametrize("m", STRIDED, ids=str)
+@pytest.mark.parametrize("N,d,H,H_kv", [(700, 128, 4, 2), (333, 64, 2, 2), (5, 64, 1, 1)])
+def test_strided_bwd(m, N, d, H, H_kv):
+    mm = dict(m, global_idx=tuple(g for g in m.get("global_idx", ()) if g < N))
+    run_bwd_extra(1, H, H_kv, N, d, mm, seed=N + d + m["stride"] + 1)
+
+
+@pytest.mark.parametrize("ci", range(len(RANDOM)))
+@pytest.mark.parametrize("N,d,H,H_kv", [(700, 128, 4, 2), (333, 64, 2, 1), (40, 64, 2, 2)])
+def test_random_blocks_bwd(ci, N, d, H, H_kv):
+    m, r, extra = RANDOM[ci]
+    mm = dict(m, global_idx=tuple(g for g in m.get("global_idx", ()) if g < N))
+    lists = rand_lists(N, m["rand_block"], r, seed=ci + N + 3, extra=extra)
+    run_bwd_extra(1, H, H_kv, N, d, mm, seed=N + ci + 2, lists=lists)
