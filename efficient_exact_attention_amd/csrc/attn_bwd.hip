@@ -93,6 +93,130 @@ __device__ __forceinline__ unsigned long long global_rows_in(const int *g, int n
 }
 
 // ---------------------------------------------------------------------------
+// Software pipeline of the dK/dV band loop (one wave per SIMD: nothing else
+// hides a wave's vector work). Iteration t runs S(t) and dP(t), then one
+// region in which the 32 MFMAs of dV += dO(t-1)^T P(t-1) and
+// dK += Q(t-1)^T dS(t-1) are issued in batches of four, each batch followed
+// by the vector work of four elements of tile t: P = exp2(S c - LSE log2 e)
+// and dS = P (dP - rowsum(dO O)). The A operands of a batch (transpose reads
+// of tile t-1's dO and Q) are read one batch ahead; the row terms of the
+// element group likewise.
+// ---------------------------------------------------------------------------
+template <class P>
+struct BwdPipe {
+    static constexpr int MB = P::MB, DB = P::DB, PVS = P::PVS;
+    static constexpr int kB = 4, kSlots = 8;
+    static constexpr int NHALF = PVS * DB;        // MFMAs per product (16 at d=128, 8 at d=64)
+    static constexpr int NB = 2 * NHALF / kB;     // batches
+    static constexpr int GPB = 4 * MB / NB;       // element groups (4 of a 32-row block) per batch
+    static_assert(GPB * NB == 4 * MB, "whole element groups per batch");
+
+    template <int I>
+    static __device__ __forceinline__ void fetch(bf16x8 (&op)[kSlots], const typename P::Lane &L, const char *ov,
+                                                 const char *qv) {
+        if constexpr (I < 2 * NHALF) {
+            constexpr int J = I % NHALF;
+            op[I % kSlots] = P::v_operand(L, I < NHALF ? ov : qv, J % DB, J / DB);
+        }
+    }
+
+    // row terms (LSE log2 e, rowsum(dO O)) of the element groups of batch B
+    template <int B>
+    static __device__ __forceinline__ void terms(f32x4 (&l4)[GPB], f32x4 (&d4)[GPB], const float *lse, const float *dl,
+                                                 int h) {
+#pragma unroll
+        for (int j = 0; j < GPB; ++j) {
+            const int gi = B * GPB + j, mb = gi / 4, g = gi % 4;
+            l4[j] = *reinterpret_cast<const f32x4 *>(&lse[32 * mb + 8 * g + 4 * h]);
+            d4[j] = *reinterpret_cast<const f32x4 *>(&dl[32 * mb + 8 * g + 4 * h]);
+        }
+    }
+
+    template <bool MM, bool VA, bool EDGE, int B>
+    static __device__ __forceinline__ void run(f32x16 (&dv)[DB], f32x16 (&dk)[DB], const typename P::PFrag &pp,
+                                               const typename P::PFrag &pd, f32x16 (&s)[MB], f32x16 (&dp)[MB],
+                                               const typename P::Lane &L, const char *ov, const char *qv,
+                                               bf16x8 (&op)[kSlots], f32x4 (&l4)[GPB], f32x4 (&d4)[GPB],
+                                               const float *lse, const float *dl, float c, int h, int q0, int qlo,
+                                               int qhi) {
+        if constexpr (B < NB) {
+            f32x4 nl4[GPB], nd4[GPB];
+            if constexpr (MM && B + 1 < NB) {
+                fetch<kB * (B + 1) + 0>(op, L, ov, qv);
+                fetch<kB * (B + 1) + 1>(op, L, ov, qv);
+                fetch<kB * (B + 1) + 2>(op, L, ov, qv);
+                fetch<kB * (B + 1) + 3>(op, L, ov, qv);
+            }
+            if constexpr (VA && B + 1 < NB) terms<B + 1>(nl4, nd4, lse, dl, h);
+            if constexpr ((MM || VA) && B + 1 < NB) __builtin_amdgcn_sched_barrier(0);
+            if constexpr (MM) {
+#pragma unroll
+                for (int u = 0; u < kB; ++u) {
+                    const int I = kB * B + u, J = I % NHALF, st = J / DB, db = J % DB;
+                    if (I < NHALF) dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[I % kSlots], pp.x[st], dv[db], 0, 0, 0);
+                    else dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[I % kSlots], pd.x[st], dk[db], 0, 0, 0);
+                }
+            }
+            if constexpr (VA) {
+#pragma unroll
+                for (int j = 0; j < GPB; ++j) {
+                    const int gi = B * GPB + j, mb = gi / 4, g = gi % 4;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int r = 4 * g + e;
+                        float p = fast_exp2(__builtin_fmaf(s[mb][r], c, -l4[j][e]));
+                        if constexpr (EDGE) {
+                            const int i = q0 + 32 * mb + acc_row(r, h);
+                            p = ((i >= qlo) & (i <= qhi)) ? p : 0.f;
+                        }
+                        s[mb][r] = p;
+                        dp[mb][r] = p * (dp[mb][r] - d4[j][e]);
+                    }
+                }
+            }
+            if constexpr (MM && VA) {
+                constexpr int NV = GPB * 4 * (EDGE ? 7 : 4) / kB;   // per element: fma, exp, sub, mul (+ mask)
+#pragma unroll
+                for (int u = 0; u < kB; ++u) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x402, NV, 0);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (VA && B + 1 < NB) {
+#pragma unroll
+                for (int j = 0; j < GPB; ++j) {
+                    l4[j] = nl4[j];
+                    d4[j] = nd4[j];
+                }
+            }
+            run<MM, VA, EDGE, B + 1>(dv, dk, pp, pd, s, dp, L, ov, qv, op, l4, d4, lse, dl, c, h, q0, qlo, qhi);
+        }
+    }
+
+    // MM: the dV/dK MFMAs of the previous tile; VA: the vector work of this
+    // tile (S, dP in s, dp become P, dS in place).
+    template <bool MM, bool VA, bool EDGE>
+    static __device__ __forceinline__ void region(f32x16 (&dv)[DB], f32x16 (&dk)[DB], const typename P::PFrag &pp,
+                                                  const typename P::PFrag &pd, f32x16 (&s)[MB], f32x16 (&dp)[MB],
+                                                  const typename P::Lane &L, const char *ov, const char *qv,
+                                                  const float *lse, const float *dl, float c, int h, int q0, int qlo,
+                                                  int qhi) {
+        bf16x8 op[kSlots];
+        f32x4 l4[GPB], d4[GPB];
+        if constexpr (MM) {
+            fetch<0>(op, L, ov, qv);
+            fetch<1>(op, L, ov, qv);
+            fetch<2>(op, L, ov, qv);
+            fetch<3>(op, L, ov, qv);
+        }
+        if constexpr (VA) terms<0>(l4, d4, lse, dl, h);
+        __builtin_amdgcn_sched_barrier(0);
+        run<MM, VA, EDGE, 0>(dv, dk, pp, pd, s, dp, L, ov, qv, op, l4, d4, lse, dl, c, h, q0, qlo, qhi);
+    }
+};
+
+// ---------------------------------------------------------------------------
 // dK, dV: keys stationary, query tiles streamed.
 // BWD_BAND / BWD_BAND_GL: one workgroup per (K/V head, [residue class,] key
 //   tile); BWD_BAND_GL adds, per query head, the gathered tile of global rows
@@ -257,56 +381,157 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_dkdv(const BwdParams prm) {
         P::pv(dk, pd, L, qv);   // dK^T += Q^T dS
     };
 
-    auto step = [&](int t, const char *qk, const char *qv, const char *ok, const char *ov, char *nqk, char *nqv,
-                    char *nok, char *nov, int sb) __attribute__((always_inline)) {
-        const bool more = t + 1 < T;
-        float nl2 = 0.f, ndl = 0.f;
-        if (more) {
-            issue(t + 1, nqk, nqv, nok, nov);
-            row_terms(t + 1, nl2, ndl);
-        }
-        const int q0 = tile_of(t) * BQ;
-        const int q1 = imin(N - 1, q0 + BQ - 1);
-        if constexpr (MODE == BWD_GSET) {
-            // set S2: rows outside the key's band, not global, causal cut
-            if (wave_active) {
-                const unsigned long long gm = global_rows_in(s_g, ng, q0);
-                tile_products(qk, qv, ok, ov, sb, TILE_EDGE, [&](int r) { return q0 + r; },
-                              [&](int i) {
-                                  return kvalid & (i < N) & ((i < qlo) | (i > qhi)) &
-                                         ((prm.causal == 0) | (i >= key)) & !((gm >> (i - q0)) & 1ull);
-                              });
+    // The split pass over global columns and the extra-rule instance (whose
+    // extra code does not fit beside the pipeline's registers) keep the
+    // unpipelined loop.
+    if constexpr (MODE == BWD_GSET || XT) {
+        auto step = [&](int t, const char *qk, const char *qv, const char *ok, const char *ov, char *nqk, char *nqv,
+                        char *nok, char *nov, int sb) __attribute__((always_inline)) {
+            const bool more = t + 1 < T;
+            float nl2 = 0.f, ndl = 0.f;
+            if (more) {
+                issue(t + 1, nqk, nqv, nok, nov);
+                row_terms(t + 1, nl2, ndl);
             }
-        } else {
+            const int q0 = tile_of(t) * BQ;
+            if constexpr (MODE == BWD_GSET) {
+                // set S2: rows outside the key's band, not global, causal cut
+                if (wave_active) {
+                    const unsigned long long gm = global_rows_in(s_g, ng, q0);
+                    tile_products(qk, qv, ok, ov, sb, TILE_EDGE, [&](int r) { return q0 + r; },
+                                  [&](int i) {
+                                      return kvalid & (i < N) & ((i < qlo) | (i > qhi)) &
+                                             ((prm.causal == 0) | (i >= key)) & !((gm >> (i - q0)) & 1ull);
+                                  });
+                }
+            } else {
+                const int q1 = imin(N - 1, q0 + BQ - 1);
+                int cl = wave_active ? classify(band, q0, q1, k0w, k1w) : TILE_SKIP;
+                if (cl == TILE_FULL && q0 + BQ - 1 >= N) cl = TILE_EDGE;
+                if (cl != TILE_SKIP)
+                    tile_products(qk, qv, ok, ov, sb, cl, [&](int r) { return q0 + r; },
+                                  [&](int i) { return (i >= qlo) & (i <= qhi); });
+            }
+            if (more && tid < BQ) {
+                s_lse[sb ^ 1][tid] = nl2;
+                s_dl[sb ^ 1][tid] = ndl;
+            }
+            wait_vmem();
+            __syncthreads();
+        };
+        if (T > 0) {
+            issue(0, qk0, qv0, ok0, ov0);
+            float l2, dl;
+            row_terms(0, l2, dl);
+            if (tid < BQ) {
+                s_lse[0][tid] = l2;
+                s_dl[0][tid] = dl;
+            }
+            wait_vmem();
+            __syncthreads();
+        }
+        for (int t = 0; t < T; t += 2) {
+            step(t, qk0, qv0, ok0, ov0, qk1, qv1, ok1, ov1, 0);
+            if (t + 1 >= T) break;
+            step(t + 1, qk1, qv1, ok1, ov1, qk0, qv0, ok0, ov0, 1);
+        }
+    } else {
+        // band tiles, software-pipelined (BwdPipe). Row layouts of tile t
+        // (qk, ok) are copied one iteration ahead; its transposed layouts
+        // (qv, ov), read by the dV/dK MFMAs one iteration later, are copied
+        // during iteration t. Both pairs double-buffered.
+        typedef BwdPipe<P> BP;
+        typename P::PFrag pp, pd;   // P and dS of the previous active tile
+        bool act_prev = false;
+        auto issue_rows = [&](int t, char *qk, char *ok) __attribute__((always_inline)) {
+            const long long bh = head_of(t);
+            const int q0 = tile_of(t) * BQ;
+            const uint16_t *qh = static_cast<const uint16_t *>(prm.q) + bh * prm.head_stride + cls_off;
+            const uint16_t *gh = static_cast<const uint16_t *>(prm.dout) + bh * prm.head_stride + cls_off;
+            P::issue_k(L, qh, N, qk, q0, dil);
+            P::issue_k(L, gh, N, ok, q0, dil);
+        };
+        auto issue_tr = [&](int t, char *qv, char *ov) __attribute__((always_inline)) {
+            const long long bh = head_of(t);
+            const int q0 = tile_of(t) * BQ;
+            const uint16_t *qh = static_cast<const uint16_t *>(prm.q) + bh * prm.head_stride + cls_off;
+            const uint16_t *gh = static_cast<const uint16_t *>(prm.dout) + bh * prm.head_stride + cls_off;
+            P::issue_v(L, qh, N, qv, q0, dil);
+            P::issue_v(L, gh, N, ov, q0, dil);
+        };
+        auto pstep = [&](int t, const char *qk, const char *ok, char *nqk, char *nok, char *qv_t, char *ov_t,
+                         const char *qv_p, const char *ov_p, int sb) __attribute__((always_inline)) {
+            const bool more = t + 1 < T;
+            float nl2 = 0.f, ndl = 0.f;
+            if (more) {
+                issue_rows(t + 1, nqk, nok);
+                row_terms(t + 1, nl2, ndl);
+            }
+            issue_tr(t, qv_t, ov_t);
+            const int q0 = tile_of(t) * BQ;
+            const int q1 = imin(N - 1, q0 + BQ - 1);
             int cl = wave_active ? classify(band, q0, q1, k0w, k1w) : TILE_SKIP;
             if (cl == TILE_FULL && q0 + BQ - 1 >= N) cl = TILE_EDGE;
-            if (cl != TILE_SKIP)
-                tile_products(qk, qv, ok, ov, sb, cl, [&](int r) { return q0 + r; },
-                              [&](int i) { return (i >= qlo) & (i <= qhi); });
+            const bool act = cl != TILE_SKIP;
+            f32x16 s[MB], dp[MB];
+            if (act) {
+                P::scores(s, kf, L, qk);    // S  = Q K^T : lane = key, registers = query rows
+                P::scores(dp, vf, L, ok);   // dP = dO V^T
+            }
+            const float *lr = s_lse[sb], *dr = s_dl[sb];
+            if (act_prev) {
+                if (act) {
+                    if (cl == TILE_EDGE)
+                        BP::template region<true, true, true>(dv, dk, pp, pd, s, dp, L, ov_p, qv_p, lr, dr, c, h, q0, qlo, qhi);
+                    else
+                        BP::template region<true, true, false>(dv, dk, pp, pd, s, dp, L, ov_p, qv_p, lr, dr, c, h, q0, qlo, qhi);
+                } else {
+                    BP::template region<true, false, false>(dv, dk, pp, pd, s, dp, L, ov_p, qv_p, lr, dr, c, h, q0, qlo, qhi);
+                }
+            } else if (act) {
+                if (cl == TILE_EDGE)
+                    BP::template region<false, true, true>(dv, dk, pp, pd, s, dp, L, ov_p, qv_p, lr, dr, c, h, q0, qlo, qhi);
+                else
+                    BP::template region<false, true, false>(dv, dk, pp, pd, s, dp, L, ov_p, qv_p, lr, dr, c, h, q0, qlo, qhi);
+            }
+            if (act) {
+                P::pack_p(pp, s);
+                P::pack_p(pd, dp);
+            }
+            act_prev = act;
+            if (more && tid < BQ) {
+                s_lse[sb ^ 1][tid] = nl2;
+                s_dl[sb ^ 1][tid] = ndl;
+            }
+            wait_vmem();
+            __syncthreads();
+        };
+        if (T > 0) {
+            issue_rows(0, qk0, ok0);
+            float l2, dl;
+            row_terms(0, l2, dl);
+            if (tid < BQ) {
+                s_lse[0][tid] = l2;
+                s_dl[0][tid] = dl;
+            }
+            wait_vmem();
+            __syncthreads();
         }
-        if (more && tid < BQ) {
-            s_lse[sb ^ 1][tid] = nl2;
-            s_dl[sb ^ 1][tid] = ndl;
+        for (int t = 0; t < T; t += 2) {
+            pstep(t, qk0, ok0, qk1, ok1, qv0, ov0, qv1, ov1, 0);
+            if (t + 1 >= T) break;
+            pstep(t + 1, qk1, ok1, qk0, ok0, qv1, ov1, qv0, ov0, 1);
         }
-        wait_vmem();
-        __syncthreads();
-    };
-
-    if (T > 0) {
-        issue(0, qk0, qv0, ok0, ov0);
-        float l2, dl;
-        row_terms(0, l2, dl);
-        if (tid < BQ) {
-            s_lse[0][tid] = l2;
-            s_dl[0][tid] = dl;
+        // the last active tile's dV/dK products (its transposed layouts were
+        // copied during the last iteration)
+        if (act_prev) {
+            f32x16 s[MB], dp[MB];
+            if ((T - 1) & 1)
+                BP::template region<true, false, false>(dv, dk, pp, pd, s, dp, L, ov1, qv1, s_lse[0], s_dl[0], c, h, 0, 0, 0);
+            else
+                BP::template region<true, false, false>(dv, dk, pp, pd, s, dp, L, ov0, qv0, s_lse[0], s_dl[0], c, h, 0, 0, 0);
         }
-        wait_vmem();
-        __syncthreads();
-    }
-    for (int t = 0; t < T; t += 2) {
-        step(t, qk0, qv0, ok0, ov0, qk1, qv1, ok1, ov1, 0);
-        if (t + 1 >= T) break;
-        step(t + 1, qk1, qv1, ok1, ov1, qk0, qv0, ok0, ov0, 1);
+        __syncthreads();   // every wave is done with the tile buffers
     }
 
     if constexpr (MODE == BWD_BAND_GL) {
