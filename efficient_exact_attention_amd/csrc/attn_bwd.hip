@@ -662,6 +662,88 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_dkdv(const BwdParams prm) {
 }
 
 // ---------------------------------------------------------------------------
+// Software pipeline of the dQ band loop, as for dK/dV: iteration t runs
+// S^T(t) and dP^T(t), then a region in which the MFMAs of
+// dQ^T += K(t-1)^T dS^T(t-1) are issued in batches of four, each followed by
+// the vector work of a share of tile t's elements (the row's LSE and row
+// term are per lane here).
+// ---------------------------------------------------------------------------
+template <class P>
+struct DqPipe {
+    static constexpr int MB = P::MB, DB = P::DB, PVS = P::PVS;
+    static constexpr int kB = 4, kSlots = 8;
+    static constexpr int NM = PVS * DB;           // MFMAs (16 at d=128, 8 at d=64)
+    static constexpr int NB = NM / kB;            // batches
+    static constexpr int EPB = 16 * MB / NB;      // elements per batch
+    static_assert(EPB * NB == 16 * MB, "whole element shares per batch");
+
+    template <int I>
+    static __device__ __forceinline__ void fetch(bf16x8 (&op)[kSlots], const typename P::Lane &L, const char *kv) {
+        if constexpr (I < NM) op[I % kSlots] = P::v_operand(L, kv, I % DB, I / DB);
+    }
+
+    template <bool MM, bool VA, bool EDGE, int B>
+    static __device__ __forceinline__ void run(f32x16 (&dq)[DB], const typename P::PFrag &pd, f32x16 (&s)[MB],
+                                               f32x16 (&dp)[MB], const typename P::Lane &L, const char *kv,
+                                               bf16x8 (&op)[kSlots], float c, float l2, float dl, int h, int k0,
+                                               int lo, int hi) {
+        if constexpr (B < NB) {
+            if constexpr (MM && B + 1 < NB) {
+                fetch<kB * (B + 1) + 0>(op, L, kv);
+                fetch<kB * (B + 1) + 1>(op, L, kv);
+                fetch<kB * (B + 1) + 2>(op, L, kv);
+                fetch<kB * (B + 1) + 3>(op, L, kv);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            if constexpr (MM) {
+#pragma unroll
+                for (int u = 0; u < kB; ++u) {
+                    const int I = kB * B + u, st = I / DB, db = I % DB;
+                    dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[I % kSlots], pd.x[st], dq[db], 0, 0, 0);
+                }
+            }
+            if constexpr (VA) {
+#pragma unroll
+                for (int e = B * EPB; e < (B + 1) * EPB; ++e) {
+                    const int mb = e / 16, r = e % 16;
+                    float p = fast_exp2(__builtin_fmaf(s[mb][r], c, -l2));
+                    if constexpr (EDGE) {
+                        const int j = k0 + mb * 32 + acc_row(r, h);
+                        p = ((j >= lo) & (j <= hi)) ? p : 0.f;
+                    }
+                    dp[mb][r] = p * (dp[mb][r] - dl);
+                }
+            }
+            if constexpr (MM && VA) {
+                constexpr int NV = EPB * (EDGE ? 7 : 4) / kB;
+#pragma unroll
+                for (int u = 0; u < kB; ++u) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x402, NV, 0);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            run<MM, VA, EDGE, B + 1>(dq, pd, s, dp, L, kv, op, c, l2, dl, h, k0, lo, hi);
+        }
+    }
+
+    template <bool MM, bool VA, bool EDGE>
+    static __device__ __forceinline__ void region(f32x16 (&dq)[DB], const typename P::PFrag &pd, f32x16 (&s)[MB],
+                                                  f32x16 (&dp)[MB], const typename P::Lane &L, const char *kv, float c,
+                                                  float l2, float dl, int h, int k0, int lo, int hi) {
+        bf16x8 op[kSlots];
+        if constexpr (MM) {
+            fetch<0>(op, L, kv);
+            fetch<1>(op, L, kv);
+            fetch<2>(op, L, kv);
+            fetch<3>(op, L, kv);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        run<MM, VA, EDGE, 0>(dq, pd, s, dp, L, kv, op, c, l2, dl, h, k0, lo, hi);
+    }
+};
+
+// ---------------------------------------------------------------------------
 // dQ: query rows stationary, key tiles streamed.
 // BWD_BAND / BWD_BAND_GL: one workgroup per (query head, [residue class,]
 //   query tile); BWD_BAND_GL adds the gathered tile of global columns (set S2).
@@ -803,15 +885,70 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_dq(const BwdParams prm) {
         __syncthreads();
     };
 
-    if (kt_lo <= kt_hi) {
-        issue(kt_lo, kk0, kv0, vk0);
+    if constexpr (MODE == BWD_GSET || XT) {
+        if (kt_lo <= kt_hi) {
+            issue(kt_lo, kk0, kv0, vk0);
+            wait_vmem();
+            __syncthreads();
+            for (int kt = kt_lo; kt <= kt_hi; kt += 2) {
+                step(kt, kk0, kv0, vk0, kk1, kv1, vk1);
+                if (kt + 1 > kt_hi) break;
+                step(kt + 1, kk1, kv1, vk1, kk0, kv0, vk0);
+            }
+        }
+    } else if (kt_lo <= kt_hi) {
+        // band tiles, software-pipelined (DqPipe): the row layouts of K and V
+        // for tile t are copied one iteration ahead, the transposed layout of
+        // K (read by the dQ MFMAs one iteration later) during iteration t
+        typedef DqPipe<P> QP;
+        typename P::PFrag pd;   // dS of the previous active tile
+        bool act_prev = false;
+        auto issue_rows = [&](int kt, char *kk, char *vk) __attribute__((always_inline)) {
+            P::issue_k(L, kh, N, kk, kt * BN, dil);
+            P::issue_k(L, vh, N, vk, kt * BN, dil);
+        };
+        auto pstep = [&](int kt, const char *kk, const char *vk, char *nkk, char *nvk, char *kv_t, const char *kv_p)
+            __attribute__((always_inline)) {
+            if (kt < kt_hi) issue_rows(kt + 1, nkk, nvk);
+            P::issue_v(L, kh, N, kv_t, kt * BN, dil);
+            const int k0 = kt * BN;
+            const int cl = wave_active ? classify(band, wr0, wr1, k0, k0 + BN - 1) : TILE_SKIP;
+            const bool act = cl != TILE_SKIP;
+            f32x16 s[MB], dp[MB];
+            if (act) {
+                P::scores(s, qf, L, kk);    // S^T  = K Q^T  : lane = query row, registers = keys
+                P::scores(dp, gf, L, vk);   // dP^T = V dO^T
+            }
+            if (act_prev) {
+                if (act) {
+                    if (cl == TILE_EDGE) QP::template region<true, true, true>(dq, pd, s, dp, L, kv_p, c, l2, dl, h, k0, lo, hi);
+                    else QP::template region<true, true, false>(dq, pd, s, dp, L, kv_p, c, l2, dl, h, k0, lo, hi);
+                } else {
+                    QP::template region<true, false, false>(dq, pd, s, dp, L, kv_p, c, l2, dl, h, k0, lo, hi);
+                }
+            } else if (act) {
+                if (cl == TILE_EDGE) QP::template region<false, true, true>(dq, pd, s, dp, L, kv_p, c, l2, dl, h, k0, lo, hi);
+                else QP::template region<false, true, false>(dq, pd, s, dp, L, kv_p, c, l2, dl, h, k0, lo, hi);
+            }
+            if (act) P::pack_p(pd, dp);
+            act_prev = act;
+            wait_vmem();
+            __syncthreads();
+        };
+        issue_rows(kt_lo, kk0, vk0);
         wait_vmem();
         __syncthreads();
         for (int kt = kt_lo; kt <= kt_hi; kt += 2) {
-            step(kt, kk0, kv0, vk0, kk1, kv1, vk1);
+            pstep(kt, kk0, vk0, kk1, vk1, kv0, kv1);
             if (kt + 1 > kt_hi) break;
-            step(kt + 1, kk1, kv1, vk1, kk0, kv0, vk0);
+            pstep(kt + 1, kk1, vk1, kk0, vk0, kv1, kv0);
         }
+        if (act_prev) {   // the last active tile's dQ products
+            f32x16 s[MB], dp[MB];
+            if ((kt_hi - kt_lo) & 1) QP::template region<true, false, false>(dq, pd, s, dp, L, kv1, c, l2, dl, h, 0, 0, 0);
+            else QP::template region<true, false, false>(dq, pd, s, dp, L, kv0, c, l2, dl, h, 0, 0, 0);
+        }
+        __syncthreads();   // every wave is done with the tile buffers
     }
 
     bool row_is_g = false;
