@@ -102,6 +102,65 @@ __device__ __forceinline__ unsigned long long global_rows_in(const int *g, int n
 // of tile t-1's dO and Q) are read one batch ahead; the row terms of the
 // element group likewise.
 // ---------------------------------------------------------------------------
+// Both score products of one tile (S with the first B operand, dP with the
+// second) as one stream of MFMAs that alternates between them, so the two
+// accumulator chains hide each other's latency and are live together. The
+// A operands (row layout, from LDS) are read one batch of four ahead.
+template <class P>
+struct ScorePair {
+    static constexpr int MB = P::MB, KS = P::KS;
+    static constexpr int kB = 4, kSlots = 8;
+    static constexpr int NM = 2 * KS * MB;   // MFMAs (32 at d=128, 16 at d=64)
+    static_assert(NM % kB == 0, "whole batches");
+
+    template <int J>
+    static __device__ __forceinline__ void fetch(bf16x8 (&op)[kSlots], const typename P::Lane &L, const char *ba,
+                                                 const char *bb) {
+        if constexpr (J < NM) {
+            constexpr int I = J / 2, ks = I / MB, mb = I % MB;
+            op[J % kSlots] = *reinterpret_cast<const bf16x8 *>(((J & 1) ? bb : ba) + L.krd[ks] + mb * 32 * P::ROWB);
+        }
+    }
+    template <int B>
+    static __device__ __forceinline__ void run(f32x16 (&sa)[MB], f32x16 (&sb)[MB], const typename P::QFrag &fa,
+                                               const typename P::QFrag &fb, const typename P::Lane &L, const char *ba,
+                                               const char *bb, bf16x8 (&op)[kSlots]) {
+        if constexpr (B < NM / kB) {
+            if constexpr (B + 1 < NM / kB) {
+                fetch<kB * (B + 1) + 0>(op, L, ba, bb);
+                fetch<kB * (B + 1) + 1>(op, L, ba, bb);
+                fetch<kB * (B + 1) + 2>(op, L, ba, bb);
+                fetch<kB * (B + 1) + 3>(op, L, ba, bb);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (int u = 0; u < kB; ++u) {
+                const int J = kB * B + u, I = J / 2, ks = I / MB, mb = I % MB;
+                if (J & 1) sb[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[J % kSlots], fb.x[ks], sb[mb], 0, 0, 0);
+                else sa[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[J % kSlots], fa.x[ks], sa[mb], 0, 0, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            run<B + 1>(sa, sb, fa, fb, L, ba, bb, op);
+        }
+    }
+    static __device__ __forceinline__ void scores(f32x16 (&sa)[MB], f32x16 (&sb)[MB], const typename P::QFrag &fa,
+                                                  const typename P::QFrag &fb, const typename P::Lane &L,
+                                                  const char *ba, const char *bb) {
+        bf16x8 op[kSlots];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            sa[mb] = f32x16{};
+            sb[mb] = f32x16{};
+        }
+        fetch<0>(op, L, ba, bb);
+        fetch<1>(op, L, ba, bb);
+        fetch<2>(op, L, ba, bb);
+        fetch<3>(op, L, ba, bb);
+        __builtin_amdgcn_sched_barrier(0);
+        run<0>(sa, sb, fa, fb, L, ba, bb, op);
+    }
+};
+
 template <class P>
 struct BwdPipe {
     static constexpr int MB = P::MB, DB = P::DB, PVS = P::PVS;
@@ -474,9 +533,16 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_dkdv(const BwdParams prm) {
             if (cl == TILE_FULL && q0 + BQ - 1 >= N) cl = TILE_EDGE;
             const bool act = cl != TILE_SKIP;
             f32x16 s[MB], dp[MB];
+            // S = Q K^T and dP = dO V^T (lane = key, registers = query rows);
+            // one after the other with global tokens, where the registers
+            // for both chains at once run out
             if (act) {
-                P::scores(s, kf, L, qk);    // S  = Q K^T : lane = key, registers = query rows
-                P::scores(dp, vf, L, ok);   // dP = dO V^T
+                if constexpr (MODE == BWD_BAND_GL) {
+                    P::scores(s, kf, L, qk);
+                    P::scores(dp, vf, L, ok);
+                } else {
+                    ScorePair<P>::scores(s, dp, kf, vf, L, qk, ok);
+                }
             }
             const float *lr = s_lse[sb], *dr = s_dl[sb];
             if (act_prev) {
@@ -915,10 +981,8 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_dq(const BwdParams prm) {
             const int cl = wave_active ? classify(band, wr0, wr1, k0, k0 + BN - 1) : TILE_SKIP;
             const bool act = cl != TILE_SKIP;
             f32x16 s[MB], dp[MB];
-            if (act) {
-                P::scores(s, qf, L, kk);    // S^T  = K Q^T  : lane = query row, registers = keys
-                P::scores(dp, gf, L, vk);   // dP^T = V dO^T
-            }
+            // S^T = K Q^T and dP^T = V dO^T (lane = query row, registers = keys)
+            if (act) ScorePair<P>::scores(s, dp, qf, gf, L, kk, vk);
             if (act_prev) {
                 if (act) {
                     if (cl == TILE_EDGE) QP::template region<true, true, true>(dq, pd, s, dp, L, kv_p, c, l2, dl, h, k0, lo, hi);
