@@ -334,7 +334,7 @@ int fwd_impl(const void *q, const void *k, const void *v, void *out, float *lse,
     const std::vector<int> &G = m.G;
 
     const long long BH = (long long)B * H;
-    const int bm = eea::band_tile_bm(d, dtype == ATTN_F32, m.band.block, m.extra());
+    const int bm = eea::band_tile_bm(d, dtype == ATTN_F32, m.band.block, m.extra(), m.band.wl, m.band.wr, m.dil);
     // query tiles per residue class (the longest class: ceil(N / dil) rows)
     const long long nqt = ((N + (long long)m.dil - 1) / m.dil + bm - 1) / bm;
     if (BH > INT_MAX || BH * m.dil * nqt > INT_MAX)

@@ -109,7 +109,8 @@ int bwd_tile_k(int d);      // keys per dK/dV workgroup
 
 // Tile shapes chosen per (d, dtype).
 int tile_bm(int d, int f32);
-int band_tile_bm(int d, int f32, int block, int extra);   // query rows per band workgroup for this mask
+int band_tile_bm(int d, int f32, int block, int extra, int wl, int wr, int dil);   // query rows per band workgroup
+bool band_is_narrow(int wl, int wr, int dil);   // normalised band short enough for the four-wave band instance
 int tile_bn(int d, int f32);
 
 // Enqueue the band pass (every query tile), then, when n_global > 0, the

@@ -6,6 +6,7 @@ budget at 512 threads, so a small change to shared code can push it over
 (its throughput then drops about threefold while every result stays right).
 This check compiles the device code to assembly on the CPU and reads the
 code-object metadata, so it catches that before any GPU run."""
+import re
 import shutil
 
 import pytest
@@ -33,9 +34,22 @@ def test_no_vector_register_spills(resources):
     assert not bad, bad
 
 
+def _band_flags(name):
+    """(DIL, BLK, XT, NAR) of a mangled fwd_band_bf16<D, DIL, BLK, XT, NAR> name."""
+    args = name.split("fwd_band_bf16I", 1)[1]
+    return tuple(f == "1" for f in re.findall(r"Lb([01])E", args)[:4])
+
+
 def test_band_kernel_fits_two_waves_per_simd(resources):
-    """The 512-thread band instances (plain and dilated) keep within 256
-    registers, the budget of two waves per SIMD."""
+    """The band instances that run two waves per SIMD (plain and dilated at
+    512 threads, narrow at 256 threads with two workgroups per CU) keep
+    within 256 registers."""
+    seen = 0
     for k, v in resources.items():
-        if "fwd_band_bf16" in k and "Lb0ELb0EEE" in k:   # BLK = XT = false: the 512-thread instances
+        if "fwd_band_bf16" not in k:
+            continue
+        dil, blk, xt, nar = _band_flags(k)
+        if not blk and not xt:
+            seen += 1
             assert v["vgpr"] + v["agpr"] <= 256, (k, v)
+    assert seen == 6   # d = 64, 128 x (plain, dilated, narrow)
