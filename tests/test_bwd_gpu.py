@@ -89,15 +89,17 @@ def test_bwd_small(mask, N, d):
 
 @pytest.mark.parametrize("H,H_kv", [(8, 2), (8, 1), (6, 3)])
 @pytest.mark.parametrize("mask", ["causal", "band50"])
-def test_bwd_gqa(H, H_kv, mask):
+@pytest.mark.parametrize("d", [64, 128])
+def test_bwd_gqa(H, H_kv, mask, d):
     m = MASKS[mask]
-    inputs, grads = run_bwd(1, H, H_kv, 700, 128, m, seed=H + H_kv)
+    inputs, grads = run_bwd(1, H, H_kv, 700, d, m, seed=H + H_kv + d)
     check_bwd(inputs, grads, dict(m, global_idx=()))
 
 
-def test_bwd_causal_long():
+@pytest.mark.parametrize("d", [64, 128])
+def test_bwd_causal_long(d):
     m = MASKS["causal"]
-    inputs, grads = run_bwd(1, 2, 2, 4097, 128, m, seed=5)
+    inputs, grads = run_bwd(1, 2, 2, 4097, d, m, seed=5 + d)
     check_bwd(inputs, grads, dict(m, global_idx=()))
 
 

@@ -53,3 +53,19 @@ def test_band_kernel_fits_two_waves_per_simd(resources):
             seen += 1
             assert v["vgpr"] + v["agpr"] <= 256, (k, v)
     assert seen == 6   # d = 64, 128 x (plain, dilated, narrow)
+
+
+def test_two_wave_backward_instances_fit(resources):
+    """At d = 64 every dQ instance, and the dK/dV instances other than the
+    one with gathered global rows (mode 1, with or without extra tiles), run
+    two waves per SIMD: 256 registers each."""
+    seen = 0
+    for k, v in resources.items():
+        m = re.search(r"bwd_(dq|dkdv)ILi64ELb([01])ELi([012])ELb([01])E", k)
+        if not m:
+            continue
+        kind, mode = m.group(1), int(m.group(3))
+        if kind == "dq" or mode != 1:
+            seen += 1
+            assert v["vgpr"] + v["agpr"] <= 256, (k, v)
+    assert seen == 8   # dq: plain, dilated, global, global + extra tiles, split pass; dkdv: plain, dilated, split pass
