@@ -303,8 +303,12 @@ int attn_plan_stats_masked(int N, const attn_mask *mask, int bm, int bn,
                            long long *tiles_edge);
 
 /*
- * attn_tile_shape - the tile shape (query rows, keys) the forward kernel uses
- * for head size d and element type dtype. Host-only, no HIP call.
+ * attn_tile_shape - the tile shape (query rows per workgroup, keys per tile)
+ * of the forward band kernel for head size d and element type dtype, with an
+ * unbounded window (plain or causal). bf16 calls whose band is bounded on
+ * both sides and at most 4096 keys wide, or that use the block-sparse,
+ * strided or random-block rules, run 128-row workgroups with the same key
+ * tiles. Host-only, no HIP call.
  */
 int attn_tile_shape(int d, int dtype, int *bm, int *bn);
 
