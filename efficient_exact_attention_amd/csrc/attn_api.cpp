@@ -530,7 +530,7 @@ int bwd_impl(const void *q, const void *k, const void *v, const void *out, const
     const eea::Band band = m.band;
 
     const long long BH = (long long)B * H;
-    const int bq = eea::bwd_tile_q(d), bk = eea::bwd_tile_k(d);
+    const int bq = eea::bwd_tile_q(d, m.ng == 0 && !m.extra()), bk = eea::bwd_tile_k(d);
     // tiles per residue class (the longest class: ceil(N / dil) rows)
     const long long Nc = (N + (long long)m.dil - 1) / m.dil;
     const long long nqt = (Nc + bq - 1) / bq, nkt = (Nc + bk - 1) / bk;

@@ -94,6 +94,13 @@ template <int D, int MODE, bool XT>
 constexpr int dkdv_waves() { return (D == 64 && MODE != BWD_BAND_GL && !XT) ? 2 : 1; }
 template <int D>
 constexpr int dq_waves() { return D == 64 ? 2 : 1; }
+// Threads of a dQ instance. At d = 128 the band instance (no global tokens,
+// no extra tiles) runs eight waves, 256 rows per workgroup, two per SIMD,
+// with the unpipelined loop (it fits 256 registers; the pipelined one does
+// not): 14 % less dQ time on a long causal head than four waves at one per
+// SIMD with the pipelined loop.
+template <int D, int MODE, bool XT>
+constexpr int dq_threads() { return (D == 128 && MODE == BWD_BAND && !XT) ? 512 : kBwdThreads; }
 
 // Bit r set when row q0 + r (r < 64) is a global position.
 __device__ __forceinline__ unsigned long long global_rows_in(const int *g, int ng, int q0) {
@@ -832,8 +839,8 @@ struct DqPipe {
 // XT (with BWD_BAND_GL): the keys this workgroup's rows see by the
 // log-spaced strided or the random-block rule, as extra key tiles.
 template <int D, bool DIL, int MODE, bool XT = false>
-__global__ void __launch_bounds__(kBwdThreads, dq_waves<D>()) bwd_dq(const BwdParams prm) {
-    typedef Bf16Path<D, kBwdThreads> P;
+__global__ void __launch_bounds__((dq_threads<D, MODE, XT>()), dq_waves<D>()) bwd_dq(const BwdParams prm) {
+    typedef Bf16Path<D, dq_threads<D, MODE, XT>()> P;
     constexpr int BN = P::BN;                 // keys per streamed tile
     constexpr int BM = 32 * P::NW;            // query rows per workgroup
     constexpr int MB = P::MB, DB = P::DB;
@@ -847,7 +854,8 @@ __global__ void __launch_bounds__(kBwdThreads, dq_waves<D>()) bwd_dq(const BwdPa
     __shared__ __attribute__((aligned(1024))) char vk1[P::TILE_BYTES];
     __shared__ int s_g[kMaxGlobal];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: the row bounds stay scalar
     const int ln = lane & 31, h = lane >> 5;
     const int ng = MODE == BWD_BAND ? 0 : prm.n_global;
     if constexpr (MODE != BWD_BAND) {
@@ -964,7 +972,7 @@ __global__ void __launch_bounds__(kBwdThreads, dq_waves<D>()) bwd_dq(const BwdPa
         __syncthreads();
     };
 
-    if constexpr (MODE == BWD_GSET || XT) {
+    if constexpr (MODE == BWD_GSET || XT || dq_threads<D, MODE, XT>() == 512) {
         if (kt_lo <= kt_hi) {
             issue(kt_lo, kk0, kv0, vk0);
             wait_vmem();
@@ -1109,6 +1117,17 @@ __global__ void __launch_bounds__(kBwdThreads, dq_waves<D>()) bwd_dq(const BwdPa
         }
     }
 
+    if constexpr (MODE == BWD_BAND) {
+        // the row again, from the lane id and the wave-uniform wave index:
+        // keeping row and valid live across the tile loop costs registers
+        // the eight-wave instance does not have
+        const int lane2 = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+        const int row2 = q0 + wave * 32 + (lane2 & 31);
+        if (row2 >= N) return;
+        uint16_t *dqh = static_cast<uint16_t *>(prm.dq) + (long long)bh * prm.head_stride + cls_off;
+        P::store_out(dqh, row2 * dil, dq, prm.scale, lane2 >> 5);
+        return;
+    }
     if (!valid) return;
     if constexpr (MODE == BWD_GSET) {   // fp32 partials: [B*H][ng][chunks][D] (dQ^T unscaled)
         float *dst = prm.part_q + (((long long)bh * ng + (wave * 32 + ln)) * prm.gchunks_q + chunk) * D;
@@ -1159,7 +1178,7 @@ __global__ void __launch_bounds__(64) bwd_merge_dkdv(const BwdParams prm) {
     }
 }
 
-int bwd_tile_q(int d) { (void)d; return 32 * (kBwdThreads / 64); }
+int bwd_tile_q(int d, int band_only) { return 32 * ((d == 128 && band_only) ? 512 : kBwdThreads) / 64; }
 int bwd_tile_k(int d) { (void)d; return 32 * (kBwdThreads / 64); }
 
 // Chunks of the split passes: a few hundred workgroups in all.
@@ -1200,9 +1219,9 @@ static hipError_t launch_bwd_impl(const BwdParams &p0, hipStream_t stream) {
     else if (p.n_global > 0)
         hipLaunchKernelGGL((bwd_dq<D, false, BWD_BAND_GL>), dim3(qgrid), dim3(kBwdThreads), 0, stream, p);
     else if (p.dil > 1)
-        hipLaunchKernelGGL((bwd_dq<D, true, BWD_BAND>), dim3(qgrid), dim3(kBwdThreads), 0, stream, p);
+        hipLaunchKernelGGL((bwd_dq<D, true, BWD_BAND>), dim3(qgrid), dim3(dq_threads<D, BWD_BAND, false>()), 0, stream, p);
     else
-        hipLaunchKernelGGL((bwd_dq<D, false, BWD_BAND>), dim3(qgrid), dim3(kBwdThreads), 0, stream, p);
+        hipLaunchKernelGGL((bwd_dq<D, false, BWD_BAND>), dim3(qgrid), dim3(dq_threads<D, BWD_BAND, false>()), 0, stream, p);
     e = hipGetLastError();
     if (e != hipSuccess || p.n_global == 0) return e;
     // split passes over the global rows and columns, then their merges

@@ -104,7 +104,7 @@ constexpr int kDecRows = 128;        // query rows per decode workgroup (four wa
 constexpr int kDecMaxChunks = 256;   // most chunks one row is split into
 hipError_t launch_decode(const DecParams &p, int d, hipStream_t stream);
 int decode_chunks(int B, int H_kv, int nrg, int S, int Nq, int win, int rolling);
-int bwd_tile_q(int d);      // query rows per dQ workgroup
+int bwd_tile_q(int d, int band_only);   // query rows per dQ workgroup (band_only: no global tokens, no extra rule)
 int bwd_tile_k(int d);      // keys per dK/dV workgroup
 
 // Tile shapes chosen per (d, dtype).

@@ -56,16 +56,18 @@ def test_band_kernel_fits_two_waves_per_simd(resources):
 
 
 def test_two_wave_backward_instances_fit(resources):
-    """At d = 64 every dQ instance, and the dK/dV instances other than the
-    one with gathered global rows (mode 1, with or without extra tiles), run
-    two waves per SIMD: 256 registers each."""
+    """Backward instances that run two waves per SIMD keep within 256
+    registers: at d = 64 every dQ instance and the dK/dV instances other than
+    the one with gathered global rows (mode 1, with or without extra tiles);
+    at d = 128 the eight-wave dQ band instances (mode 0, plain and dilated)."""
     seen = 0
     for k, v in resources.items():
-        m = re.search(r"bwd_(dq|dkdv)ILi64ELb([01])ELi([012])ELb([01])E", k)
+        m = re.search(r"bwd_(dq|dkdv)ILi(64|128)ELb([01])ELi([012])ELb([01])E", k)
         if not m:
             continue
-        kind, mode = m.group(1), int(m.group(3))
-        if kind == "dq" or mode != 1:
+        kind, d, mode = m.group(1), int(m.group(2)), int(m.group(4))
+        two = (kind == "dq" or mode != 1) if d == 64 else (kind == "dq" and mode == 0)
+        if two:
             seen += 1
             assert v["vgpr"] + v["agpr"] <= 256, (k, v)
-    assert seen == 8   # dq: plain, dilated, global, global + extra tiles, split pass; dkdv: plain, dilated, split pass
+    assert seen == 10   # d=64 dq x5, d=64 dkdv x3, d=128 dq band x2
