@@ -97,6 +97,18 @@ def test_causal_globals_bf16_d128():
     check(w, o, l, all_heads(w), np.arange(3000), qkv)
 
 
+@pytest.mark.parametrize("wl,wr,causal", [(4095, 0, 1), (4096, 0, 1), (2047, 2048, 0), (2048, 2048, 0)])
+def test_narrow_band_threshold(wl, wr, causal):
+    """Bands of at most 4096 keys run the four-wave band instance, wider ones
+    the eight-wave one: both sides of the threshold, causal and two-sided,
+    on a ragged N; every row of one head checked."""
+    w = W.random_workload(f"nb-{wl}-{wr}-{causal}", 1, 2, 6001, 64, causal=causal, win_left=wl, win_right=wr,
+                          seed=wl + wr)
+    qkv = W.make_qkv(w)
+    o, l = run_gpu(w, qkv)
+    check(w, o, l, [(0, 1)], np.arange(w.N), qkv)
+
+
 # ---- the benchmark workloads at full size ---------------------------------------------
 
 def test_c1_fp32_all_rows():
