@@ -16,9 +16,9 @@
 //    of every query head that reads this K/V head, accumulating
 //    dV^T += dO^T P and dK^T += Q^T dS in registers: grouped-query heads are
 //    summed here, with no atomics.
-//  * bwd_dq: one workgroup per (query head, 128 rows); each wave keeps its 32
-//    rows' Q and dO as operands and walks the visible 64-key tiles,
-//    accumulating dQ^T += K^T dS^T.
+//  * bwd_dq: one workgroup per (query head, 128 rows; 256 for the d = 128
+//    band instance); each wave keeps its 32 rows' Q and dO as operands and
+//    walks the visible 64-key tiles, accumulating dQ^T += K^T dS^T.
 // All products use v_mfma_f32_32x32x16_bf16 in the transposed forms of the
 // forward pass, so each of them is one of the bf16 tile path's two operand
 // patterns (row reads with the K swizzle, transpose reads with the V
@@ -113,8 +113,8 @@ __device__ __forceinline__ unsigned long long global_rows_in(const int *g, int n
 }
 
 // ---------------------------------------------------------------------------
-// Software pipeline of the dK/dV band loop (one wave per SIMD: nothing else
-// hides a wave's vector work). Iteration t runs S(t) and dP(t), then one
+// Software pipeline of the dK/dV band loop, for the instances that run one
+// wave per SIMD (nothing else then hides a wave's vector work). Iteration t runs S(t) and dP(t), then one
 // region in which the 32 MFMAs of dV += dO(t-1)^T P(t-1) and
 // dK += Q(t-1)^T dS(t-1) are issued in batches of four, each batch followed
 // by the vector work of four elements of tile t: P = exp2(S c - LSE log2 e)
