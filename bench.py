@@ -209,6 +209,8 @@ def main():
     lse = torch.empty(w.B, w.H, w.N, dtype=torch.float32, device="cuda")
     pairs = ea.attn_plan_stats(w.N, w.causal, w.win_left, w.win_right, w.global_idx, 128, 64)[0]
     flops = 4 * w.d * pairs * w.B * w.H
+    esize = 2 if w.dtype == "bf16" else 4
+    alg_bytes = 4 * w.B * w.H * w.N * w.d * esize + w.B * w.H * w.N * 4
     ws = None
     if w.global_idx:
         ws = torch.empty(ea.attn_workspace_bytes(w.B, w.H, w.N, w.d, len(w.global_idx)),
@@ -279,6 +281,10 @@ def main():
                    "inputs": f"{w.dtype} ~N(0,{w.sigma}^2)", "useful_flop_per_step": flops},
         "pct_bf16_peak": round(100.0 * value / PEAK_BF16, 2),
         "median_launch_ms": round(launch_ms[len(launch_ms) // 2], 4),
+        # Q, K, V read once and out, LSE written once, over the call: the rate
+        # that matters where the band is short and d small
+        "hbm_algorithmic_bytes": alg_bytes,
+        "hbm_algorithmic_gbs": round(alg_bytes / (avg_launch_ms * 1e-3) / 1e9, 1),
         "mall": "cold" if args.cold else "warm",
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
