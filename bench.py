@@ -7,7 +7,8 @@
                                            timed call, so no input is in MALL)
 
 One step = one attn_fwd call (every pass the mask needs) over one batch of
-seeded synthetic inputs already resident in HBM. The default workload is
+seeded synthetic inputs already resident in HBM. The untimed warm-up steps
+(20 by default) let the clocks leave their idle state first. The default workload is
 causal attention at B=1, H=32, N=32768, d=128 in bf16, the shape the
 throughput target is quoted on. Useful FLOPs count visible pairs only:
 4*d per visible (query, key) pair (QK^T and PV, two flops per multiply-add).
@@ -150,7 +151,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="tgt", choices=sorted(W.WORKLOADS))
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
