@@ -344,7 +344,12 @@ def bench_bwd(args):
                       "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
                       "config": {"workload": f"{mask_name(w)} attention backward B={w.B} H={w.H} N={w.N} d={w.d}",
                                  "useful_flop_per_step": flops},
-                      "pct_bf16_peak": round(100 * value / PEAK_BF16, 2)}), flush=True)
+                      "pct_bf16_peak": round(100 * value / PEAK_BF16, 2),
+                      "scaling": "weak", "vs_baseline": None,
+                      "roofline": {"bound": "mfma", "achieved": round(value, 2), "peak": PEAK_BF16,
+                                   "unit": "TFLOP/s", "frac": round(value / PEAK_BF16, 4), "traffic": None,
+                                   "kernel": "attn_bwd call (row terms, dK/dV, dQ; split passes and merges "
+                                             "with global tokens)"}}), flush=True)
     return 0
 
 
