@@ -1,9 +1,9 @@
 #!/usr/bin/env python3
 """Throughput of the exact-attention forward on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--config tgt|c1|c2|c3|c4|c5]
+    python bench.py [--steps K] [--warmup W] [--config causal_32k|f32_causal_256|causal_4k_b4|swa4096_32k|causal_131k|band256_globals_16k]
     python bench.py --sweep       (causal d=128 H=8 B=1, N = 512 ... 131072)
-    python bench.py --config c5 --cold   (a 1 GiB scratch write before every
+    python bench.py --config band256_globals_16k --cold   (a 1 GiB scratch write before every
                                            timed call, so no input is in MALL)
 
 One step = one attn_fwd call (every pass the mask needs) over one batch of
@@ -152,7 +152,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", default="tgt", choices=sorted(W.WORKLOADS))
+    ap.add_argument("--config", default="causal_32k", choices=sorted(W.WORKLOADS))
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", action="store_true",

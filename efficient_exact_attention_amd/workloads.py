@@ -68,19 +68,19 @@ def every_2048th(N: int) -> tuple:
 
 
 WORKLOADS = {
-    "c1": Workload("c1", 1, 1, 256, 64, "f32", 1.0, 1, -1, -1, (), 101,
+    "f32_causal_256": Workload("f32_causal_256", 1, 1, 256, 64, "f32", 1.0, 1, -1, -1, (), 101,
                    "single-head causal, fp32 inputs"),
-    "c2": Workload("c2", 4, 32, 4096, 128, "bf16", 1.0, 1, -1, -1, (), 102,
+    "causal_4k_b4": Workload("causal_4k_b4", 4, 32, 4096, 128, "bf16", 1.0, 1, -1, -1, (), 102,
                    "full causal"),
-    "c3": Workload("c3", 1, 32, 32768, 128, "bf16", 1.0, 1, 4095, 0, (), 103,
+    "swa4096_32k": Workload("swa4096_32k", 1, 32, 32768, 128, "bf16", 1.0, 1, 4095, 0, (), 103,
                    "sliding-window causal, w=4096 (row i sees i-4095..i)"),
-    "c4": Workload("c4", 1, 8, 131072, 128, "bf16", 0.5, 1, -1, -1, (), 104,
+    "causal_131k": Workload("causal_131k", 1, 8, 131072, 128, "bf16", 0.5, 1, -1, -1, (), 104,
                    "long-context causal, sigma 0.5"),
-    "c5": Workload("c5", 2, 12, 16384, 64, "bf16", 1.0, 0, 256, 256,
+    "band256_globals_16k": Workload("band256_globals_16k", 2, 12, 16384, 64, "bf16", 1.0, 0, 256, 256,
                    every_2048th(16384), 105,
                    "non-causal band +-256 plus 9 global tokens"),
-    "tgt": Workload("tgt", 1, 32, 32768, 128, "bf16", 1.0, 1, -1, -1, (), 106,
-                    "full causal, throughput target shape"),
+    "causal_32k": Workload("causal_32k", 1, 32, 32768, 128, "bf16", 1.0, 1, -1, -1, (), 106,
+                    "full causal"),
 }
 
 

@@ -363,11 +363,11 @@ def test_plan_workloads():
     """Pairs per head of the benchmark workloads and their tile counts at 128x64."""
     got = {k: ea.attn_plan_stats(w.N, w.causal, w.win_left, w.win_right, w.global_idx, 128, 64)
            for k, w in W.WORKLOADS.items()}
-    assert got["c2"] == (8_390_656, 992, 64)
-    assert got["c3"] == (125_831_168, 14_880, 960)
-    assert got["c4"][0] == 8_590_000_128
-    assert got["tgt"] == (536_887_296, 65_280, 512)
-    pairs, full, edge = got["c5"]
+    assert got["causal_4k_b4"] == (8_390_656, 992, 64)
+    assert got["swa4096_32k"] == (125_831_168, 14_880, 960)
+    assert got["causal_131k"][0] == 8_590_000_128
+    assert got["causal_32k"] == (536_887_296, 65_280, 512)
+    pairs, full, edge = got["band256_globals_16k"]
     assert pairs == 8_625_830
     # band-only tiles (global columns are handled by the gathered tile, so they
     # do not turn band tiles into edge tiles): 764 full + 504 edge, the same

@@ -69,7 +69,7 @@ def test_pair_counts_workloads():
     assert swa_pairs(32768, 4096) == 125_831_168
     assert causal_pairs(131072) == 8_590_000_128
     assert causal_pairs(32768) == 536_887_296
-    G = W.WORKLOADS["c5"].global_idx
+    G = W.WORKLOADS["band256_globals_16k"].global_idx
     assert len(G) == 9
     assert band_global_pairs(16384, 256, G) == 8_625_830
     assert oracle.visible_pairs_bruteforce(16384, 0, 256, 256, G) == 8_625_830

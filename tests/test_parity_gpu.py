@@ -111,50 +111,50 @@ def test_narrow_band_threshold(wl, wr, causal):
 
 # ---- the benchmark workloads at full size ---------------------------------------------
 
-def test_c1_fp32_all_rows():
-    w = W.WORKLOADS["c1"]
+def test_f32_causal_256_all_rows():
+    w = W.WORKLOADS["f32_causal_256"]
     qkv = W.make_qkv(w)
     o, l = run_gpu(w, qkv)
     check(w, o, l, all_heads(w), np.arange(w.N), qkv)
 
 
-def test_c2_full_causal():
-    w = W.WORKLOADS["c2"]
+def test_causal_4k_b4():
+    w = W.WORKLOADS["causal_4k_b4"]
     o, l = run_gpu(w)
     check(w, o, l, some_heads(w, 16), W.sample_rows(w, 96))
 
 
-def test_c3_sliding_window():
-    w = W.WORKLOADS["c3"]
+def test_swa4096_32k():
+    w = W.WORKLOADS["swa4096_32k"]
     o, l = run_gpu(w)
     rows = np.union1d(W.sample_rows(w, 48), np.array([4094, 4095, 4096, 4097, 8191, 8192]))
     check(w, o, l, some_heads(w, 8), rows)
 
 
-def test_c4_long_context():
-    w = W.WORKLOADS["c4"]
+def test_causal_131k_rows():
+    w = W.WORKLOADS["causal_131k"]
     o, l = run_gpu(w)
     check(w, o, l, all_heads(w), W.sample_rows(w, 40))
 
 
-def test_c5_local_global():
-    w = W.WORKLOADS["c5"]
+def test_band256_globals_16k():
+    w = W.WORKLOADS["band256_globals_16k"]
     o, l = run_gpu(w)
     rows = np.union1d(W.sample_rows(w, 64),
                       np.array([2, 255, 256, 257, 2047, 2049, 2304, 2305, 16127, 16128, 16383]))
     check(w, o, l, some_heads(w, 8), rows)
 
 
-def test_target_causal_32k():
-    w = W.WORKLOADS["tgt"]
+def test_causal_32k():
+    w = W.WORKLOADS["causal_32k"]
     o, l = run_gpu(w)
     check(w, o, l, some_heads(w, 6), W.sample_rows(w, 48))
 
 
-def test_c5_alternative_global_reading():
+def test_band256_globals_alternative_reading():
     """Globals counted from 1 ({0, 1, 2047, 4095, ...}): any index set works."""
     g = tuple(sorted({0, 1} | set(range(2047, 16384, 2048))))
-    w = W.WORKLOADS["c5"].with_(name="c5alt", global_idx=g, B=1, H=4)
+    w = W.WORKLOADS["band256_globals_16k"].with_(name="band256_globals_16k_alt", global_idx=g, B=1, H=4)
     o, l = run_gpu(w)
     check(w, o, l, all_heads(w), W.sample_rows(w, 64))
 
@@ -247,11 +247,11 @@ def test_errors_raise_before_launch():
 
 
 def test_long_context_memory_is_linear():
-    """c4 with free device memory cut to a few GiB: an N x N score buffer
+    """The N=131072 causal workload with free device memory cut to a few GiB: an N x N score buffer
     (68.7 GB per head in fp32) could not be allocated, yet the call succeeds
     and leaves free memory unchanged."""
     import efficient_exact_attention_amd as ea
-    w = W.WORKLOADS["c4"]
+    w = W.WORKLOADS["causal_131k"]
     assert ea.attn_workspace_bytes(w.B, w.H, w.N, w.d, 0) == 0
     qkv = W.make_qkv(w)
     q, k, v = (to_device(x, w.dtype) for x in qkv)

@@ -25,7 +25,7 @@ def test_head_values_match_full_tensor():
 
 
 def test_seeds_reproducible_and_distinct():
-    w = W.WORKLOADS["c1"]
+    w = W.WORKLOADS["f32_causal_256"]
     a = W.make_qkv(w)
     b = W.make_qkv(w)
     assert all(np.array_equal(x, y) for x, y in zip(a, b))
@@ -34,7 +34,7 @@ def test_seeds_reproducible_and_distinct():
 
 
 def test_sample_rows():
-    w = W.WORKLOADS["c4"]
+    w = W.WORKLOADS["causal_131k"]
     r = W.sample_rows(w, 256)
     assert len(r) == 256 and np.all(np.diff(r) > 0)
     for e in (0, 1, 127, 128, 255, 256, w.N // 2, w.N - 2, w.N - 1):
@@ -42,6 +42,6 @@ def test_sample_rows():
 
 
 def test_workload_table():
-    c5 = W.WORKLOADS["c5"]
-    assert c5.global_idx == (0, 1, 2048, 4096, 6144, 8192, 10240, 12288, 14336)
-    assert W.WORKLOADS["c3"].win_left == 4095 and W.WORKLOADS["c3"].win_right == 0
+    band = W.WORKLOADS["band256_globals_16k"]
+    assert band.global_idx == (0, 1, 2048, 4096, 6144, 8192, 10240, 12288, 14336)
+    assert W.WORKLOADS["swa4096_32k"].win_left == 4095 and W.WORKLOADS["swa4096_32k"].win_right == 0
