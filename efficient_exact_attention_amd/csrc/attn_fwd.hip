@@ -846,30 +846,60 @@ __global__ void __launch_bounds__((BLK || XT || NAR) ? 256 : 512, NAR ? 2 : 1) f
             __syncthreads();
         };
         if (prm.stride > 0) {
-            // offsets o = stride * 2^m < N; the key ranges [q0 - o, q1 - o]
-            // (farthest first) then [q0 + o, q1 + o] (nearest first) come in
-            // increasing order, so a running bound visits each tile once
+            // offsets o = stride * 2^m < N. A row sees at most one key per
+            // offset and side, so each such pair is one dot product on the
+            // vector ALU (each lane takes its half of d, as its Q operand
+            // holds it; the halves are summed across the wave halves)
+            // instead of a 64-key tile of which one key per row is used.
+            // The weight is kept in fp32 for the output as for the
+            // normaliser.
             const int st = prm.stride;
             int mtop = -1;
             while (mtop < 30 && ((long long)st << (mtop + 1)) < N) ++mtop;
-            int next = 0;
-            auto strided = [&](int j) {
-                const int dist = j > row ? j - row : row - j;
-                if (dist == 0 || dist % st) return false;
-                const int m = dist / st;
-                return (m & (m - 1)) == 0;
-            };
-            auto visit = [&](int klo, int khi) __attribute__((always_inline)) {
-                klo = imax(klo, 0);
-                khi = imin(khi, N - 1);
-                if (klo > khi) return;
-                const int t1 = khi / BN;
-                for (int t = imax(klo / BN, next); t <= t1; ++t) extra_tile(t * BN, wave_active, strided);
-                next = imax(next, t1 + 1);
-            };
-            for (int m = mtop; m >= 0; --m) visit(q0 - (st << m), q1 - (st << m));
-            if (!prm.causal)
-                for (int m = 0; m <= mtop; ++m) visit(q0 + (st << m), q1 + (st << m));
+            for (int side = 0; side < (prm.causal ? 1 : 2); ++side)
+                for (int m = 0; m <= mtop; ++m) {
+                    const int o = st << m;
+                    const int j = side ? row + o : row - o;
+                    bool ok = valid & (j >= 0) & (j < N) & ((j < lo) | (j > hi));
+                    for (int t = 0; t < ng; ++t) ok &= s_gidx[t] != j;   // pairs of the gathered global tile
+                    if (!__any(ok)) continue;
+                    const int jj = ok ? j : 0;   // a row that exists; its result is dropped
+                    const u32x4 *kr = reinterpret_cast<const u32x4 *>(kh + (long long)jj * D);
+                    float part = 0.f;
+#pragma unroll
+                    for (int ks = 0; ks < P::KS; ++ks) {
+                        const bf16x8 kv = __builtin_bit_cast(bf16x8, kr[2 * ks + h]);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const bf16x2 a = {kv[2 * e], kv[2 * e + 1]};
+                            const bf16x2 q = {qf.x[ks][2 * e], qf.x[ks][2 * e + 1]};
+                            part = __builtin_amdgcn_fdot2_f32_bf16(a, q, part, false);
+                        }
+                    }
+                    const float sl = ok ? sum_across_halves(part) * c : EEA_NEG_INF;   // log2 domain
+                    const float mnew = fmaxf(rs.m, sl);
+                    if (__any(mnew > rs.m + kRescaleLog2)) {
+                        const float alpha = (mnew == EEA_NEG_INF) ? 1.f : fast_exp2(rs.m - mnew);
+                        rs.m = mnew;
+                        rs.lpart *= alpha;
+#pragma unroll
+                        for (int db = 0; db < P::DB; ++db) rs.o[db] *= alpha;
+                    }
+                    const float pw = ok ? fast_exp2(sl - rs.m) : 0.f;
+                    if (h == 0) rs.lpart += pw;   // one half counts the key in the normaliser
+                    // O^T: this lane holds d = 32 db + 8 g + 4 h + e of its row
+                    const uint16_t *vr = vh + (long long)jj * D;
+#pragma unroll
+                    for (int db = 0; db < P::DB; ++db)
+#pragma unroll
+                        for (int g = 0; g < 4; ++g) {
+                            const uint2 w = *reinterpret_cast<const uint2 *>(vr + db * 32 + 8 * g + 4 * h);
+                            rs.o[db][4 * g + 0] += pw * __uint_as_float(w.x << 16);
+                            rs.o[db][4 * g + 1] += pw * __uint_as_float(w.x & 0xffff0000u);
+                            rs.o[db][4 * g + 2] += pw * __uint_as_float(w.y << 16);
+                            rs.o[db][4 * g + 3] += pw * __uint_as_float(w.y & 0xffff0000u);
+                        }
+                }
         }
         if (prm.rand_block > 0) {
             // each query block's listed key blocks (out-of-range entries
