@@ -814,10 +814,12 @@ __global__ void __launch_bounds__((BLK || XT || NAR) ? 256 : 512, NAR ? 2 : 1) f
     }
 
     if constexpr (XT) {
-        // --- extra key tiles of the strided and random-block rules,
-        // unpipelined. A pair counts here only outside the row's band, off
-        // the global columns (the gathered tile has those) and within the
-        // causal limit; every tile is visited once per pattern entry.
+        // --- pairs of the strided and random-block rules beyond the band:
+        // the random-block rule as unpipelined extra key tiles, the strided
+        // rule pair by pair (below). A pair counts here only outside the
+        // row's band, off the global columns (the gathered tile has those)
+        // and within the causal limit; every tile is visited once per
+        // pattern entry.
         const int q1 = imin(N - 1, q0 + BM - 1);
         auto extra_tile = [&](int k0, bool take, auto vis) __attribute__((always_inline)) {
             P::issue_k(L, kh, N, kb0, k0);
