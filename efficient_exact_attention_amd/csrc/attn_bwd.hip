@@ -1076,27 +1076,26 @@ __global__ void __launch_bounds__((dq_threads<D, MODE, XT>()), dq_waves<D>()) bw
             __syncthreads();
         };
         if (prm.stride > 0) {
+            // a row's keys at distance s * 2^m, one pair at a time on the
+            // vector ALU (as in the forward): S and dP by dot products of the
+            // lane's halves, dS, then dQ^T += dS K_j
             const int st = prm.stride;
             int mtop = -1;
             while (mtop < 30 && ((long long)st << (mtop + 1)) < N) ++mtop;
-            int next = 0;
-            auto strided = [&](int j) {
-                const int dist = j > row ? j - row : row - j;
-                if (dist == 0 || dist % st) return false;
-                const int m = dist / st;
-                return (m & (m - 1)) == 0;
-            };
-            auto visit = [&](int klo, int khi) __attribute__((always_inline)) {
-                klo = imax(klo, 0);
-                khi = imin(khi, N - 1);
-                if (klo > khi) return;
-                const int t1 = khi / BN;
-                for (int t = imax(klo / BN, next); t <= t1; ++t) extra_ktile(t * BN, wave_active, strided);
-                next = imax(next, t1 + 1);
-            };
-            for (int m = mtop; m >= 0; --m) visit(q0 - (st << m), q1 - (st << m));
-            if (!prm.causal)
-                for (int m = 0; m <= mtop; ++m) visit(q0 + (st << m), q1 + (st << m));
+            for (int side = 0; side < (prm.causal ? 1 : 2); ++side)
+                for (int m = 0; m <= mtop; ++m) {
+                    const int o = st << m;
+                    const int j = side ? row + o : row - o;
+                    bool ok = valid & !row_is_g & (j >= 0) & (j < N) & ((j < lo) | (j > hi));
+                    for (int t = 0; t < ng; ++t) ok &= s_g[t] != j;   // pairs of the gathered global tile
+                    if (!__any(ok)) continue;
+                    const int jj = ok ? j : 0;   // a row that exists; its result is dropped
+                    const uint16_t *kr = kh + (long long)jj * D, *vr = vh + (long long)jj * D;
+                    const float sc = sum_across_halves(dot_row_half(kr, qf.x, h));
+                    const float dpv = sum_across_halves(dot_row_half(vr, gf.x, h));
+                    const float p = ok ? fast_exp2(__builtin_fmaf(sc, c, -l2)) : 0.f;
+                    axpy_row_half(dq, p * (dpv - dl), kr, h);
+                }
         }
         if (prm.rand_block > 0) {
             const int rb = prm.rand_block, nr = prm.n_rand, nkb = (N + rb - 1) / rb;

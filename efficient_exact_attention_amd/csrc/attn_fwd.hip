@@ -866,18 +866,7 @@ __global__ void __launch_bounds__((BLK || XT || NAR) ? 256 : 512, NAR ? 2 : 1) f
                     for (int t = 0; t < ng; ++t) ok &= s_gidx[t] != j;   // pairs of the gathered global tile
                     if (!__any(ok)) continue;
                     const int jj = ok ? j : 0;   // a row that exists; its result is dropped
-                    const u32x4 *kr = reinterpret_cast<const u32x4 *>(kh + (long long)jj * D);
-                    float part = 0.f;
-#pragma unroll
-                    for (int ks = 0; ks < P::KS; ++ks) {
-                        const bf16x8 kv = __builtin_bit_cast(bf16x8, kr[2 * ks + h]);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const bf16x2 a = {kv[2 * e], kv[2 * e + 1]};
-                            const bf16x2 q = {qf.x[ks][2 * e], qf.x[ks][2 * e + 1]};
-                            part = __builtin_amdgcn_fdot2_f32_bf16(a, q, part, false);
-                        }
-                    }
+                    const float part = dot_row_half(kh + (long long)jj * D, qf.x, h);
                     const float sl = ok ? sum_across_halves(part) * c : EEA_NEG_INF;   // log2 domain
                     const float mnew = fmaxf(rs.m, sl);
                     if (__any(mnew > rs.m + kRescaleLog2)) {
@@ -889,18 +878,7 @@ __global__ void __launch_bounds__((BLK || XT || NAR) ? 256 : 512, NAR ? 2 : 1) f
                     }
                     const float pw = ok ? fast_exp2(sl - rs.m) : 0.f;
                     if (h == 0) rs.lpart += pw;   // one half counts the key in the normaliser
-                    // O^T: this lane holds d = 32 db + 8 g + 4 h + e of its row
-                    const uint16_t *vr = vh + (long long)jj * D;
-#pragma unroll
-                    for (int db = 0; db < P::DB; ++db)
-#pragma unroll
-                        for (int g = 0; g < 4; ++g) {
-                            const uint2 w = *reinterpret_cast<const uint2 *>(vr + db * 32 + 8 * g + 4 * h);
-                            rs.o[db][4 * g + 0] += pw * __uint_as_float(w.x << 16);
-                            rs.o[db][4 * g + 1] += pw * __uint_as_float(w.x & 0xffff0000u);
-                            rs.o[db][4 * g + 2] += pw * __uint_as_float(w.y << 16);
-                            rs.o[db][4 * g + 3] += pw * __uint_as_float(w.y & 0xffff0000u);
-                        }
+                    axpy_row_half(rs.o, pw, vh + (long long)jj * D, h);   // O^T += p V_j
                 }
         }
         if (prm.rand_block > 0) {

@@ -317,6 +317,42 @@ struct Bf16Path {
     }
 };
 
+// Single (row, key) pairs on the vector ALU, for rules that give a row a
+// handful of scattered keys (no dense tile to contract). A lane's operand
+// fragment holds the 16-byte chunks 2 ks + h of its row (as load_q reads
+// them); its transposed accumulators hold d = 32 db + 8 g + 4 h + e.
+// dot_row_half: this lane's half of row . fragment (the other half is in
+// lane ^ 32); axpy_row_half: acc += w * row over this lane's accumulator d.
+template <int KS>
+__device__ __forceinline__ float dot_row_half(const uint16_t *rowp, const bf16x8 (&x)[KS], int h) {
+    const u32x4 *r = reinterpret_cast<const u32x4 *>(rowp);
+    float part = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 v = __builtin_bit_cast(bf16x8, r[2 * ks + h]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const bf16x2 a = {v[2 * e], v[2 * e + 1]};
+            const bf16x2 b = {x[ks][2 * e], x[ks][2 * e + 1]};
+            part = __builtin_amdgcn_fdot2_f32_bf16(a, b, part, false);
+        }
+    }
+    return part;
+}
+template <int DB>
+__device__ __forceinline__ void axpy_row_half(f32x16 (&acc)[DB], float w, const uint16_t *rowp, int h) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const uint2 v = *reinterpret_cast<const uint2 *>(rowp + db * 32 + 8 * g + 4 * h);
+            acc[db][4 * g + 0] += w * __uint_as_float(v.x << 16);
+            acc[db][4 * g + 1] += w * __uint_as_float(v.x & 0xffff0000u);
+            acc[db][4 * g + 2] += w * __uint_as_float(v.y << 16);
+            acc[db][4 * g + 3] += w * __uint_as_float(v.y & 0xffff0000u);
+        }
+}
+
 // Lane l and lane l^32 hold the same row of a 32x32 accumulator column:
 // combine their values.
 __device__ __forceinline__ float max_across_halves(float x) {
