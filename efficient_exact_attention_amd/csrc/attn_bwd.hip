@@ -326,6 +326,8 @@ __global__ void __launch_bounds__(kBwdThreads, (dkdv_waves<D, MODE, XT>())) bwd_
     __shared__ __attribute__((aligned(16))) float s_lse[2][BQ];   // LSE * log2(e)
     __shared__ __attribute__((aligned(16))) float s_dl[2][BQ];    // rowsum(dO * O)
     __shared__ int s_g[kMaxGlobal];                               // sorted global positions
+    __shared__ int s_hit[XT ? kBwdThreads : 1];                    // random-block list hits of one scan chunk
+    __shared__ int s_nhit[XT ? kBwdThreads / 64 : 1];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int ln = lane & 31, h = lane >> 5;
@@ -709,21 +711,43 @@ __global__ void __launch_bounds__(kBwdThreads, (dkdv_waves<D, MODE, XT>())) bwd_
         }
         if (prm.rand_block > 0) {
             // the query blocks whose lists name a key block of this
-            // workgroup (out-of-range entries skipped, repeats once)
+            // workgroup (out-of-range entries skipped, repeats once). The
+            // lists are scanned a workgroup-width of entries at a time, one
+            // entry per thread, and the hits compacted in list order through
+            // LDS (a serial scan of every list by one wave waited on each
+            // load in turn)
             const int rb = prm.rand_block, nr = prm.n_rand, nb = (N + rb - 1) / rb;
-            for (int qb = 0; qb < nb; ++qb) {
-                const int *lst = prm.rand_idx + (long long)qb * nr;
-                for (int e = 0; e < nr; ++e) {
+            const int total = nb * nr;
+            for (int base = 0; base < total; base += kBwdThreads) {
+                const int idx = base + tid;
+                bool hit = false;
+                if (idx < total) {
+                    const int qb = idx / nr, e = idx - qb * nr;
+                    const int *lst = prm.rand_idx + (long long)qb * nr;
                     const int kb = lst[e];
-                    bool skip = kb < 0 || kb >= nb || kb * rb > K1 || kb * rb + rb - 1 < K0;
-                    for (int e2 = 0; e2 < e && !skip; ++e2) skip = lst[e2] == kb;
-                    if (skip) continue;
+                    hit = kb >= 0 && kb < nb && kb * rb <= K1 && kb * rb + rb - 1 >= K0;
+                    for (int e2 = 0; e2 < e && hit; ++e2) hit = lst[e2] != kb;
+                    if (prm.causal && imin(N - 1, qb * rb + rb - 1) < kb * rb) hit = false;
+                }
+                const unsigned long long bal = __ballot(hit);
+                if (lane == 0) s_nhit[wave] = __popcll(bal);
+                __syncthreads();
+                int off = 0, nhit = 0;
+                for (int w2 = 0; w2 < P::NW; ++w2) {
+                    off += w2 < wave ? s_nhit[w2] : 0;
+                    nhit += s_nhit[w2];
+                }
+                if (hit) s_hit[off + __popcll(bal & ((1ull << lane) - 1ull))] = idx;
+                __syncthreads();
+                for (int x = 0; x < nhit; ++x) {
+                    const int idx2 = __builtin_amdgcn_readfirstlane(s_hit[x]);
+                    const int qb = idx2 / nr, kb = prm.rand_idx[idx2];
                     const int rlo = qb * rb, rhi = imin(N - 1, rlo + rb - 1);
-                    if (prm.causal && rhi < kb * rb) continue;
                     const int klo = kb * rb, khi = kb * rb + rb - 1;
                     for (int t = rlo / BQ; t <= rhi / BQ; ++t)
                         extra_qtile(t * BQ, [&](int i) { return i >= rlo && i <= rhi && key >= klo && key <= khi; });
                 }
+                __syncthreads();   // every wave has read s_hit before the next chunk
             }
         }
     }
