@@ -176,3 +176,25 @@ def test_random_blocks_bwd(ci, N, d, H, H_kv):
     mm = dict(m, global_idx=tuple(g for g in m.get("global_idx", ()) if g < N))
     lists = rand_lists(N, m["rand_block"], r, seed=ci + N + 3, extra=extra)
     run_bwd_extra(1, H, H_kv, N, d, mm, seed=N + ci + 2, lists=lists)
+
+
+def test_random_blocks_bwd_many_list_entries_deterministic():
+    """More list entries than one scan chunk of the dK/dV kernel (128 query
+    blocks x 4 entries = 512 > 256 threads): the hits of every chunk are
+    taken, against the oracle, and two calls give identical bits."""
+    import efficient_exact_attention_amd as ea
+    N, d, b, r = 4096, 64, 32, 4
+    m = dict(rand_block=b, causal=0, win_left=16, win_right=16, global_idx=(0, 2047))
+    lists = rand_lists(N, b, r, seed=77, extra=((5, 1, -1), (9, 3, 4096)))
+    run_bwd_extra(1, 2, 2, N, d, m, seed=78, lists=lists)
+    q, k, v = _inputs(1, 2, 2, N, d, 79)
+    do = W.make_tensor(W.random_workload("xdo", 1, 2, N, d, seed=84), 0)
+    qd, kd, vd, dod = (to_device(x, "bf16") for x in (q, k, v, do))
+    kw = dict(m, rand_idx=torch.from_numpy(lists).cuda())
+    say(f"  launch random-block bwd twice: N={N} d={d} b={b} r={r}")
+    out, lse = ea.fwd(qd, kd, vd, **kw)
+    g1 = [x.clone() for x in ea.bwd(qd, kd, vd, out, dod, lse, **kw)]
+    g2 = ea.bwd(qd, kd, vd, out, dod, lse, **kw)
+    torch.cuda.synchronize()
+    for a, c in zip(g1, g2):
+        assert torch.equal(a.view(torch.int16), c.view(torch.int16))
