@@ -226,6 +226,13 @@ def attn_tile_shape(d, dtype=ATTN_BF16):
     return bm.value, bn.value
 
 
+def _ws(workspace):
+    """(device address, bytes) of a workspace tensor, or (None, 0)."""
+    if workspace is None:
+        return None, 0
+    return workspace.data_ptr(), workspace.numel() * workspace.element_size()
+
+
 def fwd(q, k, v, *, causal=False, win_left=-1, win_right=-1, global_idx=None, scale=None,
         out=None, lse=None, workspace=None, stream=None, block=0, dilation=1, stride=0, rand_block=0,
         rand_idx=None):
@@ -236,8 +243,10 @@ def fwd(q, k, v, *, causal=False, win_left=-1, win_right=-1, global_idx=None, sc
     r] of key-block lists.
 
     Allocates ``out`` (input dtype) and ``lse`` (fp32 [B, H, N]) with torch
-    unless given, enqueues the kernels on torch's current stream (or
-    ``stream``) and returns (out, lse) without synchronising.
+    unless given, and with global tokens a workspace for the global-row
+    partials (so concurrent calls on different streams share no memory),
+    enqueues the kernels on torch's current stream (or ``stream``) and
+    returns (out, lse) without synchronising.
     """
     import torch
     if q.dtype not in (torch.bfloat16, torch.float32):
@@ -265,8 +274,13 @@ def fwd(q, k, v, *, causal=False, win_left=-1, win_right=-1, global_idx=None, sc
         stream = torch.cuda.current_stream(q.device).cuda_stream
     elif hasattr(stream, "cuda_stream"):
         stream = stream.cuda_stream
-    ws, wsb = (workspace.data_ptr(), workspace.numel() * workspace.element_size()) \
-        if workspace is not None else (None, 0)
+    if workspace is None and global_idx is not None and len(global_idx) > 0:
+        # a workspace of this call's own (torch's caching allocator), so that
+        # calls on different streams never share the library's scratch
+        nb = attn_workspace_bytes(B, H, N, d, len(global_idx))
+        if nb > 0:
+            workspace = torch.empty(nb, dtype=torch.uint8, device=q.device)
+    ws, wsb = _ws(workspace)
     n_rand, rptr = 0, None
     if rand_block:
         if rand_idx is None or rand_idx.dtype != torch.int32 or not rand_idx.is_cuda or rand_idx.dim() != 2 \
@@ -288,8 +302,9 @@ def bwd(q, k, v, out, dout, lse, *, causal=False, win_left=-1, win_right=-1, glo
         rand_idx=None):
     """Gradients (dq, dk, dv) of ``fwd`` on torch CUDA bf16 tensors: q, out,
     dout [B, H, N, d], k, v [B, H_kv, N, d], lse fp32 [B, H, N] from the
-    forward call with the same mask and scale. Allocates the gradients with
-    torch unless given and enqueues the kernels without synchronising."""
+    forward call with the same mask and scale. Allocates the gradients and
+    the workspace with torch unless given and enqueues the kernels without
+    synchronising."""
     import torch
     if q.dim() != 4 or k.dim() != 4:
         raise ValueError("tensors must be [B, H, N, d]")
@@ -310,8 +325,12 @@ def bwd(q, k, v, out, dout, lse, *, causal=False, win_left=-1, win_right=-1, glo
         stream = torch.cuda.current_stream(q.device).cuda_stream
     elif hasattr(stream, "cuda_stream"):
         stream = stream.cuda_stream
-    ws, wsb = (workspace.data_ptr(), workspace.numel() * workspace.element_size()) \
-        if workspace is not None else (None, 0)
+    if workspace is None:
+        nb = attn_bwd_workspace_bytes(B, H, N, d, H_kv=H_kv,
+                                      n_global=0 if global_idx is None else len(global_idx))
+        if nb > 0:
+            workspace = torch.empty(nb, dtype=torch.uint8, device=q.device)
+    ws, wsb = _ws(workspace)
     n_rand, rptr = 0, None
     if rand_block:
         if rand_idx is None or rand_idx.dtype != torch.int32 or not rand_idx.is_cuda or rand_idx.dim() != 2 \
@@ -357,8 +376,11 @@ def decode(q, k_cache, v_cache, seq_len, *, win_left=-1, rolling=False, scale=No
         stream = torch.cuda.current_stream(q.device).cuda_stream
     elif hasattr(stream, "cuda_stream"):
         stream = stream.cuda_stream
-    ws, wsb = (workspace.data_ptr(), workspace.numel() * workspace.element_size()) \
-        if workspace is not None else (None, 0)
+    if workspace is None:
+        nb = attn_decode_workspace_bytes(B, H, H_kv, Nq, S, d, win_left, rolling)
+        if nb > 0:
+            workspace = torch.empty(nb, dtype=torch.uint8, device=q.device)
+    ws, wsb = _ws(workspace)
     attn_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), seq_len.data_ptr(), out.data_ptr(),
                 lse.data_ptr(), B, H, H_kv, Nq, S, d, win_left, int(bool(rolling)),
                 scale=0.0 if scale is None else float(scale), stream=stream, workspace=ws, workspace_bytes=wsb)

@@ -25,15 +25,32 @@ DEVICE_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
 
 
 def build(verbose: bool = False, extra_flags=()) -> str:
+    """Compile every source to an object (in parallel), then link libattn.so."""
+    import tempfile
+    from concurrent.futures import ThreadPoolExecutor
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, *DEVICE_FLAGS, *extra_flags, "-shared", f"-I{INCLUDE}", f"-I{CSRC}",
-           *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        sys.stderr.write(r.stdout + r.stderr)
-        raise RuntimeError(f"hipcc failed with status {r.returncode}")
+    with tempfile.TemporaryDirectory() as objdir:
+        def compile_one(src):
+            obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
+            cmd = [HIPCC, *DEVICE_FLAGS, *extra_flags, "-c", f"-I{INCLUDE}", f"-I{CSRC}",
+                   os.path.join(CSRC, src), "-o", obj]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            r = subprocess.run(cmd, capture_output=True, text=True)
+            if r.returncode != 0:
+                sys.stderr.write(r.stdout + r.stderr)
+                raise RuntimeError(f"hipcc failed on {src} with status {r.returncode}")
+            return obj
+
+        with ThreadPoolExecutor(len(SOURCES)) as ex:
+            objs = list(ex.map(compile_one, SOURCES))
+        cmd = [HIPCC, *DEVICE_FLAGS, *extra_flags, "-shared", *objs, "-o", tmp]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            sys.stderr.write(r.stdout + r.stderr)
+            raise RuntimeError(f"hipcc link failed with status {r.returncode}")
     os.replace(tmp, LIB)
     return LIB
 

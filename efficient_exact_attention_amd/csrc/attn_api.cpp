@@ -35,13 +35,21 @@ int fail(int code, const char *fmt, ...) {
     return code;
 }
 
+// Library-owned device scratch, one buffer per device and kind (the
+// forward's global-row partials, the backward's row terms and split-pass
+// partials, decoding's per-chunk partials). A call without a caller
+// workspace runs under the mutex: its stream first waits on the event that
+// the previous user of the buffer recorded, then its kernels are enqueued,
+// then it records the event itself. Calls on different streams therefore
+// use the buffer one after another, never at the same time.
+enum ScratchKind { SCR_FWD = 0, SCR_BWD = 1, SCR_DEC = 2, SCR_KINDS = 3 };
+
 struct DeviceSlot {
     int arch_checked = 0;
     int arch_ok = 0;
-    void *scratch = nullptr;        // forward: global-row partials
-    size_t scratch_bytes = 0;
-    void *bwd_scratch = nullptr;    // backward: per-row terms
-    size_t bwd_scratch_bytes = 0;
+    void *scratch[SCR_KINDS] = {nullptr, nullptr, nullptr};
+    size_t scratch_bytes[SCR_KINDS] = {0, 0, 0};
+    hipEvent_t last_use[SCR_KINDS] = {nullptr, nullptr, nullptr};
 };
 std::mutex g_mu;
 std::vector<DeviceSlot> g_dev;
@@ -49,6 +57,77 @@ std::vector<DeviceSlot> g_dev;
 DeviceSlot &slot(int dev) {
     if ((int)g_dev.size() <= dev) g_dev.resize(dev + 1);
     return g_dev[dev];
+}
+
+// Current device, checked to be gfx950 once. Caller holds g_mu.
+int current_device_locked(DeviceSlot **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(ATTN_ERR_DEVICE, "hipGetDevice: %s", hipGetErrorString(e));
+    DeviceSlot &s = slot(dev);
+    if (!s.arch_checked) {
+        hipDeviceProp_t prop;
+        e = hipGetDeviceProperties(&prop, dev);
+        if (e != hipSuccess) return fail(ATTN_ERR_DEVICE, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+        s.arch_ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+        s.arch_checked = 1;
+    }
+    if (!s.arch_ok) return fail(ATTN_ERR_UNSUPPORTED, "device %d is not gfx950 (MI355X)", dev);
+    *out = &s;
+    return ATTN_OK;
+}
+
+// Enqueue launch(buf) on `stream`. With caller_ws set (or need == 0) the
+// kernels run on that memory and no library state is touched beyond the
+// device check. Otherwise buf is the library scratch of `kind`, grown to at
+// least `need` bytes (the old buffer is freed only after its last user's
+// event has completed) and ordered against its previous user as described
+// at DeviceSlot. launch returns a hipError_t.
+template <class F>
+int run_on_device(int kind, size_t need, void *caller_ws, hipStream_t stream, F &&launch) {
+    std::unique_lock<std::mutex> lk(g_mu);
+    DeviceSlot *s = nullptr;
+    int rc = current_device_locked(&s);
+    if (rc != ATTN_OK) return rc;
+    hipError_t e;
+    if (caller_ws || need == 0) {
+        lk.unlock();
+        e = launch(caller_ws);
+        if (e != hipSuccess) return fail(ATTN_ERR_DEVICE, "kernel launch: %s", hipGetErrorString(e));
+        return ATTN_OK;
+    }
+    hipEvent_t &ev = s->last_use[kind];
+    if (!ev) {
+        e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+        if (e != hipSuccess) {
+            ev = nullptr;
+            return fail(ATTN_ERR_DEVICE, "hipEventCreateWithFlags: %s", hipGetErrorString(e));
+        }
+    }
+    void *&ptr = s->scratch[kind];
+    size_t &bytes = s->scratch_bytes[kind];
+    if (bytes < need) {
+        if (ptr) {
+            e = hipEventSynchronize(ev);   // the last call that used the old buffer is done
+            if (e == hipSuccess) e = hipFree(ptr);
+            ptr = nullptr;
+            bytes = 0;
+            if (e != hipSuccess) return fail(ATTN_ERR_DEVICE, "releasing the old scratch: %s", hipGetErrorString(e));
+        }
+        e = hipMalloc(&ptr, need);
+        if (e != hipSuccess) {
+            ptr = nullptr;
+            return fail(ATTN_ERR_DEVICE, "hipMalloc(%zu): %s", need, hipGetErrorString(e));
+        }
+        bytes = need;
+    }
+    e = hipStreamWaitEvent(stream, ev, 0);   // after the previous user (a no-op the first time)
+    if (e != hipSuccess) return fail(ATTN_ERR_DEVICE, "hipStreamWaitEvent: %s", hipGetErrorString(e));
+    e = launch(ptr);
+    if (e != hipSuccess) return fail(ATTN_ERR_DEVICE, "kernel launch: %s", hipGetErrorString(e));
+    e = hipEventRecord(ev, stream);
+    if (e != hipSuccess) return fail(ATTN_ERR_DEVICE, "hipEventRecord: %s", hipGetErrorString(e));
+    return ATTN_OK;
 }
 
 bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
@@ -406,80 +485,12 @@ int fwd_impl(const void *q, const void *k, const void *v, void *out, float *lse,
     }
 
     // ---- first HIP call
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return fail(ATTN_ERR_DEVICE, "hipGetDevice: %s", hipGetErrorString(e));
-    {
-        std::lock_guard<std::mutex> lk(g_mu);
-        DeviceSlot &s = slot(dev);
-        if (!s.arch_checked) {
-            hipDeviceProp_t prop;
-            e = hipGetDeviceProperties(&prop, dev);
-            if (e != hipSuccess) return fail(ATTN_ERR_DEVICE, "hipGetDeviceProperties: %s", hipGetErrorString(e));
-            s.arch_ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
-            s.arch_checked = 1;
-        }
-        if (!s.arch_ok) return fail(ATTN_ERR_UNSUPPORTED, "device %d is not gfx950 (MI355X)", dev);
-        if (ng > 0 && !p.part) {
-            if (s.scratch_bytes < need) {
-                if (s.scratch) {
-                    e = hipFree(s.scratch);
-                    s.scratch = nullptr;
-                    s.scratch_bytes = 0;
-                    if (e != hipSuccess) return fail(ATTN_ERR_DEVICE, "hipFree: %s", hipGetErrorString(e));
-                }
-                e = hipMalloc(&s.scratch, need);
-                if (e != hipSuccess) {
-                    s.scratch = nullptr;
-                    return fail(ATTN_ERR_DEVICE, "hipMalloc(%zu): %s", need, hipGetErrorString(e));
-                }
-                s.scratch_bytes = need;
-            }
-            p.part = static_cast<float *>(s.scratch);
-        }
-    }
     hipStream_t stream = opts ? static_cast<hipStream_t>(opts->stream) : nullptr;
-    e = eea::launch_forward(p, d, dtype == ATTN_F32, stream);
-    if (e != hipSuccess) return fail(ATTN_ERR_DEVICE, "kernel launch: %s", hipGetErrorString(e));
-    return ATTN_OK;
-}
-
-// Current device, checked to be gfx950, and (when need > 0 and the caller
-// gave no workspace) a per-device scratch buffer of at least `need` bytes,
-// grown under the mutex and never freed while in use by this library.
-int device_and_scratch(size_t need, void **buf, bool backward) {
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return fail(ATTN_ERR_DEVICE, "hipGetDevice: %s", hipGetErrorString(e));
-    std::lock_guard<std::mutex> lk(g_mu);
-    DeviceSlot &s = slot(dev);
-    if (!s.arch_checked) {
-        hipDeviceProp_t prop;
-        e = hipGetDeviceProperties(&prop, dev);
-        if (e != hipSuccess) return fail(ATTN_ERR_DEVICE, "hipGetDeviceProperties: %s", hipGetErrorString(e));
-        s.arch_ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
-        s.arch_checked = 1;
-    }
-    if (!s.arch_ok) return fail(ATTN_ERR_UNSUPPORTED, "device %d is not gfx950 (MI355X)", dev);
-    if (need == 0 || !buf || *buf) return ATTN_OK;
-    void *&ptr = backward ? s.bwd_scratch : s.scratch;
-    size_t &bytes = backward ? s.bwd_scratch_bytes : s.scratch_bytes;
-    if (bytes < need) {
-        if (ptr) {
-            e = hipFree(ptr);
-            ptr = nullptr;
-            bytes = 0;
-            if (e != hipSuccess) return fail(ATTN_ERR_DEVICE, "hipFree: %s", hipGetErrorString(e));
-        }
-        e = hipMalloc(&ptr, need);
-        if (e != hipSuccess) {
-            ptr = nullptr;
-            return fail(ATTN_ERR_DEVICE, "hipMalloc(%zu): %s", need, hipGetErrorString(e));
-        }
-        bytes = need;
-    }
-    *buf = ptr;
-    return ATTN_OK;
+    const int f32 = dtype == ATTN_F32;
+    return run_on_device(SCR_FWD, need, p.part, stream, [&](void *buf) {
+        p.part = static_cast<float *>(buf);
+        return eea::launch_forward(p, d, f32, stream);
+    });
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -615,17 +626,15 @@ int bwd_impl(const void *q, const void *k, const void *v, const void *out, const
     p.rand_idx = m.rand_idx;
 
     // ---- first HIP call
-    rc = device_and_scratch(need, &ws, true);
-    if (rc != ATTN_OK) return rc;
-    p.delta = static_cast<float *>(ws);
-    if (m.ng > 0) {
-        p.part_q = reinterpret_cast<float *>(static_cast<char *>(ws) + lay.part_q);
-        p.part_k = reinterpret_cast<float *>(static_cast<char *>(ws) + lay.part_k);
-    }
     hipStream_t stream = opts ? static_cast<hipStream_t>(opts->stream) : nullptr;
-    hipError_t e = eea::launch_backward(p, d, stream);
-    if (e != hipSuccess) return fail(ATTN_ERR_DEVICE, "kernel launch: %s", hipGetErrorString(e));
-    return ATTN_OK;
+    return run_on_device(SCR_BWD, need, ws, stream, [&](void *buf) {
+        p.delta = static_cast<float *>(buf);
+        if (m.ng > 0) {
+            p.part_q = reinterpret_cast<float *>(static_cast<char *>(buf) + lay.part_q);
+            p.part_k = reinterpret_cast<float *>(static_cast<char *>(buf) + lay.part_k);
+        }
+        return eea::launch_backward(p, d, stream);
+    });
 }
 
 size_t decode_workspace(int B, int H, int H_kv, int Nq, int S, int d, int win_left, int rolling) {
@@ -708,13 +717,11 @@ int decode_impl(const void *q, const void *kc, const void *vc, const int *seq_le
     p.chunks = chunks;
     p.scale_log2 = scale * 1.4426950408889634f;
 
-    int rc = device_and_scratch(need, &ws, true);
-    if (rc != ATTN_OK) return rc;
-    p.part = static_cast<float *>(ws);
     hipStream_t stream = opts ? static_cast<hipStream_t>(opts->stream) : nullptr;
-    hipError_t e = eea::launch_decode(p, d, stream);
-    if (e != hipSuccess) return fail(ATTN_ERR_DEVICE, "kernel launch: %s", hipGetErrorString(e));
-    return ATTN_OK;
+    return run_on_device(SCR_DEC, need, ws, stream, [&](void *buf) {
+        p.part = static_cast<float *>(buf);
+        return eea::launch_decode(p, d, stream);
+    });
 }
 
 }  // namespace

@@ -58,6 +58,19 @@ typedef struct attn_opts {
 } attn_opts;
 
 /*
+ * Library-owned scratch. A call that needs device scratch (forward with
+ * global rows, backward, split decoding) and gets no opts->workspace uses a
+ * buffer the library owns, one per device and per kind (forward, backward,
+ * decoding). It is allocated on first use, grown when a call needs more
+ * (the old buffer is freed once the last call that used it has finished)
+ * and kept until the process ends. Calls that share it are ordered on the
+ * device: each call's stream first waits for the work of the previous call
+ * that used the buffer, whatever stream that was, so calls on different
+ * streams run one after another where they share it. Callers that want
+ * them to overlap pass a workspace of their own to each call.
+ */
+
+/*
  * attn_fwd - masked exact attention forward, bf16 in/out, scale 1/sqrt(d),
  * default stream. Equivalent to attn_fwd_ex(..., NULL).
  *
@@ -95,8 +108,8 @@ int attn_fwd(const void *q, const void *k, const void *v, void *out, float *lse,
  * in fp32 on the matrix cores. When n_global > 0 and the window does not
  * already cover every key, the global query rows are computed by a separate
  * split-key pass that needs attn_workspace_bytes() of device scratch: taken
- * from opts->workspace if given, else from a buffer the library allocates
- * once per device (guarded by a mutex, grown on demand, never freed).
+ * from opts->workspace if given, else from a buffer the library owns (see
+ * "Library-owned scratch" above).
  */
 int attn_fwd_ex(const void *q, const void *k, const void *v, void *out, float *lse,
                 int B, int H, int N, int d, int causal, int win_left, int win_right,
@@ -199,7 +212,7 @@ int attn_fwd_gqa(const void *q, const void *k, const void *v, void *out, float *
  *   opts          as in attn_fwd_ex: only ATTN_BF16 (ATTN_F32 gives
  *                 ATTN_ERR_UNSUPPORTED), scale (must be the forward's),
  *                 stream, and a workspace of at least attn_bwd_workspace_bytes
- *                 (else the library's per-device scratch is used).
+ *                 (else the library-owned backward scratch is used).
  * Errors are reported as for attn_fwd_ex, before any launch.
  */
 int attn_bwd(const void *q, const void *k, const void *v, const void *out, const void *dout,

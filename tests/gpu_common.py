@@ -12,10 +12,15 @@ from efficient_exact_attention_amd import workloads as W
 
 # Pass criteria (all configurations): max-abs and relative L2 over every checked
 # output element, max-abs over checked LSE values; compared in fp64.
-# A bf16 output cannot hold a value of magnitude >= 2.56 to within 1e-2 (half
-# an ulp there exceeds 1e-2: 1.56e-2 in [4, 8)), so for bf16 outputs each
-# element's max-abs bound is 1e-2 plus half a bf16 ulp of the exact value
-# (at most |O| * 2^-8). Only peaked rows with large outputs ever use it.
+# A bf16 output holds 8 significant bits: storing a value y rounds it by up to
+# half a bf16 ulp, 2^(floor(log2 |y|) - 8). That is 3.9e-3 in [1, 2), 7.8e-3 in
+# [2, 4) and 1.56e-2 in [4, 8), so only from |O| >= 4 can no bf16 output be
+# within 1e-2 of the exact value at all. For bf16 outputs the element bound
+# is therefore 1e-2 for the computation plus the half ulp of the stored value
+# (rounding is monotone and powers of two are representable, so the stored
+# value's binade is at least that of the value before rounding: the half ulp
+# is taken at max(|ref|, |got|)). The raw max-abs is always reported, and
+# the benchmark workloads are held to the raw 1e-2 (strict=True).
 TOL_MAXABS = 1e-2
 TOL_RELL2 = 5e-3
 TOL_LSE = 1e-3
@@ -60,10 +65,13 @@ def host_f64(t) -> np.ndarray:
     return t.detach().to(torch.float64).cpu().numpy()
 
 
-def oracle_heads(w: W.Workload, heads, rows, qkv=None):
-    """Oracle output for the listed (b, h) heads and query rows."""
-    outs, lses = [], []
-    for (b, h) in heads:
+def oracle_heads(w: W.Workload, heads, rows, qkv=None, workers=None):
+    """Oracle output for the listed (b, h) heads and query rows. With
+    workers > 1 the heads are computed by a thread pool, the BLAS limited
+    to one thread each (numpy releases the interpreter lock in its array
+    loops and matrix products)."""
+    def one(bh):
+        b, h = bh
         if qkv is not None:
             q, k, v = (W.as_f64(x[b, h], w.dtype) for x in qkv)
         else:
@@ -71,34 +79,65 @@ def oracle_heads(w: W.Workload, heads, rows, qkv=None):
         O, L = oracle.attention(q[None, None], k[None, None], v[None, None], causal=w.causal,
                                 win_left=w.win_left, win_right=w.win_right,
                                 global_idx=w.global_idx, rows=rows)
-        outs.append(O[0, 0])
-        lses.append(L[0, 0])
-    return np.stack(outs), np.stack(lses)
+        return O[0, 0], L[0, 0]
+
+    if workers is None:
+        workers = 1 if len(heads) < 4 else host_workers()
+    if workers <= 1:
+        res = [one(bh) for bh in heads]
+    else:
+        from concurrent.futures import ThreadPoolExecutor
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1, user_api="blas"), ThreadPoolExecutor(workers) as ex:
+            res = list(ex.map(one, heads))
+    return np.stack([r[0] for r in res]), np.stack([r[1] for r in res])
+
+
+def host_workers() -> int:
+    """Threads for the oracle: the host cores this process may use, at most 16."""
+    import os
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def bf16_half_ulp(x: np.ndarray) -> np.ndarray:
+    """Half the spacing of bf16 values around |x| (0 where x == 0)."""
+    ax = np.abs(x)
+    e = np.floor(np.log2(np.where(ax > 0, ax, 1.0)))
+    return np.where(ax > 0, np.exp2(e - 8), 0.0)
 
 
 def errors(got_o, got_l, ref_o, ref_l, bf16_out=False):
-    """(max-abs excess over the bf16 output's own rounding, rel-L2, LSE max-abs).
-    For fp32 outputs the first value is the plain max-abs error."""
-    diff = got_o - ref_o
-    widen = np.abs(ref_o) * 2.0 ** -8 if bf16_out else 0.0
-    maxabs = float(np.max(np.abs(diff) - widen))
-    rel = float(np.linalg.norm(diff) / max(np.linalg.norm(ref_o), 1e-300))
-    lse = float(np.max(np.abs(got_l - ref_l)))
-    return maxabs, rel, lse
+    """(max-abs beyond the bf16 output's own rounding, rel-L2, LSE max-abs,
+    raw max-abs). For fp32 outputs the first value is the raw max-abs."""
+    diff = np.abs(got_o - ref_o)
+    raw = float(np.max(diff)) if diff.size else 0.0
+    if bf16_out:
+        widen = bf16_half_ulp(np.maximum(np.abs(ref_o), np.abs(got_o)))
+        maxabs = float(np.max(diff - widen)) if diff.size else 0.0
+    else:
+        maxabs = raw
+    rel = float(np.linalg.norm(got_o - ref_o) / max(np.linalg.norm(ref_o), 1e-300))
+    lse = float(np.max(np.abs(got_l - ref_l))) if got_l.size else 0.0
+    return maxabs, rel, lse, raw
 
 
-def check(w: W.Workload, o, l, heads, rows, qkv=None, tol=(TOL_MAXABS, TOL_RELL2, TOL_LSE)):
-    ref_o, ref_l = oracle_heads(w, heads, rows, qkv)
+def check(w: W.Workload, o, l, heads, rows, qkv=None, tol=(TOL_MAXABS, TOL_RELL2, TOL_LSE), strict=False,
+          workers=None):
+    """Compare the GPU output of `heads` x `rows` with the oracle. strict:
+    the raw max-abs (no allowance for the bf16 output rounding) must meet
+    tol[0] too."""
+    ref_o, ref_l = oracle_heads(w, heads, rows, qkv, workers=workers)
     go = np.stack([host_f64(o[b, h, rows]) for (b, h) in heads])
     gl = np.stack([host_f64(l[b, h, rows]) for (b, h) in heads])
     assert np.all(np.isfinite(go)) and np.all(np.isfinite(gl)), "non-finite output"
     e = errors(go, gl, ref_o, ref_l, bf16_out=w.dtype == "bf16")
-    raw = float(np.max(np.abs(go - ref_o)))
-    say(f"    {w.name}: max-abs {raw:.3e} (beyond bf16 output rounding {e[0]:.3e})  "
+    say(f"    {w.name}: raw max-abs {e[3]:.3e} (beyond bf16 output rounding {e[0]:.3e})  "
         f"rel-L2 {e[1]:.3e}  lse {e[2]:.3e}  ({len(heads)} heads x {len(rows)} rows)")
     assert e[0] <= tol[0], e
     assert e[1] <= tol[1], e
     assert e[2] <= tol[2], e
+    if strict:
+        assert e[3] <= tol[0], e
     return e
 
 

@@ -45,7 +45,7 @@ def _run(B, H, H_kv, N, d, mask, dtype="bf16", seed=1, rows=None):
                                     rows=rows, **mask)
     go, gl = host_f64(o[:, :, rows]), host_f64(l[:, :, rows])
     e = errors(go, gl, ref_o, ref_l, bf16_out=dtype == "bf16")
-    say(f"    max-abs {float(np.max(np.abs(go - ref_o))):.3e} rel-L2 {e[1]:.3e} lse {e[2]:.3e}")
+    say(f"    raw max-abs {e[3]:.3e} (beyond bf16 rounding {e[0]:.3e}) rel-L2 {e[1]:.3e} lse {e[2]:.3e}")
     tol = (1e-2, 5e-3, 1e-3) if dtype == "bf16" else (1e-4, 1e-5, 1e-4)
     assert e[0] <= tol[0] and e[1] <= tol[1] and e[2] <= tol[2], e
     return o, l

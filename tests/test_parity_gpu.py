@@ -110,45 +110,59 @@ def test_narrow_band_threshold(wl, wr, causal):
 
 
 # ---- the benchmark workloads at full size ---------------------------------------------
+# Held to the literal bound (raw max-abs <= 1e-2, no allowance for the bf16
+# output rounding). Every row of every head where the oracle can afford it
+# (the N=256 fp32, B=4 N=4096 causal and band + globals workloads); at
+# least 512 seeded rows per head plus tile, window and edge rows for the
+# N=32768 workloads; 256 per head for N=131072.
+
+def _edge_rows(w, *extra):
+    rows = set()
+    for bm in (128, 256):
+        rows |= {bm - 1, bm, 2 * bm - 1, 2 * bm}
+    rows |= {0, 1, w.N // 2 - 1, w.N // 2, w.N - 2, w.N - 1}
+    rows |= set(int(x) for x in extra)
+    return np.array(sorted(r for r in rows if 0 <= r < w.N), dtype=np.int64)
+
 
 def test_f32_causal_256_all_rows():
     w = W.WORKLOADS["f32_causal_256"]
     qkv = W.make_qkv(w)
     o, l = run_gpu(w, qkv)
-    check(w, o, l, all_heads(w), np.arange(w.N), qkv)
+    check(w, o, l, all_heads(w), np.arange(w.N), qkv, strict=True)
 
 
-def test_causal_4k_b4():
+def test_causal_4k_b4_all_rows():
     w = W.WORKLOADS["causal_4k_b4"]
-    o, l = run_gpu(w)
-    check(w, o, l, some_heads(w, 16), W.sample_rows(w, 96))
+    qkv = W.make_qkv(w)
+    o, l = run_gpu(w, qkv)
+    check(w, o, l, all_heads(w), np.arange(w.N), qkv, strict=True)
 
 
 def test_swa4096_32k():
     w = W.WORKLOADS["swa4096_32k"]
     o, l = run_gpu(w)
-    rows = np.union1d(W.sample_rows(w, 48), np.array([4094, 4095, 4096, 4097, 8191, 8192]))
-    check(w, o, l, some_heads(w, 8), rows)
+    rows = np.union1d(W.sample_rows(w, 512), _edge_rows(w, 4094, 4095, 4096, 4097, 8191, 8192, 4159, 4160))
+    check(w, o, l, all_heads(w), rows, strict=True)
 
 
 def test_causal_131k_rows():
     w = W.WORKLOADS["causal_131k"]
     o, l = run_gpu(w)
-    check(w, o, l, all_heads(w), W.sample_rows(w, 40))
+    check(w, o, l, all_heads(w), np.union1d(W.sample_rows(w, 256), _edge_rows(w)), strict=True)
 
 
-def test_band256_globals_16k():
+def test_band256_globals_16k_all_rows():
     w = W.WORKLOADS["band256_globals_16k"]
-    o, l = run_gpu(w)
-    rows = np.union1d(W.sample_rows(w, 64),
-                      np.array([2, 255, 256, 257, 2047, 2049, 2304, 2305, 16127, 16128, 16383]))
-    check(w, o, l, some_heads(w, 8), rows)
+    qkv = W.make_qkv(w)
+    o, l = run_gpu(w, qkv)
+    check(w, o, l, all_heads(w), np.arange(w.N), qkv, strict=True)
 
 
 def test_causal_32k():
     w = W.WORKLOADS["causal_32k"]
     o, l = run_gpu(w)
-    check(w, o, l, some_heads(w, 6), W.sample_rows(w, 48))
+    check(w, o, l, all_heads(w), np.union1d(W.sample_rows(w, 512), _edge_rows(w)), strict=True)
 
 
 def test_band256_globals_alternative_reading():
@@ -168,7 +182,8 @@ def test_constant_v():
     v = np.broadcast_to(c, v.shape).copy()
     o, _ = run_gpu(w, (q, k, v))
     want = W.bf16_bits_to_f32(c).astype(np.float64)
-    assert np.max(np.abs(host_f64(o) - want) - np.abs(want) * 2.0 ** -8) <= 1e-2
+    # the exact output is each bf16 value of c itself, representable: 1e-2 raw
+    assert np.max(np.abs(host_f64(o) - want)) <= 1e-2
 
 
 def test_identical_keys():
