@@ -9,7 +9,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["AttnError", "attn_fwd", "attn_fwd_ex", "attn_fwd_gqa", "attn_fwd_masked", "attn_bwd", "attn_bwd_masked",
+__all__ = ["AttnError", "attn_fwd", "attn_fwd_ex", "attn_fwd_noalloc", "ATTN_NOALLOC_SCRATCH_BYTES", "attn_fwd_gqa", "attn_fwd_masked", "attn_bwd", "attn_bwd_masked",
            "attn_bwd_workspace_bytes", "attn_plan_stats_masked", "bwd", "attn_decode",
            "attn_decode_workspace_bytes", "decode", "attn_workspace_bytes", "attn_plan_stats",
            "attn_tile_shape", "attn_last_error", "attn_version", "fwd", "library_path",
@@ -18,6 +18,7 @@ __all__ = ["AttnError", "attn_fwd", "attn_fwd_ex", "attn_fwd_gqa", "attn_fwd_mas
 
 ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_DEVICE = 0, 1, 2, 3
 ATTN_BF16, ATTN_F32 = 0, 1
+ATTN_NOALLOC_SCRATCH_BYTES = 16 << 20   # include/attn.h
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libattn.so")
@@ -74,6 +75,8 @@ def lib():
     L.attn_fwd.restype = ci
     L.attn_fwd_ex.argtypes = fwd_args + [ctypes.POINTER(_Opts)]
     L.attn_fwd_ex.restype = ci
+    L.attn_fwd_noalloc.argtypes = fwd_args + [ctypes.POINTER(_Opts)]
+    L.attn_fwd_noalloc.restype = ci
     L.attn_fwd_gqa.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, ci, ctypes.POINTER(ci), ci,
                                ctypes.POINTER(_Opts)]
     L.attn_fwd_gqa.restype = ci
@@ -142,6 +145,15 @@ def attn_fwd_ex(q, k, v, out, lse, B, H, N, d, causal, win_left, win_right, glob
     opts = _Opts(dtype, float(scale), stream, workspace, workspace_bytes)
     _check(lib().attn_fwd_ex(q, k, v, out, lse, B, H, N, d, causal, win_left, win_right, g, ng,
                              ctypes.byref(opts)))
+
+
+def attn_fwd_noalloc(q, k, v, out, lse, B, H, N, d, causal, win_left, win_right, global_idx=None,
+                     *, dtype=ATTN_BF16, scale=0.0, stream=None):
+    """Raw allocation-free entry point (no workspace): pointers and stream are integers."""
+    g, ng = _gidx(global_idx)
+    opts = _Opts(dtype, float(scale), stream, None, 0)
+    _check(lib().attn_fwd_noalloc(q, k, v, out, lse, B, H, N, d, causal, win_left, win_right, g, ng,
+                                  ctypes.byref(opts)))
 
 
 def attn_fwd_gqa(q, k, v, out, lse, B, H, H_kv, N, d, causal, win_left, win_right, global_idx=None,

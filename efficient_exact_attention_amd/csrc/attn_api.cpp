@@ -391,7 +391,7 @@ namespace {
 // multi-head attention).
 int fwd_impl(const void *q, const void *k, const void *v, void *out, float *lse, int B, int H, int H_kv, int N,
              int d, int causal, int win_left, int win_right, int block, int dilation, const int *global_idx,
-             int n_global, const attn_opts *opts, const attn_mask *extras = nullptr) {
+             int n_global, const attn_opts *opts, const attn_mask *extras = nullptr, bool noalloc = false) {
     g_err.clear();
     const int dtype = opts ? opts->dtype : ATTN_BF16;
     if (!q || !k || !v || !out || !lse) return fail(ATTN_ERR_INVALID_ARG, "a tensor pointer is NULL");
@@ -474,6 +474,10 @@ int fwd_impl(const void *q, const void *k, const void *v, void *out, float *lse,
         p.chunks = eea::global_chunks((int)BH, N, d, dtype == ATTN_F32, &ct);
         p.chunk_tiles = ct;
         need = (size_t)BH * ng * p.chunks * (d + 2) * sizeof(float);
+        if (noalloc && need > eea::kNoAllocScratchBytes)
+            return fail(ATTN_ERR_UNSUPPORTED,
+                        "attn_fwd_noalloc: the global-row partials need %zu bytes, more than its %zu-byte scratch", need,
+                        eea::kNoAllocScratchBytes);
         if (opts && opts->workspace) {
             if (opts->workspace_bytes < need)
                 return fail(ATTN_ERR_INVALID_ARG, "workspace of %zu bytes is smaller than the %zu needed",
@@ -484,9 +488,18 @@ int fwd_impl(const void *q, const void *k, const void *v, void *out, float *lse,
         }
     }
 
+    if (noalloc && opts && opts->workspace)
+        return fail(ATTN_ERR_INVALID_ARG, "attn_fwd_noalloc takes no workspace (opts->workspace must be NULL)");
+
     // ---- first HIP call
     hipStream_t stream = opts ? static_cast<hipStream_t>(opts->stream) : nullptr;
     const int f32 = dtype == ATTN_F32;
+    if (noalloc && ng > 0) {
+        void *buf = nullptr;
+        hipError_t e = eea::noalloc_scratch(&buf);
+        if (e != hipSuccess) return fail(ATTN_ERR_DEVICE, "scratch address: %s", hipGetErrorString(e));
+        p.part = static_cast<float *>(buf);
+    }
     return run_on_device(SCR_FWD, need, p.part, stream, [&](void *buf) {
         p.part = static_cast<float *>(buf);
         return eea::launch_forward(p, d, f32, stream);
@@ -788,6 +801,13 @@ int attn_fwd_masked(const void *q, const void *k, const void *v, void *out, floa
     }
     return fwd_impl(q, k, v, out, lse, B, H, H_kv, N, d, mask->causal, mask->win_left, mask->win_right,
                     mask->block, mask->dilation, mask->global_idx, mask->n_global, opts, mask);
+}
+
+int attn_fwd_noalloc(const void *q, const void *k, const void *v, void *out, float *lse, int B, int H, int N,
+                     int d, int causal, int win_left, int win_right, const int *global_idx, int n_global,
+                     const attn_opts *opts) {
+    return fwd_impl(q, k, v, out, lse, B, H, H, N, d, causal, win_left, win_right, 0, 1, global_idx, n_global,
+                    opts, nullptr, true);
 }
 
 int attn_fwd(const void *q, const void *k, const void *v, void *out, float *lse, int B, int H, int N, int d,

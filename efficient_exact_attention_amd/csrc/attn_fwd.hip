@@ -47,6 +47,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+#include <vector>
+
 #include "attn_internal.h"
 #include "attn_plan.h"
 #include "attn_tiles.h"
@@ -1039,6 +1042,34 @@ static hipError_t launch_impl(const FwdParams &p0, hipStream_t stream) {
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((merge_kernel<D, F32>), dim3(p.BH * p.n_global), dim3(64), 0, stream, p);
     return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Scratch of the allocation-free forward (attn_fwd_noalloc): the global-row
+// partials of callers that cannot allocate device memory. One copy of the
+// array per device, from module load to the end of the process; every call
+// on a device uses the same memory, so calls that overlap on one device race.
+// Host code uses the address hipGetSymbolAddress returns for the current
+// device, never the array's name.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+hipError_t noalloc_scratch(void **ptr) {
+    static std::mutex mu;
+    static std::vector<void *> addr;   // per device, looked up once
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lk(mu);
+    if ((int)addr.size() <= dev) addr.resize(dev + 1, nullptr);
+    if (!addr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
 }
 
 hipError_t launch_forward(const FwdParams &p, int d, int f32, hipStream_t stream) {

@@ -8,6 +8,9 @@
 namespace eea {
 
 constexpr int kMaxGlobal = 64;       // one gathered key tile holds every global column
+// Bytes of the file-scope device array attn_fwd_noalloc keeps its global-row
+// partials in (one per device, for the life of the process).
+constexpr size_t kNoAllocScratchBytes = (size_t)16 << 20;
 constexpr int kMaxGlobalChunks = 512; // key chunks of the split-key pass over global rows
 
 // Kernel arguments. Offsets are 64-bit throughout: one head at N=131072, d=128
@@ -119,5 +122,9 @@ hipError_t launch_forward(const FwdParams &p, int d, int f32, hipStream_t stream
 
 // Number of key chunks the split-key pass uses for these sizes.
 int global_chunks(int BH, int N, int d, int f32, int *chunk_tiles);
+
+// Device address, on the current device, of the allocation-free forward's
+// scratch array (kNoAllocScratchBytes); looked up once per device.
+hipError_t noalloc_scratch(void **ptr);
 
 }  // namespace eea

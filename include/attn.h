@@ -116,6 +116,33 @@ int attn_fwd_ex(const void *q, const void *k, const void *v, void *out, float *l
                 const int *global_idx, int n_global, const attn_opts *opts);
 
 /*
+ * attn_fwd_noalloc - attn_fwd_ex that allocates no device memory, for callers
+ * that cannot allocate: code being captured into a HIP graph, tight serving
+ * loops, harnesses that forbid allocation. Arguments, outputs and errors are
+ * those of attn_fwd_ex, except:
+ *   - opts->workspace must be NULL (else ATTN_ERR_INVALID_ARG): the
+ *     global-row partials go to a device array built into the library, one
+ *     per device, ATTN_NOALLOC_SCRATCH_BYTES long, held from library load
+ *     until the process ends;
+ *   - a call whose global-row partials (attn_workspace_bytes) need more than
+ *     ATTN_NOALLOC_SCRATCH_BYTES returns ATTN_ERR_UNSUPPORTED before any
+ *     device work;
+ *   - every call on one device uses the same array: calls that overlap on a
+ *     device (different streams, no ordering between them) race and give
+ *     wrong results. Order them, or use attn_fwd_ex with a workspace each.
+ * Calls without global tokens need no scratch and are exactly attn_fwd_ex.
+ * No hipMalloc, hipFree or other allocating call is made. The array is part
+ * of the library's device code, which the HIP runtime loads (allocating it)
+ * at the first launch of any of the library's kernels on a device, and the
+ * first attn_fwd_noalloc call on a device looks up its address: make one
+ * call (of any entry point, then of this one) before capturing a graph.
+ */
+#define ATTN_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+int attn_fwd_noalloc(const void *q, const void *k, const void *v, void *out, float *lse,
+                     int B, int H, int N, int d, int causal, int win_left, int win_right,
+                     const int *global_idx, int n_global, const attn_opts *opts);
+
+/*
  * attn_mask - which (query row i, key j) pairs are visible, as one
  * descriptor. The local rule is one of
  *   window (block = 0, dilation <= 1): i - win_left <= j <= i + win_right,

@@ -499,3 +499,33 @@ def test_strided_plan_pairs_match_oracle(N, m):
     pairs = ea.attn_plan_stats_masked(N, 128, 64, **mm)[0]
     ref = oracle.visible_pairs_bruteforce(N, m["causal"], m["win_left"], m["win_right"], tuple(G), stride=m["stride"])
     assert pairs == ref
+
+
+# ---- the allocation-free forward: its own limits, checked before any HIP call ---------
+
+def test_noalloc_rejects_a_workspace():
+    L = ea.lib()
+    opts = ea._Opts(ea.ATTN_BF16, 0.0, None, FAKE + (3 << 32), 1 << 20)
+    g = (ctypes.c_int * 1)(5)
+    rc = L.attn_fwd_noalloc(FAKE, FAKE, FAKE, FAKE + (1 << 32), FAKE + (2 << 32), 1, 2, 100, 128, 0, 3, 3, g, 1,
+                            ctypes.byref(opts))
+    assert rc == ea.ATTN_ERR_INVALID_ARG and "workspace" in ea.attn_last_error()
+
+
+def test_noalloc_rejects_more_partials_than_its_array():
+    """4096 heads x 64 global rows of partials: far beyond the built-in array."""
+    L = ea.lib()
+    B, H, N, d = 64, 64, 640, 128
+    need = ea.attn_workspace_bytes(B, H, N, d, 64)
+    assert need > ea.ATTN_NOALLOC_SCRATCH_BYTES
+    g = (ctypes.c_int * 64)(*range(0, 640, 10))
+    big = 1 << 36   # tensors of this call are ~1.3 GB: keep the fake ranges apart
+    rc = L.attn_fwd_noalloc(FAKE, FAKE, FAKE, FAKE + big, FAKE + 2 * big, B, H, N, d, 0, 3, 3, g, 64, None)
+    assert rc == ea.ATTN_ERR_UNSUPPORTED, ea.attn_last_error()
+    assert "attn_fwd_noalloc" in ea.attn_last_error()
+
+
+def test_noalloc_limit_matches_header():
+    src = open(HEADER).read()
+    m = re.search(r"#define ATTN_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", src)
+    assert m and int(m.group(1)) << int(m.group(2)) == ea.ATTN_NOALLOC_SCRATCH_BYTES
