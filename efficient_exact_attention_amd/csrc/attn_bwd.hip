@@ -35,7 +35,6 @@
 namespace eea {
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kBwdThreads = 256;   // 4 waves, one per SIMD (up to 512 registers each) or two per SIMD
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
@@ -1199,20 +1198,6 @@ __global__ void __launch_bounds__(64) bwd_merge_dkdv(const BwdParams prm) {
         dk[d] = (__bf16)((float)dk[d] + ak * prm.scale);
         dv[d] = (__bf16)((float)dv[d] + av);
     }
-}
-
-int bwd_tile_q(int d, int band_only) { return 32 * ((d == 128 && band_only) ? 512 : kBwdThreads) / 64; }
-int bwd_tile_k(int d) { (void)d; return 32 * (kBwdThreads / 64); }
-
-// Chunks of the split passes: a few hundred workgroups in all.
-void bwd_global_chunks(int units, int N, int *chunks, int *tiles_per_chunk) {
-    const int tiles = (N + 63) / 64;
-    int target = (512 + units - 1) / units;
-    if (target < 1) target = 1;
-    if (target > tiles) target = tiles;
-    const int ct = (tiles + target - 1) / target;
-    *tiles_per_chunk = ct;
-    *chunks = (tiles + ct - 1) / ct;
 }
 
 template <int D>

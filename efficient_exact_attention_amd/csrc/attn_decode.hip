@@ -24,9 +24,6 @@
 
 namespace eea {
 
-constexpr int kDecThreads = 256;     // four waves of 32 query rows each
-constexpr int kDecLds = 163840;      // the whole LDS of a CU: one workgroup per CU
-constexpr int kDecCUs = 256;         // compute units of an MI355X
 
 // s_waitcnt vmcnt(C) leaving the other counters alone (gfx9 encoding).
 template <int C>
@@ -349,30 +346,6 @@ __global__ void __launch_bounds__(64) decode_merge(const DecParams prm) {
 #pragma unroll
     for (int j = 0; j < PER; ++j) static_cast<__bf16 *>(prm.out)[grow * D + lane + 64 * j] = (__bf16)(acc[j] * inv);
     if (lane == 0) prm.lse[grow] = Ls > 0.f ? (M + __log2f(Ls)) * kLn2 : EEA_NEG_INF;
-}
-
-// Chunks per row group. Each CU runs one workgroup at a time, so the cost
-// of a split is (rounds of kDecCUs workgroups) x (tiles per chunk + a
-// pipeline fill of about kFillTiles tiles); take the cheapest split.
-int decode_chunks(int B, int H_kv, int nrg, int S, int Nq, int win, int rolling) {
-    constexpr int kFillTiles = 3;
-    long long tiles = (S + 63) / 64;
-    if (!rolling && win >= 0) {
-        const long long span = ((long long)Nq + win + 63) / 64 + 1;   // window slots, any alignment
-        tiles = tiles < span ? tiles : span;
-    }
-    const long long units = (long long)B * H_kv * nrg;
-    const long long cmax = tiles < kDecMaxChunks ? tiles : kDecMaxChunks;
-    long long best = 1, best_cost = -1;
-    for (long long c = 1; c <= cmax; ++c) {
-        const long long rounds = (units * c + kDecCUs - 1) / kDecCUs;
-        const long long cost = rounds * ((tiles + c - 1) / c + kFillTiles);
-        if (best_cost < 0 || cost < best_cost) {
-            best = c;
-            best_cost = cost;
-        }
-    }
-    return (int)best;
 }
 
 template <int D>

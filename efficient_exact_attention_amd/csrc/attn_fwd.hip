@@ -971,42 +971,6 @@ __global__ void __launch_bounds__(64) merge_kernel(const FwdParams prm) {
 // ---------------------------------------------------------------------------
 // Host-side launch.
 // ---------------------------------------------------------------------------
-constexpr int kBandThreadsBf16 = 512;   // 8 waves, 256 query rows
-constexpr int kBandThreadsF32 = 256;    // 4 waves, 128 query rows
-constexpr int kBandThreadsBlock = 256;  // bf16 with the block rule or extra tiles: 4 waves, 128 query rows
-constexpr int kBandThreadsNarrow = 256; // bf16 narrow band: 4 waves, 128 query rows, two workgroups per CU
-constexpr int kNarrowBand = 4096;       // widest band (keys per row) run by the narrow instance
-
-int tile_bm(int d, int f32) { (void)d; return 32 * ((f32 ? kBandThreadsF32 : kBandThreadsBf16) / 64); }
-// A bounded band of at most kNarrowBand keys per row: 256-row workgroups
-// would carry several key tiles that some of their waves skip (a wave's 32
-// rows see only a slice of the workgroup's key range), and a short loop
-// leaves the copy-in of the first tiles exposed. Four-wave workgroups, two
-// per CU, lose less of both (measured: 11-19 % faster for bands of 128 to
-// 1024 keys, even at 4096, 2.5 % slower on unbounded causal rows).
-bool band_is_narrow(int wl, int wr, int dil) { return dil == 1 && wl >= 0 && wr >= 0 && wl + wr + 1 <= kNarrowBand; }
-int band_tile_bm(int d, int f32, int block, int extra, int wl, int wr, int dil) {
-    if (f32) return tile_bm(d, f32);
-    if (block > 0 || extra) return 32 * (kBandThreadsBlock / 64);
-    if (band_is_narrow(wl, wr, dil)) return 32 * (kBandThreadsNarrow / 64);
-    return tile_bm(d, f32);
-}
-int tile_bn(int d, int f32) { (void)d; return f32 ? 32 : 64; }
-
-int global_chunks(int BH, int N, int d, int f32, int *chunk_tiles) {
-    const int bn = tile_bn(d, f32);
-    const int num_kt = (N + bn - 1) / bn;
-    // aim for a few hundred workgroups in the split-key pass (at most
-    // kMaxGlobalChunks chunks: the merge keeps one weight per chunk in LDS)
-    int target = (kMaxGlobalChunks + BH - 1) / BH;
-    if (target < 1) target = 1;
-    if (target > num_kt) target = num_kt;
-    int ct = (num_kt + target - 1) / target;
-    if (ct < 1) ct = 1;
-    if (chunk_tiles) *chunk_tiles = ct;
-    return (num_kt + ct - 1) / ct;
-}
-
 template <class PB, class PG64, class PG128, int D, bool F32>
 static hipError_t launch_impl(const FwdParams &p0, hipStream_t stream) {
     FwdParams p = p0;

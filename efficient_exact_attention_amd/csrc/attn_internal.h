@@ -1,5 +1,7 @@
-// attn_internal.h - parameter block and launcher entry points shared between
-// the C ABI (attn_api.cpp) and the HIP kernels (attn_fwd.hip).
+// attn_internal.h - parameter blocks, workgroup shapes and launcher entry
+// points shared between the C ABI (attn_api.cpp), the host planner
+// (attn_host.cpp) and the HIP kernels (attn_fwd.hip, attn_bwd.hip,
+// attn_decode.hip).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -12,6 +14,18 @@ constexpr int kMaxGlobal = 64;       // one gathered key tile holds every global
 // partials in (one per device, for the life of the process).
 constexpr size_t kNoAllocScratchBytes = (size_t)16 << 20;
 constexpr int kMaxGlobalChunks = 512; // key chunks of the split-key pass over global rows
+
+// Workgroup shapes. The kernels are instantiated with these, and the host
+// planner (attn_host.cpp) derives tile sizes and grids from the same values.
+constexpr int kBandThreadsBf16 = 512;   // 8 waves, 256 query rows
+constexpr int kBandThreadsF32 = 256;    // 4 waves, 128 query rows
+constexpr int kBandThreadsBlock = 256;  // bf16 with the block rule or extra tiles: 4 waves, 128 query rows
+constexpr int kBandThreadsNarrow = 256; // bf16 narrow band: 4 waves, 128 query rows, two workgroups per CU
+constexpr int kNarrowBand = 4096;       // widest band (keys per row) run by the narrow instance
+constexpr int kBwdThreads = 256;        // backward: 4 waves, one per SIMD (up to 512 registers each) or two per SIMD
+constexpr int kDecThreads = 256;        // decoding: four waves of 32 query rows each
+constexpr int kDecLds = 163840;         // decoding uses the whole LDS of a CU: one workgroup per CU
+constexpr int kDecCUs = 256;            // compute units of an MI355X
 
 // Kernel arguments. Offsets are 64-bit throughout: one head at N=131072, d=128
 // is 2^24 elements and B*H*N*d can exceed 2^31.
