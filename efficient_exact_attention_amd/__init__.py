@@ -12,7 +12,8 @@ import os
 __all__ = ["AttnError", "attn_fwd", "attn_fwd_ex", "attn_fwd_noalloc", "ATTN_NOALLOC_SCRATCH_BYTES", "attn_fwd_gqa", "attn_fwd_masked", "attn_bwd", "attn_bwd_masked",
            "attn_bwd_workspace_bytes", "attn_plan_stats_masked", "bwd", "attn_decode",
            "attn_decode_workspace_bytes", "decode", "attn_workspace_bytes", "attn_plan_stats",
-           "attn_tile_shape", "attn_last_error", "attn_version", "fwd", "library_path",
+           "attn_tile_shape", "attn_last_error", "attn_version", "fwd", "library_path", "open_library",
+           "DEBUG_SYNC_LIB_PATH",
            "ATTN_OK", "ATTN_ERR_INVALID_ARG", "ATTN_ERR_UNSUPPORTED", "ATTN_ERR_DEVICE",
            "ATTN_BF16", "ATTN_F32"]
 
@@ -22,6 +23,9 @@ ATTN_NOALLOC_SCRATCH_BYTES = 16 << 20   # include/attn.h
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libattn.so")
+# The same sources built with -DATTN_DEBUG_SYNC (copies and compute never
+# overlap); only the tests load it, to compare with libattn.so bit for bit.
+DEBUG_SYNC_LIB_PATH = os.path.join(_HERE, "libattn_debugsync.so")
 _lib = None
 
 
@@ -63,12 +67,19 @@ def library_path() -> str:
 def lib():
     """Load libattn.so (raises if it has not been built)."""
     global _lib
-    if _lib is not None:
-        return _lib
-    if not os.path.exists(_LIB_PATH):
-        raise RuntimeError(f"{_LIB_PATH} is missing: build it with "
+    if _lib is None:
+        _lib = open_library(_LIB_PATH)
+    return _lib
+
+
+def open_library(path):
+    """Load a build of the library at `path` with the argument types of
+    include/attn.h (raises if the file is missing). lib() uses it for the
+    shipped libattn.so; the debug-sync build opens through it too."""
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
                            "`python -m efficient_exact_attention_amd.build`")
-    L = ctypes.CDLL(_LIB_PATH)
+    L = ctypes.CDLL(path)
     vp, ci = ctypes.c_void_p, ctypes.c_int
     fwd_args = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, ctypes.POINTER(ci), ci]
     L.attn_fwd.argtypes = fwd_args
@@ -108,7 +119,6 @@ def lib():
     L.attn_last_error.restype = ctypes.c_char_p
     L.attn_version.argtypes = []
     L.attn_version.restype = ctypes.c_char_p
-    _lib = L
     return L
 
 

@@ -15,6 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libattn.so")
+DEBUG_SYNC_LIB = os.path.join(PKG, "libattn_debugsync.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["attn_api.cpp", "attn_host.cpp", "attn_fwd.hip", "attn_bwd.hip", "attn_decode.hip"]
@@ -24,11 +25,12 @@ DEVICE_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
                 "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
-def build(verbose: bool = False, extra_flags=()) -> str:
-    """Compile every source to an object (in parallel), then link libattn.so."""
+def build(verbose: bool = False, extra_flags=(), out: str = LIB, link_flags=()) -> str:
+    """Compile every source to an object (in parallel), then link `out`
+    (libattn.so by default)."""
     import tempfile
     from concurrent.futures import ThreadPoolExecutor
-    tmp = LIB + ".tmp"
+    tmp = out + ".tmp"
     with tempfile.TemporaryDirectory() as objdir:
         def compile_one(src):
             obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
@@ -44,15 +46,25 @@ def build(verbose: bool = False, extra_flags=()) -> str:
 
         with ThreadPoolExecutor(len(SOURCES)) as ex:
             objs = list(ex.map(compile_one, SOURCES))
-        cmd = [HIPCC, *DEVICE_FLAGS, *extra_flags, "-shared", *objs, "-o", tmp]
+        cmd = [HIPCC, *DEVICE_FLAGS, *extra_flags, "-shared", *link_flags, *objs, "-o", tmp]
         if verbose:
             print(" ".join(cmd), flush=True)
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             sys.stderr.write(r.stdout + r.stderr)
             raise RuntimeError(f"hipcc link failed with status {r.returncode}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
+
+
+def build_debug_sync(verbose: bool = False) -> str:
+    """The debug-sync library libattn_debugsync.so: the same sources with
+    -DATTN_DEBUG_SYNC, so that every pipelined copy into LDS is fenced by a
+    full wait and a workgroup barrier on both sides. Only tests load it, next
+    to libattn.so in one process; -Bsymbolic binds its own internal calls to
+    its own definitions."""
+    return build(verbose, extra_flags=("-DATTN_DEBUG_SYNC",), out=DEBUG_SYNC_LIB,
+                 link_flags=("-Wl,-Bsymbolic",))
 
 
 def kernel_resources(sources=None) -> dict:
@@ -92,3 +104,4 @@ def kernel_resources(sources=None) -> dict:
 
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build_debug_sync(verbose=True))

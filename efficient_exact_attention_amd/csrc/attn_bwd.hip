@@ -469,10 +469,12 @@ __global__ void __launch_bounds__(kBwdThreads, (dkdv_waves<D, MODE, XT>())) bwd_
                         char *nok, char *nov, int sb) __attribute__((always_inline)) {
             const bool more = t + 1 < T;
             float nl2 = 0.f, ndl = 0.f;
+            debug_sync();
             if (more) {
                 issue(t + 1, nqk, nqv, nok, nov);
                 row_terms(t + 1, nl2, ndl);
             }
+            debug_sync();
             const int q0 = tile_of(t) * BQ;
             if constexpr (MODE == BWD_GSET) {
                 // set S2: rows outside the key's band, not global, causal cut
@@ -543,11 +545,13 @@ __global__ void __launch_bounds__(kBwdThreads, (dkdv_waves<D, MODE, XT>())) bwd_
                          const char *qv_p, const char *ov_p, int sb) __attribute__((always_inline)) {
             const bool more = t + 1 < T;
             float nl2 = 0.f, ndl = 0.f;
+            debug_sync();
             if (more) {
                 issue_rows(t + 1, nqk, nok);
                 row_terms(t + 1, nl2, ndl);
             }
             issue_tr(t, qv_t, ov_t);
+            debug_sync();
             const int q0 = tile_of(t) * BQ;
             const int q1 = imin(N - 1, q0 + BQ - 1);
             int cl = wave_active ? classify(band, q0, q1, k0w, k1w) : TILE_SKIP;
@@ -977,7 +981,9 @@ __global__ void __launch_bounds__((dq_threads<D, MODE, XT>()), dq_waves<D>()) bw
     };
     auto step = [&](int kt, const char *kk, const char *kv, const char *vk, char *nkk, char *nkv, char *nvk)
         __attribute__((always_inline)) {
+        debug_sync();
         if (kt < kt_hi) issue(kt + 1, nkk, nkv, nvk);
+        debug_sync();
         const int k0 = kt * BN;
         if constexpr (MODE == BWD_GSET) {
             // set S3: keys outside the global row's band, causal cut
@@ -1019,8 +1025,10 @@ __global__ void __launch_bounds__((dq_threads<D, MODE, XT>()), dq_waves<D>()) bw
         };
         auto pstep = [&](int kt, const char *kk, const char *vk, char *nkk, char *nvk, char *kv_t, const char *kv_p)
             __attribute__((always_inline)) {
+            debug_sync();
             if (kt < kt_hi) issue_rows(kt + 1, nkk, nvk);
             P::issue_v(L, kh, N, kv_t, kt * BN, dil);
+            debug_sync();
             const int k0 = kt * BN;
             const int cl = wave_active ? classify(band, wr0, wr1, k0, k0 + BN - 1) : TILE_SKIP;
             const bool act = cl != TILE_SKIP;

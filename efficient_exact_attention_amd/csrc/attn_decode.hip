@@ -255,6 +255,7 @@ __global__ void __launch_bounds__(kDecThreads) decode_kernel(const DecParams prm
                 __syncthreads();
                 if (tile + NS - 1 <= t_hi)
                     issue(tile + NS - 1, stage(std::integral_constant<int, I + NS - 1>{}));
+                debug_sync();
                 if (active) compute(tile, stage(I), stage(I) + TB);
             }
         });

@@ -352,10 +352,13 @@ __global__ void __launch_bounds__(P::NT) fwd_kernel(const FwdParams prm) {
     auto step = [&](int kt, char *kr, char *vr, char *kw, char *vw) {
         const bool more = kt < kt_hi;
         typename P::Stage st;
+        debug_sync();
         if (more) {
             const TileSrc src{(kt + 1) * BN, 0, N, ng, s_gidx};
             P::issue(st, L, kh, vh, kw, vw, src, N - 1);
+            if constexpr (kDebugSync) P::finish(st, kw, vw, tid);
         }
+        debug_sync();
         const int k0 = kt * BN;
         int kind;   // -1 skip, 0 full, 1 edge
         if (MODE == MODE_BAND) {
@@ -378,7 +381,7 @@ __global__ void __launch_bounds__(P::NT) fwd_kernel(const FwdParams prm) {
             }
             softmax_pv_step<P>(rs, s, c, L, vr);
         }
-        if (more) P::finish(st, kw, vw, tid);
+        if (more && !kDebugSync) P::finish(st, kw, vw, tid);
         __syncthreads();
     };
     if (kt_lo <= kt_hi) {
@@ -782,8 +785,10 @@ __global__ void __launch_bounds__((BLK || XT || NAR) ? 256 : 512, NAR ? 2 : 1) f
     // One iteration; s holds S(j), sn receives S(j+1).
     auto iter = [&](int j, f32x16 (&s)[MB], f32x16 (&sn)[MB], const char *kr, const char *vr, char *kw, char *vw)
         __attribute__((always_inline)) {
+        debug_sync();
         if (j + 2 <= kt_hi) P::issue_k(L, kh, N, kw, (j + 2) * BN, dil);
         if (j + 1 <= kt_hi) P::issue_v(L, vh, N, vw, (j + 1) * BN, dil);
+        debug_sync();
         const bool cur = in_w(j), nxt = in_w(j + 1);
         const EdgeMask em{(j + 1) * BN, lo, hi, h};
         const float nmu = rs.m == EEA_NEG_INF ? 0.f : -rs.m;

@@ -37,6 +37,26 @@ __device__ __forceinline__ int acc_row(int r, int h) { return 8 * (r >> 2) + 4 *
 // vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt_hi[15:14]).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Debug-sync build (-DATTN_DEBUG_SYNC): every pipelined copy into an LDS
+// buffer is fenced on both sides. Before the copy, every wave has finished
+// with all earlier LDS reads (the barrier waits for them); after it, the copy
+// has landed before any wave goes on. Copies and compute then never overlap,
+// so the build's results must equal the optimised build's bit for bit; a
+// missing wait or barrier in the pipelined order would show as a difference.
+// Call sites are points that every wave of the workgroup reaches. The
+// optimised build compiles this to nothing.
+#ifdef ATTN_DEBUG_SYNC
+constexpr bool kDebugSync = true;
+#else
+constexpr bool kDebugSync = false;
+#endif
+__device__ __forceinline__ void debug_sync() {
+    if constexpr (kDebugSync) {
+        wait_vmem();
+        __syncthreads();
+    }
+}
+
 // Source rows of one key tile: keys k0.. for a band tile, or the global
 // positions g[k0..] for a gathered tile. Returns -1 for a row with no key.
 struct TileSrc {
