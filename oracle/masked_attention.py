@@ -47,8 +47,9 @@ What it computes (plain definition, no tiling, no fusion):
     - a row with no visible key (impossible under the argument rules, since
       the diagonal is always visible) yields output 0 and LSE -inf.
 
-``online_softmax_rows`` restates the block recurrence of the week-17 notes
-(FlashAttention section, online-softmax pseudocode), read row by row, so that
+``blockwise_attention_rows`` computes the same rows over arbitrary key blocks
+whose summaries (log-sum-exp and block-normalised output) are merged, the
+decomposition behind the FlashAttention passage of the week-17 notes, so that
 the algebra the GPU kernel relies on is itself checked against the two-pass
 definition above.
 """
@@ -211,15 +212,18 @@ def probabilities(q, k, *, causal: int, win_left: int = -1, win_right: int = -1,
     return p / np.where(l > 0, l, 1.0)
 
 
-def online_softmax_rows(q_rows, k, v, vis, block: int, scale: float | None = None):
-    """The block recurrence of the week-17 notes' online-softmax pseudocode,
-    applied to each query row separately (the running max is per row).
+def blockwise_attention_rows(q_rows, k, v, vis, cuts, scale: float | None = None):
+    """Attention of each query row computed over key blocks and merged, the
+    decomposition the FlashAttention passage of the week-17 notes rests on
+    (softmax over the keys taken one block at a time, never holding a full
+    row of scores).
 
-    State per row: running max m, running normaliser ("denominator") l and a
-    running output o that is renormalised after every block:
-        m_new = max(m, max of this block's scores)
-        l_new = exp(m - m_new) * l + sum(exp(s - m_new))
-        o     = (exp(m - m_new) * l * o + exp(s - m_new) @ V_block) / l_new
+    Here every block is first reduced on its own to a summary: the natural
+    log of its visible mass (its log-sum-exp) and its output normalised
+    within the block. The summaries are then folded left to right, each merge
+    weighting the two outputs by their shares of the combined mass. The
+    blocks are arbitrary: `cuts` lists the interior boundaries (sorted key
+    indices in 1..N-1), so the tests can split the keys at random places.
     q_rows: [R, d]; k, v: [N, d]; vis: bool [R, N]. Returns (O [R, d], LSE [R]).
     """
     q_rows = np.asarray(q_rows, dtype=np.float64)
@@ -229,26 +233,27 @@ def online_softmax_rows(q_rows, k, v, vis, block: int, scale: float | None = Non
     N = k.shape[0]
     if scale is None:
         scale = 1.0 / math.sqrt(d)
+    edges = [0] + [int(c) for c in cuts] + [N]
     O = np.zeros((R, v.shape[1]))
     LSE = np.full(R, -np.inf)
     for r in range(R):
-        m, l = -np.inf, 0.0
-        o = np.zeros(v.shape[1])
-        for j0 in range(0, N, block):
-            j1 = min(N, j0 + block)
-            s = (k[j0:j1] @ q_rows[r]) * scale
-            s = np.where(vis[r, j0:j1], s, -np.inf)
-            bmax = s.max()
-            m_new = max(m, bmax)
-            if m_new == -np.inf:          # nothing visible yet: state unchanged
+        total, out = -np.inf, np.zeros(v.shape[1])
+        for a, b in zip(edges[:-1], edges[1:]):
+            if b <= a:
                 continue
-            e = np.exp(s - m_new)
-            carry = math.exp(m - m_new) if m != -np.inf else 0.0
-            l_new = carry * l + e.sum()
-            o = (carry * l * o + e @ v[j0:j1]) / l_new
-            m, l = m_new, l_new
-        O[r] = o
-        LSE[r] = m + math.log(l) if l > 0 else -np.inf
+            s = np.where(vis[r, a:b], (k[a:b] @ q_rows[r]) * scale, -np.inf)
+            top = s.max()
+            if top == -np.inf:            # no visible key in this block
+                continue
+            w = np.exp(s - top)
+            mass = w.sum()
+            blk_lse = top + math.log(mass)
+            blk_out = (w @ v[a:b]) / mass
+            merged = np.logaddexp(total, blk_lse)
+            out = math.exp(total - merged) * out + math.exp(blk_lse - merged) * blk_out
+            total = merged
+        O[r] = out
+        LSE[r] = total
     return O, LSE
 
 

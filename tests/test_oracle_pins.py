@@ -105,18 +105,36 @@ def test_probabilities_sum_to_one(m):
     assert np.all(p[:, :, vis] > 0.0)
 
 
-# ---- P8 the pages' online-softmax recurrence equals the two-pass definition --------
+# ---- P8 attention over key blocks, merged, equals the two-pass definition --------
 
 @pytest.mark.parametrize("m", P.MASKS)
-def test_online_recurrence(m):
+def test_blockwise_merge(m):
     q, k, v = P._rng_qkv(9, 1, 1, 37, 8, scale=2.0)
     O, L = oracle.attention(q, k, v, **m)
     vis = oracle.mask_rows(np.arange(37), 37, global_idx=m["global_idx"],
                            **{x: m[x] for x in ("causal", "win_left", "win_right")})
-    for block in (1, 3, 7, 16, 37, 64):
-        Ob, Lb = oracle.online_softmax_rows(q[0, 0], k[0, 0], v[0, 0], vis, block)
+    rng = np.random.default_rng(10)
+    splits = [[], list(range(1, 37)), list(range(16, 37, 16))]   # one block, single keys, 16-key tiles
+    splits += [sorted(rng.choice(np.arange(1, 37), size=n, replace=False)) for n in (1, 2, 5, 11, 20) for _ in range(3)]
+    for cuts in splits:
+        Ob, Lb = oracle.blockwise_attention_rows(q[0, 0], k[0, 0], v[0, 0], vis, cuts)
         assert np.max(np.abs(Ob - O[0, 0])) <= 1e-12
         assert np.max(np.abs(Lb - L[0, 0])) <= 1e-12
+
+
+def test_blockwise_merge_survives_large_scores():
+    """Scores near 700 (exp overflows fp64 beyond 709): the block summaries
+    must keep everything relative to their own maxima."""
+    q, k, v = P._rng_qkv(11, 1, 1, 23, 4)
+    q = q * 0 + 1.0
+    k = k.copy()
+    k[0, 0, :, :] = 350.0 + np.arange(23)[:, None] * 0.25   # scaled scores 700..711
+    vis = np.ones((23, 23), bool)
+    O, L = oracle.attention(q, k, v, causal=0, win_left=-1, win_right=-1)
+    Ob, Lb = oracle.blockwise_attention_rows(q[0, 0], k[0, 0], v[0, 0], vis, [4, 9, 17])
+    assert np.all(np.isfinite(Ob)) and np.all(np.isfinite(Lb))
+    assert np.max(np.abs(Ob - O[0, 0])) <= 1e-12
+    assert np.max(np.abs(Lb - L[0, 0])) <= 1e-9
 
 
 def test_row_subset_matches_full():
