@@ -765,37 +765,62 @@ __global__ void __launch_bounds__((BLK || XT || NAR) ? 256 : 512, NAR ? 2 : 1) f
         else return classify(band, wr0, wr1, kt * BN, kt * BN + BN - 1) != TILE_FULL;
     };
 
-    P::issue_k(L, kh, N, kb0, kt_lo * BN, dil);
-    P::issue_v(L, vh, N, vb0, kt_lo * BN, dil);
-    if (kt_lo + 1 <= kt_hi) P::issue_k(L, kh, N, kb1, (kt_lo + 1) * BN, dil);
+    // Order of the band tiles: positions 0 .. nt-1. When the global rows are
+    // fused into this pass (four-wave instances), the workgroup's own key
+    // tiles (the keys under its query rows, two tiles) come last, so they are
+    // still in the two buffers when the loop ends; otherwise the order is
+    // kt_lo .. kt_hi. Position nt and beyond map past kt_hi (no wave's tile).
+    // The online softmax does not depend on the order of the tiles.
+    // Only the 128-row instances (four waves, not the extra rules) fuse; in
+    // the others the order is the plain one at compile time.
+    constexpr bool CANFUSE = (BLK || NAR) && !XT && !DIL;
+    const bool fuse = CANFUSE && ng > 0 && prm.fuse_grows;
+    const int nt = kt_hi - kt_lo + 1;
+    const int own_lo = fuse ? imax(unit * 2, kt_lo) : kt_hi + 1;
+    const int nown = fuse ? imax(0, imin(imin(unit * 2 + 1, kt_hi), (N - 1) / BN) - own_lo + 1) : 0;
+    const int npre = nt - nown;
+    auto tile_at = [&](int pos) {
+        if constexpr (!CANFUSE) return kt_lo + pos;
+        if (pos < npre) {
+            const int t = kt_lo + pos;
+            return t >= own_lo ? t + nown : t;
+        }
+        return pos < nt ? own_lo + (pos - npre) : kt_hi + 1;
+    };
+
+    P::issue_k(L, kh, N, kb0, tile_at(0) * BN, dil);
+    P::issue_v(L, vh, N, vb0, tile_at(0) * BN, dil);
+    if (1 < nt) P::issue_k(L, kh, N, kb1, tile_at(1) * BN, dil);
     wait_vmem();
     __syncthreads();
 
     f32x16 sa[MB], sb[MB];
     typename P::PFrag pf;
-    if (in_w(kt_lo)) {
+    if (in_w(tile_at(0))) {
         P::scores(sa, qf, L, kb0);
-        const EdgeMask em{kt_lo * BN, lo, hi, h};
-        const float mx = is_edge(kt_lo) ? BP::template region_b<false, true, true>(rs.o, pf, sb, rs.lpart, sa, L, vb0, em)
-                                        : BP::template region_b<false, true, false>(rs.o, pf, sb, rs.lpart, sa, L, vb0, em);
+        const EdgeMask em{tile_at(0) * BN, lo, hi, h};
+        const float mx = is_edge(tile_at(0))
+                             ? BP::template region_b<false, true, true>(rs.o, pf, sb, rs.lpart, sa, L, vb0, em)
+                             : BP::template region_b<false, true, false>(rs.o, pf, sb, rs.lpart, sa, L, vb0, em);
         raise_max<P>(rs, mx, c);
     }
     __syncthreads();   // every wave is done with kb0
 
-    // One iteration; s holds S(j), sn receives S(j+1).
+    // One iteration at position j; s holds S(tile j), sn receives S(tile j+1).
     auto iter = [&](int j, f32x16 (&s)[MB], f32x16 (&sn)[MB], const char *kr, const char *vr, char *kw, char *vw)
         __attribute__((always_inline)) {
+        const int tn = tile_at(j + 1);
         debug_sync();
-        if (j + 2 <= kt_hi) P::issue_k(L, kh, N, kw, (j + 2) * BN, dil);
-        if (j + 1 <= kt_hi) P::issue_v(L, vh, N, vw, (j + 1) * BN, dil);
+        if (j + 2 < nt) P::issue_k(L, kh, N, kw, tile_at(j + 2) * BN, dil);
+        if (j + 1 < nt) P::issue_v(L, vh, N, vw, tn * BN, dil);
         debug_sync();
-        const bool cur = in_w(j), nxt = in_w(j + 1);
-        const EdgeMask em{(j + 1) * BN, lo, hi, h};
+        const bool cur = in_w(tile_at(j)), nxt = in_w(tn);
+        const EdgeMask em{tn * BN, lo, hi, h};
         const float nmu = rs.m == EEA_NEG_INF ? 0.f : -rs.m;
         if (cur) {
             if (nxt) {
                 BP::template region_a<true, true>(sn, s, pf, qf, L, kr, c, nmu);
-                const float mx = is_edge(j + 1)
+                const float mx = is_edge(tn)
                                      ? BP::template region_b<true, true, true>(rs.o, pf, s, rs.lpart, sn, L, vr, em)
                                      : BP::template region_b<true, true, false>(rs.o, pf, s, rs.lpart, sn, L, vr, em);
                 raise_max<P>(rs, mx, c);
@@ -805,7 +830,7 @@ __global__ void __launch_bounds__((BLK || XT || NAR) ? 256 : 512, NAR ? 2 : 1) f
             }
         } else if (nxt) {
             BP::template region_a<true, false>(sn, s, pf, qf, L, kr, c, nmu);
-            const float mx = is_edge(j + 1)
+            const float mx = is_edge(tn)
                                  ? BP::template region_b<false, true, true>(rs.o, pf, s, rs.lpart, sn, L, vr, em)
                                  : BP::template region_b<false, true, false>(rs.o, pf, s, rs.lpart, sn, L, vr, em);
             raise_max<P>(rs, mx, c);
@@ -813,11 +838,11 @@ __global__ void __launch_bounds__((BLK || XT || NAR) ? 256 : 512, NAR ? 2 : 1) f
         wait_vmem();
         __syncthreads();
     };
-    // K(x) sits in kb[(x - kt_lo) & 1], V(x) in vb[(x - kt_lo) & 1]; the loop
-    // is unrolled by two so every buffer is a named object.
-    for (int j = kt_lo; j <= kt_hi; j += 2) {
+    // The tiles of positions x sit in kb[x & 1] and vb[x & 1]; the loop is
+    // unrolled by two so every buffer is a named object.
+    for (int j = 0; j < nt; j += 2) {
         iter(j, sa, sb, kb1, vb0, kb0, vb1);
-        if (j + 1 > kt_hi) break;
+        if (j + 1 >= nt) break;
         iter(j + 1, sb, sa, kb0, vb1, kb1, vb0);
     }
 
@@ -910,67 +935,154 @@ __global__ void __launch_bounds__((BLK || XT || NAR) ? 256 : 512, NAR ? 2 : 1) f
         }
     }
 
-    // --- epilogue
-    if (!valid) return;
-    const int orow = rcls + row * dil;   // row index in the stored sequence
-    if (ng > 0) {
-        for (int t = 0; t < ng; ++t)
-            if (s_gidx[t] == orow) return;   // global rows are written by the merge
+    // --- epilogue (the row taken afresh from the lane index, as in the
+    // global-row phase below)
+    {
+        const int elane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+        const int eh = elane >> 5;
+        const int erow = q0 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * 32 + (elane & 31);
+        const int orow = rcls + erow * dil;   // row index in the stored sequence
+        bool store = erow < N;
+        for (int t = 0; t < ng; ++t) store &= s_gidx[t] != orow;   // global rows are written by the merge
+        if (store) {
+            const float l = sum_across_halves(rs.lpart);
+            const float inv = l > 0.f ? 1.f / l : 0.f;
+            uint16_t *oh = static_cast<uint16_t *>(prm.out) + (long long)bh * prm.head_stride;
+            P::store_out(oh, orow, rs.o, inv, eh);
+            if (eh == 0) prm.lse[(long long)bh * prm.N + orow] = l > 0.f ? (rs.m + __log2f(l)) * kLn2 : EEA_NEG_INF;
+        }
     }
-    const float l = sum_across_halves(rs.lpart);
-    const float inv = l > 0.f ? 1.f / l : 0.f;
-    uint16_t *oh = static_cast<uint16_t *>(prm.out) + (long long)bh * prm.head_stride;
-    P::store_out(oh, orow, rs.o, inv, h);
-    if (h == 0) prm.lse[(long long)bh * prm.N + orow] = l > 0.f ? (rs.m + __log2f(l)) * kLn2 : EEA_NEG_INF;
+
+    if (fuse) {
+        // --- the global rows against this workgroup's own key tiles (the
+        // keys under its 128 query rows, positions npre and npre + 1 of the
+        // loop, still in the buffers of those positions). Over all query
+        // tiles every key tile is some workgroup's own exactly once, so the
+        // partials (output, max, normaliser) of the global rows cover every
+        // key once, without a pass of their own over K and V: partial
+        // 2 * unit + t of each global row, combined by merge_kernel. One wave
+        // per (row block of 32 global rows, own tile t); a global row sees
+        // every key up to the causal limit. No barrier: the last iteration's
+        // barrier follows the last copy.
+        // Lane and wave indices are taken afresh (mbcnt, and the wave index
+        // in a scalar register): keeping the entry ones live across the band
+        // loop costs registers the loop needs.
+        const int glane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+        const int gh = glane >> 5;
+        const int gwave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        const int rb = gwave >> 1, t = gwave & 1;
+        if (rb * 32 < ng) {   // wave-uniform
+            const int gt = rb * 32 + (glane & 31);
+            const int grow = gt < ng ? s_gidx[gt] : 0;
+            typename P::QFrag gq;
+            P::load_q(gq, qh, grow, gt < ng, gh);
+            typename P::Lane GL;   // lane offsets taken afresh as well
+            P::init_lane(GL, glane, gwave, 1);
+            RowState<P> gs;
+            gs.m = EEA_NEG_INF;
+            gs.lpart = 0.f;
+#pragma unroll
+            for (int db = 0; db < P::DB; ++db) gs.o[db] = f32x16{};
+            auto own_tile = [&](const char *kbuf, const char *vbuf) __attribute__((always_inline)) {
+                const int kt = own_lo + t;
+                f32x16 s[MB];
+                P::scores(s, gq, GL, kbuf);
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int jk = kt * BN + mb * 32 + acc_row(r, gh);
+                        const bool vis = (gt < ng) & (jk < N) & ((prm.causal == 0) | (jk <= grow));
+                        s[mb][r] = vis ? s[mb][r] : EEA_NEG_INF;
+                    }
+                softmax_pv_step<P>(gs, s, c, GL, vbuf);
+            };
+            if (t < nown) {   // else past the sequence: an empty partial
+                if ((npre + t) & 1) own_tile(kb1, vb1);
+                else own_tile(kb0, vb0);
+            }
+            if (gt < ng) {
+                const float l = sum_across_halves(gs.lpart);
+                float *dst = prm.part + (((long long)bh * ng + gt) * prm.chunks + 2 * unit + t) * (D + 2);
+#pragma unroll
+                for (int db = 0; db < P::DB; ++db)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        float *pp = dst + db * 32 + 8 * g + 4 * gh;
+                        pp[0] = gs.o[db][4 * g + 0];
+                        pp[1] = gs.o[db][4 * g + 1];
+                        pp[2] = gs.o[db][4 * g + 2];
+                        pp[3] = gs.o[db][4 * g + 3];
+                    }
+                if (gh == 0) {
+                    dst[D] = gs.m;
+                    dst[D + 1] = l;
+                }
+            }
+        }
+    }
 }
 
 // Merge of the split-key partials of one global row: the same rescaling
 // identity as the online softmax, applied across chunks.
 template <int D, bool F32>
-__global__ void __launch_bounds__(64) merge_kernel(const FwdParams prm) {
-    // the chunk maxima are read across lanes (no chain of dependent loads);
-    // each chunk's weight exp2(m_c - M) goes to LDS for the output sum
-    __shared__ float wsh[kMaxGlobalChunks];
-    const int ng = prm.n_global, lane = threadIdx.x;
+__global__ void __launch_bounds__(256) merge_kernel(const FwdParams prm) {
+    // One workgroup per (head, global row); its four waves take every fourth
+    // partial. Per wave: the largest partial max, then the weights
+    // exp2(m_c - M) and the weighted normalisers and outputs of its partials
+    // (lanes over d); the four waves' results are combined through LDS.
+    __shared__ float wm[4], wl[4];
+    __shared__ float wo[4][D];
+    const int ng = prm.n_global, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int bh = blockIdx.x / ng, t = blockIdx.x - bh * ng;
     const int g = prm.gidx[t];
     const int C = prm.chunks;
     const float *src = prm.part + ((long long)bh * ng + t) * C * (D + 2);
     float M = EEA_NEG_INF;
-    for (int ci = lane; ci < C; ci += 64) M = fmaxf(M, src[ci * (D + 2) + D]);
+    for (int ci = wave + 4 * lane; ci < C; ci += 256) M = fmaxf(M, src[ci * (D + 2) + D]);
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-    float Lsum = 0.f;
-    for (int ci = lane; ci < C; ci += 64) {
-        const float mc = src[ci * (D + 2) + D];
-        const float w = mc == EEA_NEG_INF ? 0.f : fast_exp2(mc - M);
-        wsh[ci] = w;
-        Lsum += w * src[ci * (D + 2) + D + 1];
-    }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) Lsum += __shfl_xor(Lsum, off);
-    __syncthreads();
-    const float inv = Lsum > 0.f ? 1.f / Lsum : 0.f;
     constexpr int PER = D / 64;
-    float acc[PER];
+    float acc[PER], Lsum = 0.f;
 #pragma unroll
     for (int j = 0; j < PER; ++j) acc[j] = 0.f;
 #pragma unroll 4
-    for (int ci = 0; ci < C; ++ci) {
-        const float w = wsh[ci];
+    for (int ci = wave; ci < C; ci += 4) {
+        const float *pc = src + ci * (D + 2);
+        const float mc = pc[D];
+        const float w = mc == EEA_NEG_INF ? 0.f : fast_exp2(mc - M);
+        Lsum += w * pc[D + 1];
 #pragma unroll
-        for (int j = 0; j < PER; ++j) acc[j] += src[ci * (D + 2) + lane + 64 * j] * w;
+        for (int j = 0; j < PER; ++j) acc[j] += pc[lane + 64 * j] * w;
     }
+    if (lane == 0) {
+        wm[wave] = M;
+        wl[wave] = Lsum;
+    }
+#pragma unroll
+    for (int j = 0; j < PER; ++j) wo[wave][lane + 64 * j] = acc[j];
+    __syncthreads();
+    if (wave != 0) return;
+    const float Mt = fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3]));
+    float sc[4], Lt = 0.f;
+#pragma unroll
+    for (int w4 = 0; w4 < 4; ++w4) {
+        sc[w4] = wm[w4] == EEA_NEG_INF ? 0.f : fast_exp2(wm[w4] - Mt);
+        Lt += sc[w4] * wl[w4];
+    }
+    const float inv = Lt > 0.f ? 1.f / Lt : 0.f;
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
-        const long long o = ((long long)bh * prm.N + g) * D + lane + 64 * j;
+        const int dd = lane + 64 * j;
+        const float o = (sc[0] * wo[0][dd] + sc[1] * wo[1][dd] + sc[2] * wo[2][dd] + sc[3] * wo[3][dd]) * inv;
+        const long long oi = ((long long)bh * prm.N + g) * D + dd;
         if (F32) {
-            static_cast<float *>(prm.out)[o] = acc[j] * inv;
+            static_cast<float *>(prm.out)[oi] = o;
         } else {
-            static_cast<__bf16 *>(prm.out)[o] = (__bf16)(acc[j] * inv);
+            static_cast<__bf16 *>(prm.out)[oi] = (__bf16)o;
         }
     }
-    if (lane == 0) prm.lse[(long long)bh * prm.N + g] = Lsum > 0.f ? (M + __log2f(Lsum)) * kLn2 : EEA_NEG_INF;
+    if (lane == 0) prm.lse[(long long)bh * prm.N + g] = Lt > 0.f ? (Mt + __log2f(Lt)) * kLn2 : EEA_NEG_INF;
 }
 
 // ---------------------------------------------------------------------------
@@ -1001,6 +1113,10 @@ static hipError_t launch_impl(const FwdParams &p0, hipStream_t stream) {
         hipLaunchKernelGGL((fwd_band_bf16<D, false, false>), dim3(grid), dim3(PB::NT), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.n_global == 0) return e;
+    if (p.fuse_grows) {   // the band pass wrote the global rows' partials
+        hipLaunchKernelGGL((merge_kernel<D, F32>), dim3(p.BH * p.n_global), dim3(256), 0, stream, p);
+        return hipGetLastError();
+    }
     const int ggrid = p.BH * p.chunks;
     p.xcd_remap = (ggrid % 8 == 0) ? 1 : 0;
     if (p.n_global <= 32)
@@ -1009,7 +1125,7 @@ static hipError_t launch_impl(const FwdParams &p0, hipStream_t stream) {
         hipLaunchKernelGGL((fwd_kernel<PG128, MODE_GROWS>), dim3(ggrid), dim3(128), 0, stream, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((merge_kernel<D, F32>), dim3(p.BH * p.n_global), dim3(64), 0, stream, p);
+    hipLaunchKernelGGL((merge_kernel<D, F32>), dim3(p.BH * p.n_global), dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 
