@@ -144,10 +144,10 @@ size_t workspace_for(int BH, int N, int d, int ng) {
         size_t b = (size_t)BH * ng * chunks * (d + 2) * sizeof(float);
         best = std::max(best, b);
     }
-    // global rows fused into the bf16 band pass: two partials per query tile
+    // global rows fused into the bf16 band pass: one partial per query tile
     // of 128 rows
     const int nqt = (N + 127) / 128;
-    best = std::max(best, (size_t)BH * ng * (2 * (size_t)nqt) * (d + 2) * sizeof(float));
+    best = std::max(best, (size_t)BH * ng * (size_t)nqt * (d + 2) * sizeof(float));
     return best;
 }
 
@@ -476,8 +476,8 @@ int fwd_impl(const void *q, const void *k, const void *v, void *out, float *lse,
     if (ng > 0) {
         if (eea::fuse_global_rows(dtype == ATTN_F32, m.dil, m.extra(), bm, (int)nqt)) {
             p.fuse_grows = 1;
-            p.chunks = 2 * (int)nqt;
-            p.chunk_tiles = 1;
+            p.chunks = (int)nqt;
+            p.chunk_tiles = 2;
         } else {
             int ct = 0;
             p.chunks = eea::global_chunks((int)BH, N, d, dtype == ATTN_F32, &ct);

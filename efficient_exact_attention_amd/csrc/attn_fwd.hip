@@ -959,9 +959,9 @@ __global__ void __launch_bounds__((BLK || XT || NAR) ? 256 : 512, NAR ? 2 : 1) f
         // loop, still in the buffers of those positions). Over all query
         // tiles every key tile is some workgroup's own exactly once, so the
         // partials (output, max, normaliser) of the global rows cover every
-        // key once, without a pass of their own over K and V: partial
-        // 2 * unit + t of each global row, combined by merge_kernel. One wave
-        // per (row block of 32 global rows, own tile t); a global row sees
+        // key once, without a pass of their own over K and V: partial `unit`
+        // of each global row, combined by merge_kernel. One wave per row
+        // block of 32 global rows takes both own tiles; a global row sees
         // every key up to the causal limit. No barrier: the last iteration's
         // barrier follows the last copy.
         // Lane and wave indices are taken afresh (mbcnt, and the wave index
@@ -970,7 +970,7 @@ __global__ void __launch_bounds__((BLK || XT || NAR) ? 256 : 512, NAR ? 2 : 1) f
         const int glane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
         const int gh = glane >> 5;
         const int gwave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-        const int rb = gwave >> 1, t = gwave & 1;
+        const int rb = gwave;
         if (rb * 32 < ng) {   // wave-uniform
             const int gt = rb * 32 + (glane & 31);
             const int grow = gt < ng ? s_gidx[gt] : 0;
@@ -983,7 +983,7 @@ __global__ void __launch_bounds__((BLK || XT || NAR) ? 256 : 512, NAR ? 2 : 1) f
             gs.lpart = 0.f;
 #pragma unroll
             for (int db = 0; db < P::DB; ++db) gs.o[db] = f32x16{};
-            auto own_tile = [&](const char *kbuf, const char *vbuf) __attribute__((always_inline)) {
+            auto own_tile = [&](int t, const char *kbuf, const char *vbuf) __attribute__((always_inline)) {
                 const int kt = own_lo + t;
                 f32x16 s[MB];
                 P::scores(s, gq, GL, kbuf);
@@ -997,13 +997,18 @@ __global__ void __launch_bounds__((BLK || XT || NAR) ? 256 : 512, NAR ? 2 : 1) f
                     }
                 softmax_pv_step<P>(gs, s, c, GL, vbuf);
             };
-            if (t < nown) {   // else past the sequence: an empty partial
-                if ((npre + t) & 1) own_tile(kb1, vb1);
-                else own_tile(kb0, vb0);
+            // own tile t at position npre + t, in buffer (npre + t) & 1; a
+            // last query tile may own one tile only (nown == 1)
+            if (npre & 1) {
+                own_tile(0, kb1, vb1);
+                if (nown > 1) own_tile(1, kb0, vb0);
+            } else {
+                own_tile(0, kb0, vb0);
+                if (nown > 1) own_tile(1, kb1, vb1);
             }
             if (gt < ng) {
                 const float l = sum_across_halves(gs.lpart);
-                float *dst = prm.part + (((long long)bh * ng + gt) * prm.chunks + 2 * unit + t) * (D + 2);
+                float *dst = prm.part + (((long long)bh * ng + gt) * prm.chunks + unit) * (D + 2);
 #pragma unroll
                 for (int db = 0; db < P::DB; ++db)
 #pragma unroll

@@ -45,7 +45,7 @@ int global_chunks(int BH, int N, int d, int f32, int *chunk_tiles) {
 // The bf16 band pass of 128-row workgroups can take the global rows on: each
 // workgroup computes their partials on the two key tiles under its own query
 // rows (visited last, so they are still in LDS when its band loop ends), one
-// partial per such tile, so the split-key pass (which reads K and V once
+// partial per workgroup, so the split-key pass (which reads K and V once
 // more) and its launch disappear. Not with the strided or random-block rules,
 // whose extra tiles reuse the buffers after the band loop.
 bool fuse_global_rows(int f32, int dil, int extra, int bm, int num_qt) {

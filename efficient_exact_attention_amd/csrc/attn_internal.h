@@ -47,8 +47,8 @@ struct FwdParams {
     int causal;
     int n_global;         // 0 when the band already covers every visible key
     int num_qt;           // query tiles per head (per residue class when dil > 1)
-    int chunks;           // key chunks per global row (split-key pass; with fuse_grows: 2 per query tile)
-    int chunk_tiles;      // key tiles per chunk (1 with fuse_grows)
+    int chunks;           // key chunks per global row (split-key pass; with fuse_grows: query tiles)
+    int chunk_tiles;      // key tiles per chunk (2 with fuse_grows: a band workgroup's own key tiles)
     int fuse_grows;       // 1: the bf16 band pass computes the global rows' partials on its own key tiles
     int xcd_remap;        // 1: group consecutive work items on one XCD; 2: heads per XCD, heaviest tiles first
     float scale_log2;     // score scale * log2(e)
@@ -137,8 +137,8 @@ hipError_t launch_forward(const FwdParams &p, int d, int f32, hipStream_t stream
 
 // Number of key chunks the split-key pass uses for these sizes.
 int global_chunks(int BH, int N, int d, int f32, int *chunk_tiles);
-// Whether the band pass computes the global rows' partials itself (two per
-// query tile of bm rows: its own key tiles), instead of the split-key pass.
+// Whether the band pass computes the global rows' partials itself (one per
+// query tile of bm rows, over its own key tiles), instead of the split-key pass.
 bool fuse_global_rows(int f32, int dil, int extra, int bm, int num_qt);
 
 // Device address, on the current device, of the allocation-free forward's
