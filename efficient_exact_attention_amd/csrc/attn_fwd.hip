@@ -502,6 +502,12 @@ struct BandPipe {
                 }
             }
             if constexpr (EXP) {
+                // The scaling FMAs stay beside this region's MFMAs: the scores
+                // are redefined here (an empty asm, no instruction); both
+                // region A variants exponentiate the same scores, and the
+                // compiler would otherwise compute all of them ahead of the
+                // branch between the variants, in one block with no MFMA.
+                if constexpr ((B * EA) % 16 == 0) asm volatile("" : "+v"(s[(B * EA) / 16]));
 #pragma unroll
                 for (int e = B * EA; e < (B + 1) * EA; ++e)
                     s[e / 16][e % 16] = fast_exp2(__builtin_fmaf(s[e / 16][e % 16], c, nmu));
@@ -637,7 +643,7 @@ __device__ __forceinline__ void raise_max(RowState<P> &rs, float mx, float c) {
 // SIMD) for that reason. NAR (narrow bands, band_is_narrow) is the plain
 // kernel at 256 threads with the two-waves-per-SIMD budget, so two
 // workgroups share a CU.
-template <int D, bool DIL, bool BLK, bool XT = false, bool NAR = false>
+template <int D, bool DIL, bool BLK, bool XT = false, bool NAR = false, bool FUS = false>
 __global__ void __launch_bounds__((BLK || XT || NAR) ? 256 : 512, NAR ? 2 : 1) fwd_band_bf16(const FwdParams prm) {
     constexpr bool GEN = BLK;
     typedef Bf16Path<D, (BLK || XT || NAR) ? 256 : 512> P;
@@ -650,6 +656,14 @@ __global__ void __launch_bounds__((BLK || XT || NAR) ? 256 : 512, NAR ? 2 : 1) f
     __shared__ __attribute__((aligned(1024))) char kb1[P::TILE_BYTES];
     __shared__ __attribute__((aligned(1024))) char vb0[P::TILE_BYTES];
     __shared__ __attribute__((aligned(1024))) char vb1[P::TILE_BYTES];
+    // GSEP: the gathered tile of global columns has buffers of its own, so
+    // its copy goes out with the band's first copies (one wait for both).
+    // Only in the four-wave d=64 instance, whose short loops make the extra
+    // wait a large share; elsewhere it costs registers (d=128 at 256) or the
+    // LDS two workgroups share.
+    constexpr bool GSEP = FUS && NAR && D == 64;
+    __shared__ __attribute__((aligned(1024))) char kgb[GSEP ? P::TILE_BYTES : 16];
+    __shared__ __attribute__((aligned(1024))) char vgb[GSEP ? P::TILE_BYTES : 16];
     __shared__ int s_gidx[kMaxGlobal];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -724,30 +738,35 @@ __global__ void __launch_bounds__((BLK || XT || NAR) ? 256 : 512, NAR ? 2 : 1) f
     for (int db = 0; db < P::DB; ++db) rs.o[db] = f32x16{};
     const float c = prm.scale_log2;
 
-    // --- gathered tiles of global columns (one per BN globals), unpipelined
-    // (global tokens are not combined with a dilated mask)
+    // --- the gathered tile of global columns (at most kMaxGlobal = BN of
+    // them: one tile), unpipelined (global tokens are not combined with a
+    // dilated mask). A global column counts here only outside the row's
+    // window.
+    static_assert(kMaxGlobal <= BN, "the global columns fit one gathered tile");
+    auto gathered = [&](const char *kbuf, const char *vbuf) __attribute__((always_inline)) {
+        f32x16 s[MB];
+        P::scores(s, qf, L, kbuf);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int col = mb * 32 + acc_row(r, h);
+                const int g = s_gidx[col < kMaxGlobal ? col : 0];
+                const bool vis = (col < ng) & ((prm.causal == 0) | (g <= row)) & ((g < lo) | (g > hi));
+                s[mb][r] = vis ? s[mb][r] : EEA_NEG_INF;
+            }
+        softmax_pv_step<P>(rs, s, c, L, vbuf);
+    };
     if (ng > 0) {
-        for (int g0 = 0; g0 < ng; g0 += BN) {
-            typename P::Stage st;
-            const TileSrc src{g0, 1, N, ng, s_gidx};
+        typename P::Stage st;
+        const TileSrc src{0, 1, N, ng, s_gidx};
+        if constexpr (GSEP) {
+            P::issue(st, L, kh, vh, kgb, vgb, src, s_gidx[0]);   // waited for with the band's first tiles
+        } else {
             P::issue(st, L, kh, vh, kb0, vb0, src, s_gidx[0]);
             P::finish(st, kb0, vb0, tid);
             __syncthreads();
-            if (wave_active) {
-                f32x16 s[MB];
-                P::scores(s, qf, L, kb0);
-                // a global column counts here only outside the row's window
-#pragma unroll
-                for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int col = g0 + mb * 32 + acc_row(r, h);
-                        const int g = s_gidx[col < kMaxGlobal ? col : 0];
-                        const bool vis = (col < ng) & ((prm.causal == 0) | (g <= row)) & ((g < lo) | (g > hi));
-                        s[mb][r] = vis ? s[mb][r] : EEA_NEG_INF;
-                    }
-                softmax_pv_step<P>(rs, s, c, L, vb0);
-            }
+            if (wave_active) gathered(kb0, vb0);
             __syncthreads();
         }
     }
@@ -771,9 +790,11 @@ __global__ void __launch_bounds__((BLK || XT || NAR) ? 256 : 512, NAR ? 2 : 1) f
     // still in the two buffers when the loop ends; otherwise the order is
     // kt_lo .. kt_hi. Position nt and beyond map past kt_hi (no wave's tile).
     // The online softmax does not depend on the order of the tiles.
-    // Only the 128-row instances (four waves, not the extra rules) fuse; in
-    // the others the order is the plain one at compile time.
-    constexpr bool CANFUSE = (BLK || NAR) && !XT && !DIL;
+    // Only the FUS instances (128-row workgroups with global tokens: the
+    // narrow and block-rule ones) fuse; in the others the order is the plain
+    // one at compile time.
+    constexpr bool CANFUSE = FUS;
+    static_assert(!FUS || ((BLK || NAR) && !XT && !DIL), "fusion needs 128-row workgroups");
     const bool fuse = CANFUSE && ng > 0 && prm.fuse_grows;
     const int nt = kt_hi - kt_lo + 1;
     const int own_lo = fuse ? imax(unit * 2, kt_lo) : kt_hi + 1;
@@ -793,6 +814,9 @@ __global__ void __launch_bounds__((BLK || XT || NAR) ? 256 : 512, NAR ? 2 : 1) f
     if (1 < nt) P::issue_k(L, kh, N, kb1, tile_at(1) * BN, dil);
     wait_vmem();
     __syncthreads();
+    if constexpr (GSEP) {
+        if (ng > 0 && wave_active) gathered(kgb, vgb);
+    }
 
     f32x16 sa[MB], sb[MB];
     typename P::PFrag pf;
@@ -1108,10 +1132,16 @@ static hipError_t launch_impl(const FwdParams &p0, hipStream_t stream) {
         hipLaunchKernelGGL((fwd_kernel<PB, MODE_BAND>), dim3(grid), dim3(PB::NT), 0, stream, p);
     else if (p.stride > 0 || p.rand_block > 0)
         hipLaunchKernelGGL((fwd_band_bf16<D, false, false, true>), dim3(grid), dim3(kBandThreadsBlock), 0, stream, p);
+    else if (p.block > 0 && p.fuse_grows)
+        hipLaunchKernelGGL((fwd_band_bf16<D, false, true, false, false, true>), dim3(grid), dim3(kBandThreadsBlock), 0,
+                           stream, p);
     else if (p.block > 0)
         hipLaunchKernelGGL((fwd_band_bf16<D, false, true>), dim3(grid), dim3(kBandThreadsBlock), 0, stream, p);
     else if (p.dil > 1)
         hipLaunchKernelGGL((fwd_band_bf16<D, true, false>), dim3(grid), dim3(PB::NT), 0, stream, p);
+    else if (band_is_narrow(p.wl, p.wr, p.dil) && p.fuse_grows)
+        hipLaunchKernelGGL((fwd_band_bf16<D, false, false, false, true, true>), dim3(grid), dim3(kBandThreadsNarrow), 0,
+                           stream, p);
     else if (band_is_narrow(p.wl, p.wr, p.dil))
         hipLaunchKernelGGL((fwd_band_bf16<D, false, false, false, true>), dim3(grid), dim3(kBandThreadsNarrow), 0, stream, p);
     else

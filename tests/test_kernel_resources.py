@@ -35,24 +35,24 @@ def test_no_vector_register_spills(resources):
 
 
 def _band_flags(name):
-    """(DIL, BLK, XT, NAR) of a mangled fwd_band_bf16<D, DIL, BLK, XT, NAR> name."""
+    """(DIL, BLK, XT, NAR, FUS) of a mangled fwd_band_bf16<D, DIL, BLK, XT, NAR, FUS> name."""
     args = name.split("fwd_band_bf16I", 1)[1]
-    return tuple(f == "1" for f in re.findall(r"Lb([01])E", args)[:4])
+    return tuple(f == "1" for f in re.findall(r"Lb([01])E", args)[:5])
 
 
 def test_band_kernel_fits_two_waves_per_simd(resources):
     """The band instances that run two waves per SIMD (plain and dilated at
-    512 threads, narrow at 256 threads with two workgroups per CU) keep
-    within 256 registers."""
+    512 threads, narrow at 256 threads with two workgroups per CU, with and
+    without the fused global rows) keep within 256 registers."""
     seen = 0
     for k, v in resources.items():
         if "fwd_band_bf16" not in k:
             continue
-        dil, blk, xt, nar = _band_flags(k)
+        dil, blk, xt, nar, fus = _band_flags(k)
         if not blk and not xt:
             seen += 1
             assert v["vgpr"] + v["agpr"] <= 256, (k, v)
-    assert seen == 6   # d = 64, 128 x (plain, dilated, narrow)
+    assert seen == 8   # d = 64, 128 x (plain, dilated, narrow, narrow with fused global rows)
 
 
 def test_two_wave_backward_instances_fit(resources):
