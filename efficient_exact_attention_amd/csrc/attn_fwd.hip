@@ -452,15 +452,20 @@ __global__ void __launch_bounds__(P::NT) fwd_kernel(const FwdParams prm) {
 // followed by a share of the vector work, so the vector instructions issue
 // while the MFMA before them is still in the matrix pipe.
 // ---------------------------------------------------------------------------
+// Edge-tile mask: key k0 + mb*32 + acc_row(r, h) is visible to the lane's row
+// iff it lies in [lo, hi]; the half-wave offset 4h is folded into the bounds
+// (lo4 = lo - 4h, hi4 = hi - 4h), so h need not stay live in the loop.
 struct EdgeMask {
-    int k0, lo, hi, h;   // first key of the tile; the lane's row interval; half-wave
+    int k0, lo4, hi4;   // first key of the tile; the lane's row interval less 4h
 };
 
 template <class P>
 struct BandPipe {
     static constexpr int MB = P::MB, KS = P::KS, DB = P::DB, PVS = P::PVS;
     static constexpr int NE = 16 * MB;                    // scores per lane per tile
-    static constexpr int kB = 4, kSlots = 8;              // MFMAs per batch; operand slots
+    // MFMAs per batch and operand slots; at d = 64 batches of two, whose
+    // operand slots (half as many) let the narrow instance fit 168 registers
+    static constexpr int kB = P::D == 64 ? 2 : 4, kSlots = 2 * kB;
     static constexpr int BQK = KS * MB / kB, BPV = PVS * DB / kB;
     static constexpr int EA = NE / BQK, EB = NE / BPV;    // scores handled per batch
     static_assert(EA % 8 == 0 && EB % 2 == 0, "whole packed groups per batch");
@@ -479,6 +484,25 @@ struct BandPipe {
     static __device__ __forceinline__ void v_fetch(bf16x8 (&op)[kSlots], const LN &L, const char *vbuf) {
         if constexpr (I < PVS * DB) op[I % kSlots] = P::v_operand(L, vbuf, I % DB, I / DB);
     }
+    // The kB operand reads of batch B.
+    template <int B>
+    static __device__ __forceinline__ void k_batch(bf16x8 (&op)[kSlots], const LN &L, const char *kbuf) {
+        k_fetch<kB * B + 0>(op, L, kbuf);
+        k_fetch<kB * B + 1>(op, L, kbuf);
+        if constexpr (kB == 4) {
+            k_fetch<kB * B + 2>(op, L, kbuf);
+            k_fetch<kB * B + 3>(op, L, kbuf);
+        }
+    }
+    template <int B>
+    static __device__ __forceinline__ void v_batch(bf16x8 (&op)[kSlots], const LN &L, const char *vbuf) {
+        v_fetch<kB * B + 0>(op, L, vbuf);
+        v_fetch<kB * B + 1>(op, L, vbuf);
+        if constexpr (kB == 4) {
+            v_fetch<kB * B + 2>(op, L, vbuf);
+            v_fetch<kB * B + 3>(op, L, vbuf);
+        }
+    }
 
     // Region A, batch B: the reads of batch B+1, four QK MFMAs, and the
     // exponentials of scores [B*EA, (B+1)*EA) of the previous tile.
@@ -488,10 +512,7 @@ struct BandPipe {
                                                  float nmu) {
         if constexpr (B < BQK) {
             if constexpr (QK && B + 1 < BQK) {
-                k_fetch<kB * (B + 1) + 0>(op, L, kbuf);
-                k_fetch<kB * (B + 1) + 1>(op, L, kbuf);
-                k_fetch<kB * (B + 1) + 2>(op, L, kbuf);
-                k_fetch<kB * (B + 1) + 3>(op, L, kbuf);
+                k_batch<B + 1>(op, L, kbuf);
                 __builtin_amdgcn_sched_barrier(0);
             }
             if constexpr (QK) {
@@ -538,10 +559,7 @@ struct BandPipe {
         if constexpr (QK) {
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb) sn[mb] = f32x16{};
-            k_fetch<0>(op, L, kbuf);
-            k_fetch<1>(op, L, kbuf);
-            k_fetch<2>(op, L, kbuf);
-            k_fetch<3>(op, L, kbuf);
+            k_batch<0>(op, L, kbuf);
             __builtin_amdgcn_sched_barrier(0);
         }
         // Raised wave priority while the QK^T MFMAs are issued: with the
@@ -562,10 +580,7 @@ struct BandPipe {
                                                  const char *vbuf, bf16x8 (&op)[kSlots], const EdgeMask &em) {
         if constexpr (B < BPV) {
             if constexpr (PV && B + 1 < BPV) {
-                v_fetch<kB * (B + 1) + 0>(op, L, vbuf);
-                v_fetch<kB * (B + 1) + 1>(op, L, vbuf);
-                v_fetch<kB * (B + 1) + 2>(op, L, vbuf);
-                v_fetch<kB * (B + 1) + 3>(op, L, vbuf);
+                v_batch<B + 1>(op, L, vbuf);
                 __builtin_amdgcn_sched_barrier(0);
             }
             if constexpr (PV) {
@@ -582,8 +597,8 @@ struct BandPipe {
                 for (int e = B * EB; e < (B + 1) * EB; ++e) {
                     const int mb = e / 16, r = e % 16;
                     if constexpr (EDGE) {
-                        const int j = em.k0 + mb * 32 + acc_row(r, em.h);
-                        sn[mb][r] = ((j >= em.lo) & (j <= em.hi)) ? sn[mb][r] : EEA_NEG_INF;
+                        const int j = em.k0 + mb * 32 + acc_row(r, 0);
+                        sn[mb][r] = ((j >= em.lo4) & (j <= em.hi4)) ? sn[mb][r] : EEA_NEG_INF;
                     }
                     mx[e & 1] = fmaxf(mx[e & 1], sn[mb][r]);
                 }
@@ -607,10 +622,7 @@ struct BandPipe {
         bf16x8 op[kSlots];
         float sum[2] = {0.f, 0.f}, mx[2] = {EEA_NEG_INF, EEA_NEG_INF};
         if constexpr (PV) {
-            v_fetch<0>(op, L, vbuf);
-            v_fetch<1>(op, L, vbuf);
-            v_fetch<2>(op, L, vbuf);
-            v_fetch<3>(op, L, vbuf);
+            v_batch<0>(op, L, vbuf);
             __builtin_amdgcn_sched_barrier(0);
         }
         b_run<PV, NEXT, EDGE, 0>(o, pf, s, sum, sn, mx, L, vbuf, op, em);
@@ -642,9 +654,13 @@ __device__ __forceinline__ void raise_max(RowState<P> &rs, float mx, float c) {
 // the block-rule and extra-tile instances run 256 threads (one wave per
 // SIMD) for that reason. NAR (narrow bands, band_is_narrow) is the plain
 // kernel at 256 threads with the two-waves-per-SIMD budget, so two
-// workgroups share a CU.
+// workgroups share a CU; at d = 64 it fits 168 registers and three share a
+// CU (three waves per SIMD), which hides the copy-in, epilogue and global-row
+// phases of its short loops behind the other workgroups' loops (c. 15 % on a
+// band of 513 keys).
 template <int D, bool DIL, bool BLK, bool XT = false, bool NAR = false, bool FUS = false>
-__global__ void __launch_bounds__((BLK || XT || NAR) ? 256 : 512, NAR ? 2 : 1) fwd_band_bf16(const FwdParams prm) {
+__global__ void __launch_bounds__((BLK || XT || NAR) ? 256 : 512, NAR ? (D == 64 ? 3 : 2) : 1)
+    fwd_band_bf16(const FwdParams prm) {
     constexpr bool GEN = BLK;
     typedef Bf16Path<D, (BLK || XT || NAR) ? 256 : 512> P;
     typedef BandPipe<P> BP;
@@ -711,7 +727,10 @@ __global__ void __launch_bounds__((BLK || XT || NAR) ? 256 : 512, NAR ? 2 : 1) f
         static_cast<const uint16_t *>(prm.v) + kv_head(prm, bh) * prm.head_stride + (long long)rcls * D;
 
     typename P::Lane L;
-    P::init_lane(L, lane, wave, dil);
+    // the wave index in a scalar register: the epilogue and the global-row
+    // phase take it from here, so no lane register stays live across the loop
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    P::init_lane(L, lane, wave_u, dil);
 
     __syncthreads();   // s_gidx visible
 
@@ -720,6 +739,7 @@ __global__ void __launch_bounds__((BLK || XT || NAR) ? 256 : 512, NAR ? 2 : 1) f
     const bool valid = row < N;
     const int lo = row_lo(band, row);
     const int hi = row_hi(band, row);
+    const int lo4 = lo - 4 * h, hi4 = hi - 4 * h;
     const int wr0 = q0 + wave * 32;
     const int wr1 = imin(N - 1, wr0 + 31);
     const bool wave_active = wr0 < N;
@@ -822,7 +842,7 @@ __global__ void __launch_bounds__((BLK || XT || NAR) ? 256 : 512, NAR ? 2 : 1) f
     typename P::PFrag pf;
     if (in_w(tile_at(0))) {
         P::scores(sa, qf, L, kb0);
-        const EdgeMask em{tile_at(0) * BN, lo, hi, h};
+        const EdgeMask em{tile_at(0) * BN, lo4, hi4};
         const float mx = is_edge(tile_at(0))
                              ? BP::template region_b<false, true, true>(rs.o, pf, sb, rs.lpart, sa, L, vb0, em)
                              : BP::template region_b<false, true, false>(rs.o, pf, sb, rs.lpart, sa, L, vb0, em);
@@ -839,7 +859,7 @@ __global__ void __launch_bounds__((BLK || XT || NAR) ? 256 : 512, NAR ? 2 : 1) f
         if (j + 1 < nt) P::issue_v(L, vh, N, vw, tn * BN, dil);
         debug_sync();
         const bool cur = in_w(tile_at(j)), nxt = in_w(tn);
-        const EdgeMask em{tn * BN, lo, hi, h};
+        const EdgeMask em{tn * BN, lo4, hi4};
         const float nmu = rs.m == EEA_NEG_INF ? 0.f : -rs.m;
         if (cur) {
             if (nxt) {
@@ -964,7 +984,7 @@ __global__ void __launch_bounds__((BLK || XT || NAR) ? 256 : 512, NAR ? 2 : 1) f
     {
         const int elane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
         const int eh = elane >> 5;
-        const int erow = q0 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * 32 + (elane & 31);
+        const int erow = q0 + wave_u * 32 + (elane & 31);
         const int orow = rcls + erow * dil;   // row index in the stored sequence
         bool store = erow < N;
         for (int t = 0; t < ng; ++t) store &= s_gidx[t] != orow;   // global rows are written by the merge
@@ -993,7 +1013,7 @@ __global__ void __launch_bounds__((BLK || XT || NAR) ? 256 : 512, NAR ? 2 : 1) f
         // loop costs registers the loop needs.
         const int glane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
         const int gh = glane >> 5;
-        const int gwave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        const int gwave = wave_u;
         const int rb = gwave;
         if (rb * 32 < ng) {   // wave-uniform
             const int gt = rb * 32 + (glane & 31);

@@ -15,8 +15,9 @@ int tile_bm(int d, int f32) { (void)d; return 32 * ((f32 ? kBandThreadsF32 : kBa
 // would carry several key tiles that some of their waves skip (a wave's 32
 // rows see only a slice of the workgroup's key range), and a short loop
 // leaves the copy-in of the first tiles exposed. Four-wave workgroups, two
-// per CU, lose less of both (measured: 11-19 % faster for bands of 128 to
-// 1024 keys, even at 4096, 2.5 % slower on unbounded causal rows).
+// per CU (three at d = 64), lose less of both (measured: 11-19 % faster for
+// bands of 128 to 1024 keys, even at 4096, 2.5 % slower on unbounded causal
+// rows).
 bool band_is_narrow(int wl, int wr, int dil) { return dil == 1 && wl >= 0 && wr >= 0 && wl + wr + 1 <= kNarrowBand; }
 
 int band_tile_bm(int d, int f32, int block, int extra, int wl, int wr, int dil) {

@@ -193,14 +193,26 @@ struct Bf16Path {
     // With dil > 1 (init_lane given the same dil), tile row r is stored row
     // (k0 + r) * dil of the tensor at kh, and N counts the rows of that
     // strided sequence; rows past it still read as zeros.
+    // At d = 64 a wave's loads are 8 tile rows apart, and kx(r + 8) =
+    // kx(r) ^ 4 while vx(r + 8) = vx(r): load i's offsets follow from load
+    // 0's (the row part is a multiple of ROWB, the chunk part below it), so
+    // only load 0's stay live.
+    static __device__ __forceinline__ int k_off(const Lane &L, int i, int dil) {
+        if constexpr (D == 64) return ((L.ldk[0] ^ (64 * (i & 1))) + 8 * i * dil * ROWB);
+        else return L.ldk[i];
+    }
+    static __device__ __forceinline__ int v_off(const Lane &L, int i, int dil) {
+        if constexpr (D == 64) return L.ldv[0] + 8 * i * dil * ROWB;
+        else return L.ldv[i];
+    }
     static __device__ __forceinline__ void issue_k(const Lane &L, const elem_t *kh, int N, char *kbuf, int k0,
                                                    int dil = 1) {
         const __amdgpu_buffer_rsrc_t kr = head_rsrc(kh, (N - 1) * dil + 1);
         const unsigned base = (unsigned)k0 * dil * ROWB;
 #pragma unroll
         for (int i = 0; i < SPW; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (EEA_LDS void *)(kbuf + L.ldlds[i]), 16, base + L.ldk[i], 0,
-                                                     0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (EEA_LDS void *)(kbuf + L.ldlds[i]), 16,
+                                                     base + k_off(L, i, dil), 0, 0, 0);
     }
     static __device__ __forceinline__ void issue_v(const Lane &L, const elem_t *vh, int N, char *vbuf, int k0,
                                                    int dil = 1) {
@@ -208,8 +220,8 @@ struct Bf16Path {
         const unsigned base = (unsigned)k0 * dil * ROWB;
 #pragma unroll
         for (int i = 0; i < SPW; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (EEA_LDS void *)(vbuf + L.ldlds[i]), 16, base + L.ldv[i], 0,
-                                                     0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (EEA_LDS void *)(vbuf + L.ldlds[i]), 16,
+                                                     base + v_off(L, i, dil), 0, 0, 0);
     }
 
     static __device__ __forceinline__ void finish(Stage &, char *, char *, int) { wait_vmem(); }

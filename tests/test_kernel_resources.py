@@ -55,6 +55,21 @@ def test_band_kernel_fits_two_waves_per_simd(resources):
     assert seen == 8   # d = 64, 128 x (plain, dilated, narrow, narrow with fused global rows)
 
 
+def test_narrow_d64_fits_three_workgroups_per_cu(resources):
+    """The d = 64 narrow band instances (with and without the fused global
+    rows) run three four-wave workgroups per CU, three waves per SIMD: at
+    most 168 registers each (512 / 3, in granules of 8)."""
+    seen = 0
+    for k, v in resources.items():
+        if "fwd_band_bf16ILi64E" not in k:
+            continue
+        dil, blk, xt, nar, fus = _band_flags(k)
+        if nar:
+            seen += 1
+            assert v["vgpr"] + v["agpr"] <= 168, (k, v)
+    assert seen == 2
+
+
 def test_two_wave_backward_instances_fit(resources):
     """Backward instances that run two waves per SIMD keep within 256
     registers: at d = 64 every dQ instance and the dK/dV instances other than
