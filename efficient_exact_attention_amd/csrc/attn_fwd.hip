@@ -452,6 +452,17 @@ __global__ void __launch_bounds__(P::NT) fwd_kernel(const FwdParams prm) {
 // followed by a share of the vector work, so the vector instructions issue
 // while the MFMA before them is still in the matrix pipe.
 // ---------------------------------------------------------------------------
+// Materialise wave-uniform values in scalar registers at this point (an
+// empty asm per value, no instruction of its own).
+template <class T>
+__device__ __forceinline__ void scalar_ready1(const T &x) {
+    asm volatile("" ::"s"(x));
+}
+template <class... T>
+__device__ __forceinline__ void scalar_ready(const T &...x) {
+    (scalar_ready1(x), ...);
+}
+
 // Edge-tile mask: key k0 + mb*32 + acc_row(r, h) is visible to the lane's row
 // iff it lies in [lo, hi]; the half-wave offset 4h is folded into the bounds
 // (lo4 = lo - 4h, hi4 = hi - 4h), so h need not stay live in the loop.
@@ -665,6 +676,14 @@ __global__ void __launch_bounds__((BLK || XT || NAR) ? 256 : 512, NAR ? (D == 64
     typedef Bf16Path<D, (BLK || XT || NAR) ? 256 : 512> P;
     typedef BandPipe<P> BP;
     constexpr int BN = P::BN, BM = 32 * P::NW, MB = P::MB;
+
+    // Every scalar parameter is read here, in one batch: left to itself the
+    // compiler loads each from the kernel-argument segment where it is first
+    // needed and waits for it there, about ten memory round trips one after
+    // another before the first tile. Later uses reuse these loads.
+    scalar_ready(prm.q, prm.k, prm.v, prm.out, prm.lse, prm.part, prm.head_stride, prm.BH, prm.H, prm.group, prm.N,
+                 prm.wl, prm.wr, prm.block, prm.cap, prm.dil, prm.causal, prm.n_global, prm.num_qt, prm.chunks,
+                 prm.fuse_grows, prm.xcd_remap, prm.scale_log2, gridDim.x);
 
     // Two K and two V buffers as distinct objects: the copy into one is never
     // mistaken for a hazard of the reads from another.
