@@ -700,6 +700,7 @@ __global__ void __launch_bounds__((BLK || XT || NAR) ? 256 : 512, NAR ? (D == 64
     __shared__ __attribute__((aligned(1024))) char kgb[GSEP ? P::TILE_BYTES : 16];
     __shared__ __attribute__((aligned(1024))) char vgb[GSEP ? P::TILE_BYTES : 16];
     __shared__ int s_gidx[kMaxGlobal];
+    __shared__ float s_gml[FUS ? 2 : 1][2][64];   // global-row exchange: max, normaliser
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int ln = lane & 31, h = lane >> 5;
@@ -1023,52 +1024,71 @@ __global__ void __launch_bounds__((BLK || XT || NAR) ? 256 : 512, NAR ? (D == 64
         // tiles every key tile is some workgroup's own exactly once, so the
         // partials (output, max, normaliser) of the global rows cover every
         // key once, without a pass of their own over K and V: partial `unit`
-        // of each global row, combined by merge_kernel. One wave per row
-        // block of 32 global rows takes both own tiles; a global row sees
-        // every key up to the causal limit. No barrier: the last iteration's
-        // barrier follows the last copy.
+        // of each global row, combined by merge_kernel. Two waves per row
+        // block of 32 global rows, one own tile each (a last query tile may
+        // own one tile only); the second wave's state is folded into the
+        // first's through LDS (the K buffers, free once both own tiles are
+        // read), so each workgroup still writes one partial. A global row
+        // sees every key up to the causal limit.
         // Lane and wave indices are taken afresh (mbcnt, and the wave index
         // in a scalar register): keeping the entry ones live across the band
         // loop costs registers the loop needs.
         const int glane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
         const int gh = glane >> 5;
-        const int gwave = wave_u;
-        const int rb = gwave;
-        if (rb * 32 < ng) {   // wave-uniform
-            const int gt = rb * 32 + (glane & 31);
+        const int rb = wave_u >> 1, ot = wave_u & 1;   // row block, own tile
+        const bool rows = rb * 32 < ng;                // wave-uniform
+        const int gt = rb * 32 + (glane & 31);
+        RowState<P> gs;
+        gs.m = EEA_NEG_INF;
+        gs.lpart = 0.f;
+#pragma unroll
+        for (int db = 0; db < P::DB; ++db) gs.o[db] = f32x16{};
+        if (rows && ot < nown) {
             const int grow = gt < ng ? s_gidx[gt] : 0;
             typename P::QFrag gq;
             P::load_q(gq, qh, grow, gt < ng, gh);
             typename P::Lane GL;   // lane offsets taken afresh as well
-            P::init_lane(GL, glane, gwave, 1);
-            RowState<P> gs;
-            gs.m = EEA_NEG_INF;
-            gs.lpart = 0.f;
+            P::init_lane(GL, glane, wave_u, 1);
+            // own tile ot sits at position npre + ot, in buffer (npre + ot) & 1
+            const bool second = ((npre + ot) & 1) != 0;
+            const char *kbuf = second ? kb1 : kb0;
+            const char *vbuf = second ? vb1 : vb0;
+            const int kt = own_lo + ot;
+            f32x16 s[MB];
+            P::scores(s, gq, GL, kbuf);
 #pragma unroll
-            for (int db = 0; db < P::DB; ++db) gs.o[db] = f32x16{};
-            auto own_tile = [&](int t, const char *kbuf, const char *vbuf) __attribute__((always_inline)) {
-                const int kt = own_lo + t;
-                f32x16 s[MB];
-                P::scores(s, gq, GL, kbuf);
+            for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-                for (int mb = 0; mb < MB; ++mb)
+                for (int r = 0; r < 16; ++r) {
+                    const int jk = kt * BN + mb * 32 + acc_row(r, gh);
+                    const bool vis = (gt < ng) & (jk < N) & ((prm.causal == 0) | (jk <= grow));
+                    s[mb][r] = vis ? s[mb][r] : EEA_NEG_INF;
+                }
+            softmax_pv_step<P>(gs, s, c, GL, vbuf);
+        }
+        __syncthreads();   // both own tiles read: the K buffers take the exchange
+        static_assert(P::DB * 16 * 64 * 4 <= P::TILE_BYTES, "one wave's output fits a K buffer");
+        float *xo = reinterpret_cast<float *>(rb ? kb1 : kb0);
+        if (rows && ot == 1) {
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int jk = kt * BN + mb * 32 + acc_row(r, gh);
-                        const bool vis = (gt < ng) & (jk < N) & ((prm.causal == 0) | (jk <= grow));
-                        s[mb][r] = vis ? s[mb][r] : EEA_NEG_INF;
-                    }
-                softmax_pv_step<P>(gs, s, c, GL, vbuf);
-            };
-            // own tile t at position npre + t, in buffer (npre + t) & 1; a
-            // last query tile may own one tile only (nown == 1)
-            if (npre & 1) {
-                own_tile(0, kb1, vb1);
-                if (nown > 1) own_tile(1, kb0, vb0);
-            } else {
-                own_tile(0, kb0, vb0);
-                if (nown > 1) own_tile(1, kb1, vb1);
-            }
+            for (int db = 0; db < P::DB; ++db)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) xo[(db * 16 + i) * 64 + glane] = gs.o[db][i];
+            s_gml[rb][0][glane] = gs.m;
+            s_gml[rb][1][glane] = gs.lpart;
+        }
+        __syncthreads();
+        if (rows && ot == 0) {
+            const float m1 = s_gml[rb][0][glane], l1 = s_gml[rb][1][glane];
+            const float m = fmaxf(gs.m, m1);
+            const float w0 = gs.m == EEA_NEG_INF ? 0.f : fast_exp2(gs.m - m);
+            const float w1 = m1 == EEA_NEG_INF ? 0.f : fast_exp2(m1 - m);
+            gs.m = m;
+            gs.lpart = w0 * gs.lpart + w1 * l1;
+#pragma unroll
+            for (int db = 0; db < P::DB; ++db)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) gs.o[db][i] = w0 * gs.o[db][i] + w1 * xo[(db * 16 + i) * 64 + glane];
             if (gt < ng) {
                 const float l = sum_across_halves(gs.lpart);
                 float *dst = prm.part + (((long long)bh * ng + gt) * prm.chunks + unit) * (D + 2);
