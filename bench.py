@@ -146,6 +146,34 @@ def cpu_baseline(w, budget_s, gpu_out=None, gpu_lse=None):
                 full_call_seconds_extrapolated=round(t_used * w.B * w.H * w.N / nrows, 1)), max_err
 
 
+def gemm_reference(args):
+    """The vendor library's dense bf16 GEMM (torch.matmul, hipBLASLt on ROCm)
+    on large shapes: the matrix-core rate the GPU sustains under its power
+    limit, beside which the attention kernels' TFLOP/s can be read. One JSON
+    line per shape; not part of the attention path."""
+    import torch
+    for m, n, k in ((8192, 8192, 8192), (16384, 16384, 8192)):
+        g = torch.Generator(device="cuda").manual_seed(11)
+        a = torch.randn(m, k, device="cuda", dtype=torch.bfloat16, generator=g)
+        b = torch.randn(k, n, device="cuda", dtype=torch.bfloat16, generator=g)
+        for _ in range(max(args.warmup, 5)):
+            c = a @ b
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            c = a @ b
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        tf = 2.0 * m * n * k / ms / 1e9
+        print(json.dumps({"metric": "library bf16 GEMM throughput", "value": round(tf, 1), "unit": "TFLOP/s",
+                          "shape": [m, n, k], "ms_per_call": round(ms, 4), "steps": args.steps,
+                          "frac_of_published_peak": round(tf / PEAK_BF16, 4)}), flush=True)
+        del a, b, c
+    return 0
+
+
 def main():
     from efficient_exact_attention_amd import workloads as W
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
@@ -167,6 +195,9 @@ def main():
                     help="time the forward of a strided or random-block (BigBird-style) workload instead")
     ap.add_argument("--cold", action="store_true",
                     help="write a 1 GiB scratch buffer before every timed call (cold MALL)")
+    ap.add_argument("--gemm-reference", action="store_true",
+                    help="time the library bf16 GEMM (torch.matmul: hipBLASLt) on large square shapes instead: "
+                         "the dense matrix-core rate this GPU sustains at its power limit, for comparison")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="after timing, run one plain device copy of this many bytes "
                          "(calibration dispatch for HBM byte counters)")
@@ -186,6 +217,8 @@ def main():
         print("no GPU visible", file=sys.stderr)
         return 1
 
+    if args.gemm_reference:
+        return gemm_reference(args)
     if args.sweep:
         return sweep(args)
     if args.bwd:
