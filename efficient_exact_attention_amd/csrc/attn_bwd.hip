@@ -417,7 +417,9 @@ __global__ void __launch_bounds__(kBwdThreads, (dkdv_waves<D, MODE, XT>())) bwd_
         P::issue_k(L, gh, N, ok, q0, dil);
         P::issue_v(L, gh, N, ov, q0, dil);
     };
-    // per-row terms of tile t, loaded into registers now and stored to LDS later
+    // per-row terms of tile t, loaded into registers now and stored to LDS
+    // later (the LSE is scaled to log2 units at the store: a multiply here
+    // would wait for the load, and with it for every copy issued before it)
     auto row_terms = [&](int t, float &l2, float &dl) __attribute__((always_inline)) {
         l2 = 0.f;
         dl = 0.f;
@@ -426,7 +428,7 @@ __global__ void __launch_bounds__(kBwdThreads, (dkdv_waves<D, MODE, XT>())) bwd_
             const int i = tile_of(t) * BQ + tid;
             if (i < N) {
                 const long long gi = bh * prm.N + rcls + (long long)i * dil;   // row in the stored sequence
-                l2 = prm.lse[gi] * kLog2e;
+                l2 = prm.lse[gi];
                 dl = prm.delta[gi];
             }
         }
@@ -471,8 +473,8 @@ __global__ void __launch_bounds__(kBwdThreads, (dkdv_waves<D, MODE, XT>())) bwd_
             float nl2 = 0.f, ndl = 0.f;
             debug_sync();
             if (more) {
+                row_terms(t + 1, nl2, ndl);   // before the copies, as in the pipelined loop
                 issue(t + 1, nqk, nqv, nok, nov);
-                row_terms(t + 1, nl2, ndl);
             }
             debug_sync();
             const int q0 = tile_of(t) * BQ;
@@ -495,7 +497,9 @@ __global__ void __launch_bounds__(kBwdThreads, (dkdv_waves<D, MODE, XT>())) bwd_
                                   [&](int i) { return (i >= qlo) & (i <= qhi); });
             }
             if (more && tid < BQ) {
-                s_lse[sb ^ 1][tid] = nl2;
+                // first use of the loaded terms here (empty asm: no instruction)
+                asm volatile("" : "+v"(nl2), "+v"(ndl));
+                s_lse[sb ^ 1][tid] = nl2 * kLog2e;
                 s_dl[sb ^ 1][tid] = ndl;
             }
             wait_vmem();
@@ -506,7 +510,7 @@ __global__ void __launch_bounds__(kBwdThreads, (dkdv_waves<D, MODE, XT>())) bwd_
             float l2, dl;
             row_terms(0, l2, dl);
             if (tid < BQ) {
-                s_lse[0][tid] = l2;
+                s_lse[0][tid] = l2 * kLog2e;
                 s_dl[0][tid] = dl;
             }
             wait_vmem();
@@ -546,10 +550,11 @@ __global__ void __launch_bounds__(kBwdThreads, (dkdv_waves<D, MODE, XT>())) bwd_
             const bool more = t + 1 < T;
             float nl2 = 0.f, ndl = 0.f;
             debug_sync();
-            if (more) {
-                issue_rows(t + 1, nqk, nok);
-                row_terms(t + 1, nl2, ndl);
-            }
+            // the row terms' loads go out first: a wait for them (the
+            // compiler places one among the score MFMAs) then does not also
+            // wait for the tile copies issued after them
+            if (more) row_terms(t + 1, nl2, ndl);
+            if (more) issue_rows(t + 1, nqk, nok);
             issue_tr(t, qv_t, ov_t);
             debug_sync();
             const int q0 = tile_of(t) * BQ;
@@ -591,7 +596,9 @@ __global__ void __launch_bounds__(kBwdThreads, (dkdv_waves<D, MODE, XT>())) bwd_
             }
             act_prev = act;
             if (more && tid < BQ) {
-                s_lse[sb ^ 1][tid] = nl2;
+                // first use of the loaded terms here (empty asm: no instruction)
+                asm volatile("" : "+v"(nl2), "+v"(ndl));
+                s_lse[sb ^ 1][tid] = nl2 * kLog2e;
                 s_dl[sb ^ 1][tid] = ndl;
             }
             wait_vmem();
@@ -602,7 +609,7 @@ __global__ void __launch_bounds__(kBwdThreads, (dkdv_waves<D, MODE, XT>())) bwd_
             float l2, dl;
             row_terms(0, l2, dl);
             if (tid < BQ) {
-                s_lse[0][tid] = l2;
+                s_lse[0][tid] = l2 * kLog2e;
                 s_dl[0][tid] = dl;
             }
             wait_vmem();
