@@ -242,7 +242,7 @@ struct BwdPipe {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int r = 4 * g + e;
-                        float p = fast_exp2(__builtin_fmaf(s[mb][r], c, -l4[j][e]));
+                        float p = fast_exp2(__builtin_fmaf(s[mb][r], c, -(l4[j][e] * kLog2e)));
                         if constexpr (EDGE) {
                             const int i = q0 + 32 * mb + acc_row(r, h);
                             p = ((i >= qlo) & (i <= qhi)) ? p : 0.f;
@@ -322,7 +322,7 @@ __global__ void __launch_bounds__(kBwdThreads, (dkdv_waves<D, MODE, XT>())) bwd_
     __shared__ __attribute__((aligned(1024))) char qv1[P::TILE_BYTES];
     __shared__ __attribute__((aligned(1024))) char ok1[P::TILE_BYTES];
     __shared__ __attribute__((aligned(1024))) char ov1[P::TILE_BYTES];
-    __shared__ __attribute__((aligned(16))) float s_lse[2][BQ];   // LSE * log2(e)
+    __shared__ __attribute__((aligned(16))) float s_lse[2][BQ];   // LSE (natural log; scaled at use)
     __shared__ __attribute__((aligned(16))) float s_dl[2][BQ];    // rowsum(dO * O)
     __shared__ int s_g[kMaxGlobal];                               // sorted global positions
     __shared__ int s_hit[XT ? kBwdThreads : 1];                    // random-block list hits of one scan chunk
@@ -417,20 +417,21 @@ __global__ void __launch_bounds__(kBwdThreads, (dkdv_waves<D, MODE, XT>())) bwd_
         P::issue_k(L, gh, N, ok, q0, dil);
         P::issue_v(L, gh, N, ov, q0, dil);
     };
-    // per-row terms of tile t, loaded into registers now and stored to LDS
-    // later (the LSE is scaled to log2 units at the store: a multiply here
-    // would wait for the load, and with it for every copy issued before it)
-    auto row_terms = [&](int t, float &l2, float &dl) __attribute__((always_inline)) {
-        l2 = 0.f;
-        dl = 0.f;
-        if (tid < BQ) {
+    // per-row terms of tile t (LSE and rowsum(dO * O)) copied straight into
+    // LDS by one wave, like the tiles (rows past the sequence read as 0): a
+    // load into registers made the compiler wait for it, and with it for
+    // every tile copy issued before it, ahead of the next score MFMAs
+    auto issue_terms = [&](int t, float *lse_dst, float *dl_dst) __attribute__((always_inline)) {
+        if (wave == 0) {
             const long long bh = head_of(t);
-            const int i = tile_of(t) * BQ + tid;
-            if (i < N) {
-                const long long gi = bh * prm.N + rcls + (long long)i * dil;   // row in the stored sequence
-                l2 = prm.lse[gi];
-                dl = prm.delta[gi];
-            }
+            const int i = tile_of(t) * BQ + lane;
+            const unsigned off = (unsigned)(rcls + i * dil) * 4u;   // row in the stored sequence
+            const __amdgpu_buffer_rsrc_t lr =
+                __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(prm.lse + bh * prm.N), 0, prm.N * 4, 0x00020000);
+            const __amdgpu_buffer_rsrc_t dr =
+                __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(prm.delta + bh * prm.N), 0, prm.N * 4, 0x00020000);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(lr, (EEA_LDS void *)lse_dst, 4, off, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(dr, (EEA_LDS void *)dl_dst, 4, off, 0, 0, 0);
         }
     };
 
@@ -450,7 +451,7 @@ __global__ void __launch_bounds__(kBwdThreads, (dkdv_waves<D, MODE, XT>())) bwd_
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int r = 4 * g + e;
-                    float p = fast_exp2(__builtin_fmaf(s[mb][r], c, -l4[e]));
+                    float p = fast_exp2(__builtin_fmaf(s[mb][r], c, -(l4[e] * kLog2e)));
                     if (cl == TILE_EDGE) p = vis(row(32 * mb + acc_row(r, h))) ? p : 0.f;
                     s[mb][r] = p;
                     dp[mb][r] = p * (dp[mb][r] - d4[e]);
@@ -470,11 +471,10 @@ __global__ void __launch_bounds__(kBwdThreads, (dkdv_waves<D, MODE, XT>())) bwd_
         auto step = [&](int t, const char *qk, const char *qv, const char *ok, const char *ov, char *nqk, char *nqv,
                         char *nok, char *nov, int sb) __attribute__((always_inline)) {
             const bool more = t + 1 < T;
-            float nl2 = 0.f, ndl = 0.f;
             debug_sync();
             if (more) {
-                row_terms(t + 1, nl2, ndl);   // before the copies, as in the pipelined loop
                 issue(t + 1, nqk, nqv, nok, nov);
+                issue_terms(t + 1, s_lse[sb ^ 1], s_dl[sb ^ 1]);
             }
             debug_sync();
             const int q0 = tile_of(t) * BQ;
@@ -496,23 +496,12 @@ __global__ void __launch_bounds__(kBwdThreads, (dkdv_waves<D, MODE, XT>())) bwd_
                     tile_products(qk, qv, ok, ov, sb, cl, [&](int r) { return q0 + r; },
                                   [&](int i) { return (i >= qlo) & (i <= qhi); });
             }
-            if (more && tid < BQ) {
-                // first use of the loaded terms here (empty asm: no instruction)
-                asm volatile("" : "+v"(nl2), "+v"(ndl));
-                s_lse[sb ^ 1][tid] = nl2 * kLog2e;
-                s_dl[sb ^ 1][tid] = ndl;
-            }
             wait_vmem();
             __syncthreads();
         };
         if (T > 0) {
             issue(0, qk0, qv0, ok0, ov0);
-            float l2, dl;
-            row_terms(0, l2, dl);
-            if (tid < BQ) {
-                s_lse[0][tid] = l2 * kLog2e;
-                s_dl[0][tid] = dl;
-            }
+            issue_terms(0, s_lse[0], s_dl[0]);
             wait_vmem();
             __syncthreads();
         }
@@ -548,13 +537,11 @@ __global__ void __launch_bounds__(kBwdThreads, (dkdv_waves<D, MODE, XT>())) bwd_
         auto pstep = [&](int t, const char *qk, const char *ok, char *nqk, char *nok, char *qv_t, char *ov_t,
                          const char *qv_p, const char *ov_p, int sb) __attribute__((always_inline)) {
             const bool more = t + 1 < T;
-            float nl2 = 0.f, ndl = 0.f;
             debug_sync();
-            // the row terms' loads go out first: a wait for them (the
-            // compiler places one among the score MFMAs) then does not also
-            // wait for the tile copies issued after them
-            if (more) row_terms(t + 1, nl2, ndl);
-            if (more) issue_rows(t + 1, nqk, nok);
+            if (more) {
+                issue_rows(t + 1, nqk, nok);
+                issue_terms(t + 1, s_lse[sb ^ 1], s_dl[sb ^ 1]);
+            }
             issue_tr(t, qv_t, ov_t);
             debug_sync();
             const int q0 = tile_of(t) * BQ;
@@ -595,23 +582,12 @@ __global__ void __launch_bounds__(kBwdThreads, (dkdv_waves<D, MODE, XT>())) bwd_
                 P::pack_p(pd, dp);
             }
             act_prev = act;
-            if (more && tid < BQ) {
-                // first use of the loaded terms here (empty asm: no instruction)
-                asm volatile("" : "+v"(nl2), "+v"(ndl));
-                s_lse[sb ^ 1][tid] = nl2 * kLog2e;
-                s_dl[sb ^ 1][tid] = ndl;
-            }
             wait_vmem();
             __syncthreads();
         };
         if (T > 0) {
             issue_rows(0, qk0, ok0);
-            float l2, dl;
-            row_terms(0, l2, dl);
-            if (tid < BQ) {
-                s_lse[0][tid] = l2 * kLog2e;
-                s_dl[0][tid] = dl;
-            }
+            issue_terms(0, s_lse[0], s_dl[0]);
             wait_vmem();
             __syncthreads();
         }
@@ -645,7 +621,7 @@ __global__ void __launch_bounds__(kBwdThreads, (dkdv_waves<D, MODE, XT>())) bwd_
             P::issue(st, L, gh, gh, ok0, ov0, src, s_g[0]);
             if (tid < BQ) {
                 const bool gv = tid < ng;
-                s_lse[0][tid] = gv ? prm.lse[bh * N + s_g[tid]] * kLog2e : 0.f;
+                s_lse[0][tid] = gv ? prm.lse[bh * N + s_g[tid]] : 0.f;
                 s_dl[0][tid] = gv ? prm.delta[bh * N + s_g[tid]] : 0.f;
             }
             wait_vmem();
@@ -677,7 +653,7 @@ __global__ void __launch_bounds__(kBwdThreads, (dkdv_waves<D, MODE, XT>())) bwd_
                 P::issue_v(L, gh, N, ov0, q0);
                 if (tid < BQ) {
                     const int i = q0 + tid;
-                    s_lse[0][tid] = i < N ? prm.lse[bh * N + i] * kLog2e : 0.f;
+                    s_lse[0][tid] = i < N ? prm.lse[bh * N + i] : 0.f;
                     s_dl[0][tid] = i < N ? prm.delta[bh * N + i] : 0.f;
                 }
                 wait_vmem();
