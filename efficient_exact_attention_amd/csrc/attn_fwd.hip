@@ -784,6 +784,56 @@ __global__ void __launch_bounds__((BLK || XT || NAR) ? 256 : 512, NAR ? (D == 64
     // window.
     static_assert(kMaxGlobal <= BN, "the global columns fit one gathered tile");
     auto gathered = [&](const char *kbuf, const char *vbuf) __attribute__((always_inline)) {
+        if (ng <= 32) {
+            // every global column in the tile's first 32 columns: the second
+            // row block of scores would be all masked, so only the first one
+            // is computed (its products, exponentials and PV steps; the
+            // skipped ones would add exact zeros, so the bits are the same)
+            f32x16 s0 = f32x16{};
+#pragma unroll
+            for (int ks = 0; ks < P::KS; ++ks)
+                s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8 *>(kbuf + L.krd[ks]),
+                                                             qf.x[ks], s0, 0, 0, 0);
+            float mx = EEA_NEG_INF;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int col = acc_row(r, h);
+                const int g = s_gidx[col];
+                const bool vis = (col < ng) & ((prm.causal == 0) | (g <= row)) & ((g < lo) | (g > hi));
+                s0[r] = vis ? s0[r] : EEA_NEG_INF;
+                mx = fmaxf(mx, s0[r]);
+            }
+            mx = max_across_halves(mx);
+            const float mnew = fmaxf(rs.m, mx * c);
+            if (__any(mnew > rs.m + kRescaleLog2)) {
+                const float alpha = (mnew == EEA_NEG_INF) ? 1.f : fast_exp2(rs.m - mnew);
+                rs.m = mnew;
+                rs.lpart *= alpha;
+#pragma unroll
+                for (int db = 0; db < P::DB; ++db) rs.o[db] *= alpha;
+            }
+            const float mu = (rs.m == EEA_NEG_INF) ? 0.f : rs.m;
+            float sum = 0.f;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float pr = fast_exp2(__builtin_fmaf(s0[r], c, -mu));
+                s0[r] = pr;
+                sum += pr;
+            }
+            rs.lpart += sum;
+#pragma unroll
+            for (int st = 0; st < 2; ++st) {
+                const int r0 = 8 * st;
+                f32x8 x = {s0[r0 + 0], s0[r0 + 1], s0[r0 + 2], s0[r0 + 3],
+                           s0[r0 + 4], s0[r0 + 5], s0[r0 + 6], s0[r0 + 7]};
+                const bf16x8 pw = __builtin_convertvector(x, bf16x8);
+#pragma unroll
+                for (int db = 0; db < P::DB; ++db)
+                    rs.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(P::v_operand(L, vbuf, db, st), pw, rs.o[db],
+                                                                       0, 0, 0);
+            }
+            return;
+        }
         f32x16 s[MB];
         P::scores(s, qf, L, kbuf);
 #pragma unroll
