@@ -662,15 +662,18 @@ __device__ __forceinline__ void raise_max(RowState<P> &rs, float mx, float c) {
 // tiles of the log-spaced strided and random-block rules follow the band.
 // Each is folded to a constant where off, since at 512 threads (two waves
 // per SIMD, 256 registers each) the kernel has almost no registers to spare;
-// the block-rule and extra-tile instances run 256 threads (one wave per
-// SIMD) for that reason. NAR (narrow bands, band_is_narrow) is the plain
+// the block-rule and extra-tile instances run 256 threads for that reason:
+// the block-rule one at one wave per SIMD, the extra-tile one with two
+// workgroups per CU (its unpipelined extra tiles wait on their copies, which
+// the other workgroup's waves fill; 30 % faster on the strided rule than one
+// workgroup per CU). NAR (narrow bands, band_is_narrow) is the plain
 // kernel at 256 threads with the two-waves-per-SIMD budget, so two
 // workgroups share a CU; at d = 64 it fits 168 registers and three share a
 // CU (three waves per SIMD), which hides the copy-in, epilogue and global-row
 // phases of its short loops behind the other workgroups' loops (c. 15 % on a
 // band of 513 keys).
 template <int D, bool DIL, bool BLK, bool XT = false, bool NAR = false, bool FUS = false>
-__global__ void __launch_bounds__((BLK || XT || NAR) ? 256 : 512, NAR ? (D == 64 ? 3 : 2) : 1)
+__global__ void __launch_bounds__((BLK || XT || NAR) ? 256 : 512, NAR ? (D == 64 ? 3 : 2) : XT ? 2 : 1)
     fwd_band_bf16(const FwdParams prm) {
     constexpr bool GEN = BLK;
     typedef Bf16Path<D, (BLK || XT || NAR) ? 256 : 512> P;
@@ -968,17 +971,31 @@ __global__ void __launch_bounds__((BLK || XT || NAR) ? 256 : 512, NAR ? (D == 64
         // and within the causal limit; every tile is visited once per
         // pattern entry.
         const int q1 = imin(N - 1, q0 + BM - 1);
+        // whether position j is a global token: a scan of the few, else a
+        // binary search of the sorted positions in s_gidx (seven reads at
+        // most, each lane its own j)
+        auto is_global = [&](int j) __attribute__((always_inline)) {
+            if (ng <= 6) {
+                bool g = false;
+                for (int t = 0; t < ng; ++t) g |= s_gidx[t] == j;
+                return g;
+            }
+            int pos = 0;   // entries below j
+#pragma unroll
+            for (int step = 32; step > 0; step >>= 1)
+                if (pos + step <= ng && s_gidx[pos + step - 1] < j) pos += step;
+            return pos < ng && s_gidx[pos] == j;
+        };
+        static_assert(kMaxGlobal == 64 && BN == 64, "the search covers 64 positions, one tile row per lane");
         auto extra_tile = [&](int k0, bool take, auto vis) __attribute__((always_inline)) {
             P::issue_k(L, kh, N, kb0, k0);
             P::issue_v(L, vh, N, vb0, k0);
             wait_vmem();
             __syncthreads();
             if (take) {
-                unsigned long long gm = 0;   // global columns of this tile
-                for (int t = 0; t < ng; ++t) {
-                    const int r = s_gidx[t] - k0;
-                    if (r >= 0 && r < BN) gm |= 1ull << r;
-                }
+                // global columns of this tile, one bit per key: lane l tests
+                // key k0 + l
+                const unsigned long long gm = __ballot(is_global(k0 + lane));
                 f32x16 s[MB];
                 P::scores(s, qf, L, kb0);
 #pragma unroll
@@ -1010,7 +1027,7 @@ __global__ void __launch_bounds__((BLK || XT || NAR) ? 256 : 512, NAR ? (D == 64
                     const int o = st << m;
                     const int j = side ? row + o : row - o;
                     bool ok = valid & (j >= 0) & (j < N) & ((j < lo) | (j > hi));
-                    for (int t = 0; t < ng; ++t) ok &= s_gidx[t] != j;   // pairs of the gathered global tile
+                    if (ng > 0) ok &= !is_global(j);   // pairs of the gathered global tile
                     if (!__any(ok)) continue;
                     const int jj = ok ? j : 0;   // a row that exists; its result is dropped
                     const float part = dot_row_half(kh + (long long)jj * D, qf.x, h);
