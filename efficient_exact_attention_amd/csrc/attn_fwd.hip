@@ -998,15 +998,25 @@ __global__ void __launch_bounds__((BLK || XT || NAR) ? 256 : 512, NAR ? (D == 64
                 const unsigned long long gm = __ballot(is_global(k0 + lane));
                 f32x16 s[MB];
                 P::scores(s, qf, L, kb0);
+                // no mask needed when every key of the tile passes for every
+                // row of the wave (all rows exist, the tile lies inside the
+                // listed block, outside every row's band, holds no global
+                // column and, under a causal mask, precedes every row)
+                const int k1 = k0 + BN - 1;
+                const bool full = (wr0 + 31 < N) & vis(k0) & vis(k1) & (gm == 0) &
+                                  (classify(band, wr0, wr0 + 31, k0, k1) == TILE_SKIP) &
+                                  ((prm.causal == 0) | (k1 <= wr0));
+                if (!full) {
 #pragma unroll
-                for (int mb = 0; mb < MB; ++mb)
+                    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int jr = mb * 32 + acc_row(r, h), j = k0 + jr;
-                        const bool ok = valid & (j < N) & ((j < lo) | (j > hi)) & ((prm.causal == 0) | (j <= row)) &
-                                        !((gm >> jr) & 1ull) && vis(j);
-                        s[mb][r] = ok ? s[mb][r] : EEA_NEG_INF;
-                    }
+                        for (int r = 0; r < 16; ++r) {
+                            const int jr = mb * 32 + acc_row(r, h), j = k0 + jr;
+                            const bool ok = valid & (j < N) & ((j < lo) | (j > hi)) & ((prm.causal == 0) | (j <= row)) &
+                                            !((gm >> jr) & 1ull) && vis(j);
+                            s[mb][r] = ok ? s[mb][r] : EEA_NEG_INF;
+                        }
+                }
                 softmax_pv_step<P>(rs, s, c, L, vb0);
             }
             __syncthreads();
