@@ -837,17 +837,33 @@ __global__ void __launch_bounds__((BLK || XT || NAR) ? 256 : 512, NAR ? (D == 64
             }
             return;
         }
+        // clean: every global column passes for every row of the wave (all
+        // rows exist, no global position lies in any row's band, and under a
+        // causal mask every one precedes every row); only the columns past
+        // the last global are then masked. The positions are sorted, and
+        // the band ends never decrease with the row. (Wave-uniform: a scalar
+        // branch.)
+        const int gmin = __builtin_amdgcn_readfirstlane(s_gidx[0]);
+        const int gmax = __builtin_amdgcn_readfirstlane(s_gidx[ng - 1]);
+        const int w0 = q0 + wave_u * 32;
+        const bool clean = (w0 + 31 < N) & ((gmax < row_lo(band, w0)) | (gmin > row_hi(band, w0 + 31))) &
+                           ((prm.causal == 0) | (gmax <= w0));
         f32x16 s[MB];
         P::scores(s, qf, L, kbuf);
+        if (!clean || ng < kMaxGlobal) {
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
+            for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int col = mb * 32 + acc_row(r, h);
-                const int g = s_gidx[col < kMaxGlobal ? col : 0];
-                const bool vis = (col < ng) & ((prm.causal == 0) | (g <= row)) & ((g < lo) | (g > hi));
-                s[mb][r] = vis ? s[mb][r] : EEA_NEG_INF;
-            }
+                for (int r = 0; r < 16; ++r) {
+                    const int col = mb * 32 + acc_row(r, h);
+                    bool vis = col < ng;
+                    if (!clean) {
+                        const int g = s_gidx[col < kMaxGlobal ? col : 0];
+                        vis &= ((prm.causal == 0) | (g <= row)) & ((g < lo) | (g > hi));
+                    }
+                    s[mb][r] = vis ? s[mb][r] : EEA_NEG_INF;
+                }
+        }
         softmax_pv_step<P>(rs, s, c, L, vbuf);
     };
     if (ng > 0) {
