@@ -474,7 +474,7 @@ int fwd_impl(const void *q, const void *k, const void *v, void *out, float *lse,
 
     size_t need = 0;
     if (ng > 0) {
-        if (eea::fuse_global_rows(dtype == ATTN_F32, m.dil, m.extra(), bm, (int)nqt)) {
+        if (eea::fuse_global_rows(dtype == ATTN_F32, d, m.dil, bm, ng)) {
             p.fuse_grows = 1;
             p.chunks = (int)nqt;
             p.chunk_tiles = 2;

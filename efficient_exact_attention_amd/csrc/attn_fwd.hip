@@ -900,10 +900,10 @@ __global__ void __launch_bounds__((BLK || XT || NAR) ? 256 : 512, NAR ? (D == 64
     // kt_lo .. kt_hi. Position nt and beyond map past kt_hi (no wave's tile).
     // The online softmax does not depend on the order of the tiles.
     // Only the FUS instances (128-row workgroups with global tokens: the
-    // narrow and block-rule ones) fuse; in the others the order is the plain
-    // one at compile time.
+    // narrow, block-rule and extra-tile ones) fuse; in the others the order
+    // is the plain one at compile time.
     constexpr bool CANFUSE = FUS;
-    static_assert(!FUS || ((BLK || NAR) && !XT && !DIL), "fusion needs 128-row workgroups");
+    static_assert(!FUS || ((BLK || NAR || XT) && !DIL), "fusion needs 128-row workgroups");
     const bool fuse = CANFUSE && ng > 0 && prm.fuse_grows;
     const int nt = kt_hi - kt_lo + 1;
     const int own_lo = fuse ? imax(unit * 2, kt_lo) : kt_hi + 1;
@@ -979,6 +979,108 @@ __global__ void __launch_bounds__((BLK || XT || NAR) ? 256 : 512, NAR ? (D == 64
         iter(j + 1, sb, sa, kb0, vb1, kb1, vb0);
     }
 
+    // The fused global-row phase runs right after the band loop when the
+    // extra-tile rules follow (their tiles reuse the band buffers), else
+    // after the epilogue.
+    auto global_rows = [&]() __attribute__((always_inline)) {
+        // --- the global rows against this workgroup's own key tiles (the
+        // keys under its 128 query rows, positions npre and npre + 1 of the
+        // loop, still in the buffers of those positions). Over all query
+        // tiles every key tile is some workgroup's own exactly once, so the
+        // partials (output, max, normaliser) of the global rows cover every
+        // key once, without a pass of their own over K and V: partial `unit`
+        // of each global row, combined by merge_kernel. Two waves per row
+        // block of 32 global rows, one own tile each (a last query tile may
+        // own one tile only); the second wave's state is folded into the
+        // first's through LDS (the K buffers, free once both own tiles are
+        // read), so each workgroup still writes one partial. A global row
+        // sees every key up to the causal limit.
+        // Lane and wave indices are taken afresh (mbcnt, and the wave index
+        // in a scalar register): keeping the entry ones live across the band
+        // loop costs registers the loop needs.
+        const int glane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+        const int gh = glane >> 5;
+        const int rb = wave_u >> 1, ot = wave_u & 1;   // row block, own tile
+        const bool rows = rb * 32 < ng;                // wave-uniform
+        const int gt = rb * 32 + (glane & 31);
+        RowState<P> gs;
+        gs.m = EEA_NEG_INF;
+        gs.lpart = 0.f;
+#pragma unroll
+        for (int db = 0; db < P::DB; ++db) gs.o[db] = f32x16{};
+        if (rows && ot < nown) {
+            const int grow = gt < ng ? s_gidx[gt] : 0;
+            typename P::QFrag gq;
+            P::load_q(gq, qh, grow, gt < ng, gh);
+            typename P::Lane GL;   // lane offsets taken afresh as well
+            P::init_lane(GL, glane, wave_u, 1);
+            // own tile ot sits at position npre + ot, in buffer (npre + ot) & 1
+            const bool second = ((npre + ot) & 1) != 0;
+            const char *kbuf = second ? kb1 : kb0;
+            const char *vbuf = second ? vb1 : vb0;
+            const int kt = own_lo + ot;
+            f32x16 s[MB];
+            P::scores(s, gq, GL, kbuf);
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int jk = kt * BN + mb * 32 + acc_row(r, gh);
+                    const bool vis = (gt < ng) & (jk < N) & ((prm.causal == 0) | (jk <= grow));
+                    s[mb][r] = vis ? s[mb][r] : EEA_NEG_INF;
+                }
+            softmax_pv_step<P>(gs, s, c, GL, vbuf);
+        }
+        __syncthreads();   // both own tiles read: the K buffers take the exchange
+        static_assert(P::DB * 16 * 64 * 4 <= P::TILE_BYTES, "one wave's output fits a K buffer");
+        float *xo = reinterpret_cast<float *>(rb ? kb1 : kb0);
+        if (rows && ot == 1) {
+#pragma unroll
+            for (int db = 0; db < P::DB; ++db)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) xo[(db * 16 + i) * 64 + glane] = gs.o[db][i];
+            s_gml[rb][0][glane] = gs.m;
+            s_gml[rb][1][glane] = gs.lpart;
+        }
+        __syncthreads();
+        if (rows && ot == 0) {
+            const float m1 = s_gml[rb][0][glane], l1 = s_gml[rb][1][glane];
+            const float m = fmaxf(gs.m, m1);
+            const float w0 = gs.m == EEA_NEG_INF ? 0.f : fast_exp2(gs.m - m);
+            const float w1 = m1 == EEA_NEG_INF ? 0.f : fast_exp2(m1 - m);
+            gs.m = m;
+            gs.lpart = w0 * gs.lpart + w1 * l1;
+#pragma unroll
+            for (int db = 0; db < P::DB; ++db)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) gs.o[db][i] = w0 * gs.o[db][i] + w1 * xo[(db * 16 + i) * 64 + glane];
+            if (gt < ng) {
+                const float l = sum_across_halves(gs.lpart);
+                float *dst = prm.part + (((long long)bh * ng + gt) * prm.chunks + unit) * (D + 2);
+#pragma unroll
+                for (int db = 0; db < P::DB; ++db)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        float *pp = dst + db * 32 + 8 * g + 4 * gh;
+                        pp[0] = gs.o[db][4 * g + 0];
+                        pp[1] = gs.o[db][4 * g + 1];
+                        pp[2] = gs.o[db][4 * g + 2];
+                        pp[3] = gs.o[db][4 * g + 3];
+                    }
+                if (gh == 0) {
+                    dst[D] = gs.m;
+                    dst[D + 1] = l;
+                }
+            }
+        }
+    };
+
+    if constexpr (XT) {
+        if (fuse) {
+            global_rows();
+            __syncthreads();   // the own tiles and the exchange buffers are free again
+        }
+    }
     if constexpr (XT) {
         // --- pairs of the strided and random-block rules beyond the band:
         // the random-block rule as unpipelined extra key tiles, the strided
@@ -1110,97 +1212,8 @@ __global__ void __launch_bounds__((BLK || XT || NAR) ? 256 : 512, NAR ? (D == 64
         }
     }
 
-    if (fuse) {
-        // --- the global rows against this workgroup's own key tiles (the
-        // keys under its 128 query rows, positions npre and npre + 1 of the
-        // loop, still in the buffers of those positions). Over all query
-        // tiles every key tile is some workgroup's own exactly once, so the
-        // partials (output, max, normaliser) of the global rows cover every
-        // key once, without a pass of their own over K and V: partial `unit`
-        // of each global row, combined by merge_kernel. Two waves per row
-        // block of 32 global rows, one own tile each (a last query tile may
-        // own one tile only); the second wave's state is folded into the
-        // first's through LDS (the K buffers, free once both own tiles are
-        // read), so each workgroup still writes one partial. A global row
-        // sees every key up to the causal limit.
-        // Lane and wave indices are taken afresh (mbcnt, and the wave index
-        // in a scalar register): keeping the entry ones live across the band
-        // loop costs registers the loop needs.
-        const int glane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
-        const int gh = glane >> 5;
-        const int rb = wave_u >> 1, ot = wave_u & 1;   // row block, own tile
-        const bool rows = rb * 32 < ng;                // wave-uniform
-        const int gt = rb * 32 + (glane & 31);
-        RowState<P> gs;
-        gs.m = EEA_NEG_INF;
-        gs.lpart = 0.f;
-#pragma unroll
-        for (int db = 0; db < P::DB; ++db) gs.o[db] = f32x16{};
-        if (rows && ot < nown) {
-            const int grow = gt < ng ? s_gidx[gt] : 0;
-            typename P::QFrag gq;
-            P::load_q(gq, qh, grow, gt < ng, gh);
-            typename P::Lane GL;   // lane offsets taken afresh as well
-            P::init_lane(GL, glane, wave_u, 1);
-            // own tile ot sits at position npre + ot, in buffer (npre + ot) & 1
-            const bool second = ((npre + ot) & 1) != 0;
-            const char *kbuf = second ? kb1 : kb0;
-            const char *vbuf = second ? vb1 : vb0;
-            const int kt = own_lo + ot;
-            f32x16 s[MB];
-            P::scores(s, gq, GL, kbuf);
-#pragma unroll
-            for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int jk = kt * BN + mb * 32 + acc_row(r, gh);
-                    const bool vis = (gt < ng) & (jk < N) & ((prm.causal == 0) | (jk <= grow));
-                    s[mb][r] = vis ? s[mb][r] : EEA_NEG_INF;
-                }
-            softmax_pv_step<P>(gs, s, c, GL, vbuf);
-        }
-        __syncthreads();   // both own tiles read: the K buffers take the exchange
-        static_assert(P::DB * 16 * 64 * 4 <= P::TILE_BYTES, "one wave's output fits a K buffer");
-        float *xo = reinterpret_cast<float *>(rb ? kb1 : kb0);
-        if (rows && ot == 1) {
-#pragma unroll
-            for (int db = 0; db < P::DB; ++db)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) xo[(db * 16 + i) * 64 + glane] = gs.o[db][i];
-            s_gml[rb][0][glane] = gs.m;
-            s_gml[rb][1][glane] = gs.lpart;
-        }
-        __syncthreads();
-        if (rows && ot == 0) {
-            const float m1 = s_gml[rb][0][glane], l1 = s_gml[rb][1][glane];
-            const float m = fmaxf(gs.m, m1);
-            const float w0 = gs.m == EEA_NEG_INF ? 0.f : fast_exp2(gs.m - m);
-            const float w1 = m1 == EEA_NEG_INF ? 0.f : fast_exp2(m1 - m);
-            gs.m = m;
-            gs.lpart = w0 * gs.lpart + w1 * l1;
-#pragma unroll
-            for (int db = 0; db < P::DB; ++db)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) gs.o[db][i] = w0 * gs.o[db][i] + w1 * xo[(db * 16 + i) * 64 + glane];
-            if (gt < ng) {
-                const float l = sum_across_halves(gs.lpart);
-                float *dst = prm.part + (((long long)bh * ng + gt) * prm.chunks + unit) * (D + 2);
-#pragma unroll
-                for (int db = 0; db < P::DB; ++db)
-#pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        float *pp = dst + db * 32 + 8 * g + 4 * gh;
-                        pp[0] = gs.o[db][4 * g + 0];
-                        pp[1] = gs.o[db][4 * g + 1];
-                        pp[2] = gs.o[db][4 * g + 2];
-                        pp[3] = gs.o[db][4 * g + 3];
-                    }
-                if (gh == 0) {
-                    dst[D] = gs.m;
-                    dst[D + 1] = l;
-                }
-            }
-        }
+    if constexpr (!XT) {
+        if (fuse) global_rows();
     }
 }
 
@@ -1282,6 +1295,9 @@ static hipError_t launch_impl(const FwdParams &p0, hipStream_t stream) {
     if (!F32 && p.dil == 1 && p.causal && p.BH % 8 == 0 && p.num_qt <= 32) p.xcd_remap = 2;
     if constexpr (F32)
         hipLaunchKernelGGL((fwd_kernel<PB, MODE_BAND>), dim3(grid), dim3(PB::NT), 0, stream, p);
+    else if ((p.stride > 0 || p.rand_block > 0) && p.fuse_grows)
+        hipLaunchKernelGGL((fwd_band_bf16<D, false, false, true, false, true>), dim3(grid), dim3(kBandThreadsBlock), 0,
+                           stream, p);
     else if (p.stride > 0 || p.rand_block > 0)
         hipLaunchKernelGGL((fwd_band_bf16<D, false, false, true>), dim3(grid), dim3(kBandThreadsBlock), 0, stream, p);
     else if (p.block > 0 && p.fuse_grows)

@@ -47,11 +47,14 @@ int global_chunks(int BH, int N, int d, int f32, int *chunk_tiles) {
 // workgroup computes their partials on the two key tiles under its own query
 // rows (visited last, so they are still in LDS when its band loop ends), one
 // partial per workgroup, so the split-key pass (which reads K and V once
-// more) and its launch disappear. Not with the strided or random-block rules,
-// whose extra tiles reuse the buffers after the band loop.
-bool fuse_global_rows(int f32, int dil, int extra, int bm, int num_qt) {
-    (void)num_qt;
-    return !f32 && dil == 1 && !extra && bm == 128;
+// more) and its launch disappear. With the strided or random-block rules the
+// phase runs before their extra tiles, which reuse the buffers. More than 32
+// global rows at d = 128 stay with the split-key pass: one partial of d + 2
+// floats per global row and query tile is then more to write and merge than
+// the pass reads (measured 7-28 % slower fused; at d = 64 fused is 1-6 %
+// faster on the narrow band, about even with the extra tiles).
+bool fuse_global_rows(int f32, int d, int dil, int bm, int ng) {
+    return !f32 && dil == 1 && bm == 128 && (ng <= 32 || d == 64);
 }
 
 // ---------------------------------------------------------------------------

@@ -139,7 +139,7 @@ hipError_t launch_forward(const FwdParams &p, int d, int f32, hipStream_t stream
 int global_chunks(int BH, int N, int d, int f32, int *chunk_tiles);
 // Whether the band pass computes the global rows' partials itself (one per
 // query tile of bm rows, over its own key tiles), instead of the split-key pass.
-bool fuse_global_rows(int f32, int dil, int extra, int bm, int num_qt);
+bool fuse_global_rows(int f32, int d, int dil, int bm, int ng);
 
 // Device address, on the current device, of the allocation-free forward's
 // scratch array (kNoAllocScratchBytes); looked up once per device.

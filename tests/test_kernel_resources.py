@@ -43,7 +43,8 @@ def _band_flags(name):
 def test_band_kernel_fits_two_waves_per_simd(resources):
     """The band instances that run two waves per SIMD (plain and dilated at
     512 threads; narrow, with and without the fused global rows, and the
-    strided/random-block instance at 256 threads with two workgroups per CU)
+    strided/random-block instances, with and without the fused global rows,
+    at 256 threads with two workgroups per CU)
     keep within 256 registers."""
     seen = 0
     for k, v in resources.items():
@@ -53,7 +54,7 @@ def test_band_kernel_fits_two_waves_per_simd(resources):
         if not blk:
             seen += 1
             assert v["vgpr"] + v["agpr"] <= 256, (k, v)
-    assert seen == 10   # d = 64, 128 x (plain, dilated, narrow, narrow with fused global rows, extra tiles)
+    assert seen == 12   # d = 64, 128 x (plain, dilated, narrow, narrow and extra tiles with and without fused global rows)
 
 
 def test_narrow_d64_fits_three_workgroups_per_cu(resources):
