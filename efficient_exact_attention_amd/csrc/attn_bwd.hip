@@ -306,22 +306,25 @@ struct BwdPipe {
 // log-spaced strided or the random-block rule, as extra query tiles.
 template <int D, bool DIL, int MODE, bool XT = false>
 __global__ void __launch_bounds__(kBwdThreads, (dkdv_waves<D, MODE, XT>())) bwd_dkdv(const BwdParams prm) {
-    typedef Bf16Path<D, kBwdThreads> P;
+    // Q and dO tiles are read both ways (row reads for S and dP, transpose
+    // reads for dK and dV): the unified LDS layout serves both from one copy.
+    typedef Bf16Path<D, kBwdThreads, true> P;
     constexpr int BQ = P::BN;               // query rows per streamed tile
     constexpr int BK = 32 * P::NW;          // keys per workgroup
     constexpr int MB = P::MB, DB = P::DB;
     static_assert(!(DIL && MODE != BWD_BAND), "dilation is not combined with global tokens");
+    // the software-pipelined band loop (below) reads a tile's rows in one
+    // iteration and its transposed operands in the next: three buffer sets
+    constexpr bool PIPE = !(MODE == BWD_GSET || XT || dkdv_waves<D, MODE, XT>() == 2);
 
-    // Q and dO of one query tile, each in both layouts, double-buffered; the
-    // eight buffers are distinct objects and the loop is unrolled by two.
-    __shared__ __attribute__((aligned(1024))) char qk0[P::TILE_BYTES];
-    __shared__ __attribute__((aligned(1024))) char qv0[P::TILE_BYTES];
-    __shared__ __attribute__((aligned(1024))) char ok0[P::TILE_BYTES];
-    __shared__ __attribute__((aligned(1024))) char ov0[P::TILE_BYTES];
-    __shared__ __attribute__((aligned(1024))) char qk1[P::TILE_BYTES];
-    __shared__ __attribute__((aligned(1024))) char qv1[P::TILE_BYTES];
-    __shared__ __attribute__((aligned(1024))) char ok1[P::TILE_BYTES];
-    __shared__ __attribute__((aligned(1024))) char ov1[P::TILE_BYTES];
+    // Q and dO of one query tile, one copy each; two sets (three for the
+    // pipelined loop), distinct objects, the loops unrolled to match.
+    __shared__ __attribute__((aligned(1024))) char qb0[P::TILE_BYTES];
+    __shared__ __attribute__((aligned(1024))) char ob0[P::TILE_BYTES];
+    __shared__ __attribute__((aligned(1024))) char qb1[P::TILE_BYTES];
+    __shared__ __attribute__((aligned(1024))) char ob1[P::TILE_BYTES];
+    __shared__ __attribute__((aligned(1024))) char qb2[PIPE ? P::TILE_BYTES : 16];
+    __shared__ __attribute__((aligned(1024))) char ob2[PIPE ? P::TILE_BYTES : 16];
     __shared__ __attribute__((aligned(16))) float s_lse[2][BQ];   // LSE (natural log; scaled at use)
     __shared__ __attribute__((aligned(16))) float s_dl[2][BQ];    // rowsum(dO * O)
     __shared__ int s_g[kMaxGlobal];                               // sorted global positions
@@ -407,15 +410,13 @@ __global__ void __launch_bounds__(kBwdThreads, (dkdv_waves<D, MODE, XT>())) bwd_
 
     auto head_of = [&](int t) { return b * prm.H + kvh * prm.group + t / nqt; };
     auto tile_of = [&](int t) { return qt_lo + t % nqt; };
-    auto issue = [&](int t, char *qk, char *qv, char *ok, char *ov) __attribute__((always_inline)) {
+    auto issue = [&](int t, char *qb, char *ob) __attribute__((always_inline)) {
         const long long bh = head_of(t);
         const int q0 = tile_of(t) * BQ;
         const uint16_t *qh = static_cast<const uint16_t *>(prm.q) + bh * prm.head_stride + cls_off;
         const uint16_t *gh = static_cast<const uint16_t *>(prm.dout) + bh * prm.head_stride + cls_off;
-        P::issue_k(L, qh, N, qk, q0, dil);
-        P::issue_v(L, qh, N, qv, q0, dil);
-        P::issue_k(L, gh, N, ok, q0, dil);
-        P::issue_v(L, gh, N, ov, q0, dil);
+        P::issue_k(L, qh, N, qb, q0, dil);
+        P::issue_k(L, gh, N, ob, q0, dil);
     };
     // per-row terms of tile t (LSE and rowsum(dO * O)) copied straight into
     // LDS by one wave, like the tiles (rows past the sequence read as 0): a
@@ -437,11 +438,11 @@ __global__ void __launch_bounds__(kBwdThreads, (dkdv_waves<D, MODE, XT>())) bwd_
 
     // the four products of one staged query tile; row(r) gives the sequence
     // row of tile slot r (or -1), vis(i) the extra test of an edge tile
-    auto tile_products = [&](const char *qk, const char *qv, const char *ok, const char *ov, int sb, int cl,
-                             auto row, auto vis) __attribute__((always_inline)) {
+    auto tile_products = [&](const char *qb, const char *ob, int sb, int cl, auto row, auto vis)
+        __attribute__((always_inline)) {
         f32x16 s[MB], dp[MB];
-        P::scores(s, kf, L, qk);    // S  = Q K^T : lane = key, registers = query rows
-        P::scores(dp, vf, L, ok);   // dP = dO V^T
+        P::scores(s, kf, L, qb);    // S  = Q K^T : lane = key, registers = query rows
+        P::scores(dp, vf, L, ob);   // dP = dO V^T
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -460,20 +461,20 @@ __global__ void __launch_bounds__(kBwdThreads, (dkdv_waves<D, MODE, XT>())) bwd_
         typename P::PFrag pp, pd;
         P::pack_p(pp, s);
         P::pack_p(pd, dp);
-        P::pv(dv, pp, L, ov);   // dV^T += dO^T P
-        P::pv(dk, pd, L, qv);   // dK^T += Q^T dS
+        P::pv(dv, pp, L, ob);   // dV^T += dO^T P
+        P::pv(dk, pd, L, qb);   // dK^T += Q^T dS
     };
 
     // The split pass over global columns and the extra-rule instance (whose
     // extra code does not fit beside the pipeline's registers) keep the
     // unpipelined loop.
-    if constexpr (MODE == BWD_GSET || XT || dkdv_waves<D, MODE, XT>() == 2) {
-        auto step = [&](int t, const char *qk, const char *qv, const char *ok, const char *ov, char *nqk, char *nqv,
-                        char *nok, char *nov, int sb) __attribute__((always_inline)) {
+    if constexpr (!PIPE) {
+        auto step = [&](int t, const char *qb, const char *ob, char *nqb, char *nob, int sb)
+            __attribute__((always_inline)) {
             const bool more = t + 1 < T;
             debug_sync();
             if (more) {
-                issue(t + 1, nqk, nqv, nok, nov);
+                issue(t + 1, nqb, nob);
                 issue_terms(t + 1, s_lse[sb ^ 1], s_dl[sb ^ 1]);
             }
             debug_sync();
@@ -482,7 +483,7 @@ __global__ void __launch_bounds__(kBwdThreads, (dkdv_waves<D, MODE, XT>())) bwd_
                 // set S2: rows outside the key's band, not global, causal cut
                 if (wave_active) {
                     const unsigned long long gm = global_rows_in(s_g, ng, q0);
-                    tile_products(qk, qv, ok, ov, sb, TILE_EDGE, [&](int r) { return q0 + r; },
+                    tile_products(qb, ob, sb, TILE_EDGE, [&](int r) { return q0 + r; },
                                   [&](int i) {
                                       return kvalid & (i < N) & ((i < qlo) | (i > qhi)) &
                                              ((prm.causal == 0) | (i >= key)) & !((gm >> (i - q0)) & 1ull);
@@ -493,56 +494,39 @@ __global__ void __launch_bounds__(kBwdThreads, (dkdv_waves<D, MODE, XT>())) bwd_
                 int cl = wave_active ? classify(band, q0, q1, k0w, k1w) : TILE_SKIP;
                 if (cl == TILE_FULL && q0 + BQ - 1 >= N) cl = TILE_EDGE;
                 if (cl != TILE_SKIP)
-                    tile_products(qk, qv, ok, ov, sb, cl, [&](int r) { return q0 + r; },
+                    tile_products(qb, ob, sb, cl, [&](int r) { return q0 + r; },
                                   [&](int i) { return (i >= qlo) & (i <= qhi); });
             }
             wait_vmem();
             __syncthreads();
         };
         if (T > 0) {
-            issue(0, qk0, qv0, ok0, ov0);
+            issue(0, qb0, ob0);
             issue_terms(0, s_lse[0], s_dl[0]);
             wait_vmem();
             __syncthreads();
         }
         for (int t = 0; t < T; t += 2) {
-            step(t, qk0, qv0, ok0, ov0, qk1, qv1, ok1, ov1, 0);
+            step(t, qb0, ob0, qb1, ob1, 0);
             if (t + 1 >= T) break;
-            step(t + 1, qk1, qv1, ok1, ov1, qk0, qv0, ok0, ov0, 1);
+            step(t + 1, qb1, ob1, qb0, ob0, 1);
         }
     } else {
-        // band tiles, software-pipelined (BwdPipe). Row layouts of tile t
-        // (qk, ok) are copied one iteration ahead; its transposed layouts
-        // (qv, ov), read by the dV/dK MFMAs one iteration later, are copied
-        // during iteration t. Both pairs double-buffered.
+        // band tiles, software-pipelined (BwdPipe). Iteration t copies tile
+        // t+1, reads tile t's rows (S, dP) and tile t-1's transposed operands
+        // (dV, dK of tile t-1): three buffer sets in rotation, the loop
+        // unrolled by three so every buffer is a named object.
         typedef BwdPipe<P> BP;
         typename P::PFrag pp, pd;   // P and dS of the previous active tile
         bool act_prev = false;
-        auto issue_rows = [&](int t, char *qk, char *ok) __attribute__((always_inline)) {
-            const long long bh = head_of(t);
-            const int q0 = tile_of(t) * BQ;
-            const uint16_t *qh = static_cast<const uint16_t *>(prm.q) + bh * prm.head_stride + cls_off;
-            const uint16_t *gh = static_cast<const uint16_t *>(prm.dout) + bh * prm.head_stride + cls_off;
-            P::issue_k(L, qh, N, qk, q0, dil);
-            P::issue_k(L, gh, N, ok, q0, dil);
-        };
-        auto issue_tr = [&](int t, char *qv, char *ov) __attribute__((always_inline)) {
-            const long long bh = head_of(t);
-            const int q0 = tile_of(t) * BQ;
-            const uint16_t *qh = static_cast<const uint16_t *>(prm.q) + bh * prm.head_stride + cls_off;
-            const uint16_t *gh = static_cast<const uint16_t *>(prm.dout) + bh * prm.head_stride + cls_off;
-            P::issue_v(L, qh, N, qv, q0, dil);
-            P::issue_v(L, gh, N, ov, q0, dil);
-        };
-        auto pstep = [&](int t, const char *qk, const char *ok, char *nqk, char *nok, char *qv_t, char *ov_t,
-                         const char *qv_p, const char *ov_p, int sb) __attribute__((always_inline)) {
+        auto pstep = [&](int t, const char *qb, const char *ob, char *nqb, char *nob, const char *qb_p,
+                         const char *ob_p, int sb) __attribute__((always_inline)) {
             const bool more = t + 1 < T;
             debug_sync();
             if (more) {
-                issue_rows(t + 1, nqk, nok);
+                issue(t + 1, nqb, nob);
                 issue_terms(t + 1, s_lse[sb ^ 1], s_dl[sb ^ 1]);
             }
-            issue_tr(t, qv_t, ov_t);
             debug_sync();
             const int q0 = tile_of(t) * BQ;
             const int q1 = imin(N - 1, q0 + BQ - 1);
@@ -555,27 +539,27 @@ __global__ void __launch_bounds__(kBwdThreads, (dkdv_waves<D, MODE, XT>())) bwd_
             // for both chains at once run out
             if (act) {
                 if constexpr (MODE == BWD_BAND_GL) {
-                    P::scores(s, kf, L, qk);
-                    P::scores(dp, vf, L, ok);
+                    P::scores(s, kf, L, qb);
+                    P::scores(dp, vf, L, ob);
                 } else {
-                    ScorePair<P>::scores(s, dp, kf, vf, L, qk, ok);
+                    ScorePair<P>::scores(s, dp, kf, vf, L, qb, ob);
                 }
             }
             const float *lr = s_lse[sb], *dr = s_dl[sb];
             if (act_prev) {
                 if (act) {
                     if (cl == TILE_EDGE)
-                        BP::template region<true, true, true>(dv, dk, pp, pd, s, dp, L, ov_p, qv_p, lr, dr, c, h, q0, qlo, qhi);
+                        BP::template region<true, true, true>(dv, dk, pp, pd, s, dp, L, ob_p, qb_p, lr, dr, c, h, q0, qlo, qhi);
                     else
-                        BP::template region<true, true, false>(dv, dk, pp, pd, s, dp, L, ov_p, qv_p, lr, dr, c, h, q0, qlo, qhi);
+                        BP::template region<true, true, false>(dv, dk, pp, pd, s, dp, L, ob_p, qb_p, lr, dr, c, h, q0, qlo, qhi);
                 } else {
-                    BP::template region<true, false, false>(dv, dk, pp, pd, s, dp, L, ov_p, qv_p, lr, dr, c, h, q0, qlo, qhi);
+                    BP::template region<true, false, false>(dv, dk, pp, pd, s, dp, L, ob_p, qb_p, lr, dr, c, h, q0, qlo, qhi);
                 }
             } else if (act) {
                 if (cl == TILE_EDGE)
-                    BP::template region<false, true, true>(dv, dk, pp, pd, s, dp, L, ov_p, qv_p, lr, dr, c, h, q0, qlo, qhi);
+                    BP::template region<false, true, true>(dv, dk, pp, pd, s, dp, L, ob_p, qb_p, lr, dr, c, h, q0, qlo, qhi);
                 else
-                    BP::template region<false, true, false>(dv, dk, pp, pd, s, dp, L, ov_p, qv_p, lr, dr, c, h, q0, qlo, qhi);
+                    BP::template region<false, true, false>(dv, dk, pp, pd, s, dp, L, ob_p, qb_p, lr, dr, c, h, q0, qlo, qhi);
             }
             if (act) {
                 P::pack_p(pp, s);
@@ -586,24 +570,30 @@ __global__ void __launch_bounds__(kBwdThreads, (dkdv_waves<D, MODE, XT>())) bwd_
             __syncthreads();
         };
         if (T > 0) {
-            issue_rows(0, qk0, ok0);
+            issue(0, qb0, ob0);
             issue_terms(0, s_lse[0], s_dl[0]);
             wait_vmem();
             __syncthreads();
         }
-        for (int t = 0; t < T; t += 2) {
-            pstep(t, qk0, ok0, qk1, ok1, qv0, ov0, qv1, ov1, 0);
+        // tile x sits in set x % 3; its row terms in slot x & 1
+        for (int t = 0; t < T; t += 3) {
+            pstep(t, qb0, ob0, qb1, ob1, qb2, ob2, t & 1);
             if (t + 1 >= T) break;
-            pstep(t + 1, qk1, ok1, qk0, ok0, qv1, ov1, qv0, ov0, 1);
+            pstep(t + 1, qb1, ob1, qb2, ob2, qb0, ob0, (t + 1) & 1);
+            if (t + 2 >= T) break;
+            pstep(t + 2, qb2, ob2, qb0, ob0, qb1, ob1, t & 1);
         }
-        // the last active tile's dV/dK products (its transposed layouts were
-        // copied during the last iteration)
+        // the last active tile's dV/dK products (its operands are still in
+        // the set of tile T-1)
         if (act_prev) {
             f32x16 s[MB], dp[MB];
-            if ((T - 1) & 1)
-                BP::template region<true, false, false>(dv, dk, pp, pd, s, dp, L, ov1, qv1, s_lse[0], s_dl[0], c, h, 0, 0, 0);
+            const int r = (T - 1) % 3;
+            if (r == 0)
+                BP::template region<true, false, false>(dv, dk, pp, pd, s, dp, L, ob0, qb0, s_lse[0], s_dl[0], c, h, 0, 0, 0);
+            else if (r == 1)
+                BP::template region<true, false, false>(dv, dk, pp, pd, s, dp, L, ob1, qb1, s_lse[0], s_dl[0], c, h, 0, 0, 0);
             else
-                BP::template region<true, false, false>(dv, dk, pp, pd, s, dp, L, ov0, qv0, s_lse[0], s_dl[0], c, h, 0, 0, 0);
+                BP::template region<true, false, false>(dv, dk, pp, pd, s, dp, L, ob2, qb2, s_lse[0], s_dl[0], c, h, 0, 0, 0);
         }
         __syncthreads();   // every wave is done with the tile buffers
     }
@@ -616,9 +606,8 @@ __global__ void __launch_bounds__(kBwdThreads, (dkdv_waves<D, MODE, XT>())) bwd_
             const uint16_t *qh = static_cast<const uint16_t *>(prm.q) + bh * prm.head_stride;
             const uint16_t *gh = static_cast<const uint16_t *>(prm.dout) + bh * prm.head_stride;
             const TileSrc src{0, 1, N, ng, s_g};
-            typename P::Stage st;
-            P::issue(st, L, qh, qh, qk0, qv0, src, s_g[0]);
-            P::issue(st, L, gh, gh, ok0, ov0, src, s_g[0]);
+            P::issue_one(L, qh, qb0, src, s_g[0]);
+            P::issue_one(L, gh, ob0, src, s_g[0]);
             if (tid < BQ) {
                 const bool gv = tid < ng;
                 s_lse[0][tid] = gv ? prm.lse[bh * N + s_g[tid]] : 0.f;
@@ -627,7 +616,7 @@ __global__ void __launch_bounds__(kBwdThreads, (dkdv_waves<D, MODE, XT>())) bwd_
             wait_vmem();
             __syncthreads();
             if (wave_active)
-                tile_products(qk0, qv0, ok0, ov0, 0, TILE_EDGE, [&](int r) { return r < ng ? s_g[r] : -1; },
+                tile_products(qb0, ob0, 0, TILE_EDGE, [&](int r) { return r < ng ? s_g[r] : -1; },
                               [&](int i) {   // row i's band holds the key iff qlo <= i <= qhi
                                   return kvalid & (i >= 0) & ((prm.causal == 0) | (key <= i)) &
                                          ((i < qlo) | (i > qhi));
@@ -647,10 +636,8 @@ __global__ void __launch_bounds__(kBwdThreads, (dkdv_waves<D, MODE, XT>())) bwd_
                 const long long bh = (long long)b * prm.H + kvh * prm.group + hq;
                 const uint16_t *qh = static_cast<const uint16_t *>(prm.q) + bh * prm.head_stride;
                 const uint16_t *gh = static_cast<const uint16_t *>(prm.dout) + bh * prm.head_stride;
-                P::issue_k(L, qh, N, qk0, q0);
-                P::issue_v(L, qh, N, qv0, q0);
-                P::issue_k(L, gh, N, ok0, q0);
-                P::issue_v(L, gh, N, ov0, q0);
+                P::issue_k(L, qh, N, qb0, q0);
+                P::issue_k(L, gh, N, ob0, q0);
                 if (tid < BQ) {
                     const int i = q0 + tid;
                     s_lse[0][tid] = i < N ? prm.lse[bh * N + i] : 0.f;
@@ -660,7 +647,7 @@ __global__ void __launch_bounds__(kBwdThreads, (dkdv_waves<D, MODE, XT>())) bwd_
                 __syncthreads();
                 if (wave_active) {
                     const unsigned long long gm = global_rows_in(s_g, ng, q0);
-                    tile_products(qk0, qv0, ok0, ov0, 0, TILE_EDGE, [&](int r) { return q0 + r; }, [&](int i) {
+                    tile_products(qb0, ob0, 0, TILE_EDGE, [&](int r) { return q0 + r; }, [&](int i) {
                         return kvalid & !key_is_g & (i < N) & ((i < qlo) | (i > qhi)) &
                                ((prm.causal == 0) | (i >= key)) & !((gm >> (i - q0)) & 1ull) && vis(i);
                     });

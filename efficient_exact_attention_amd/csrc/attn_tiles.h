@@ -75,9 +75,12 @@ struct TileSrc {
 // bf16 inputs: QK^T and PV on v_mfma_f32_32x32x16_bf16; tiles loaded
 // global -> LDS directly, V operands through the LDS transpose read.
 // ---------------------------------------------------------------------------
-template <int D_, int NT_>
+// UNI_: one LDS layout per tile for both operand patterns (row reads and
+// transpose reads), so a tile that is read both ways is copied once (see ux).
+template <int D_, int NT_, bool UNI_ = false>
 struct Bf16Path {
     static constexpr int D = D_, BN = 64, NT = NT_, NW = NT / 64;
+    static constexpr bool UNI = UNI_;
     static constexpr bool F32 = false;
     static constexpr int KS = D / 16;     // k-steps of QK^T
     static constexpr int MB = BN / 32;    // 32-key blocks per tile
@@ -110,11 +113,23 @@ struct Bf16Path {
     static __device__ __forceinline__ int vx(int r) {
         return D == 128 ? ((r & 3) << 2) : (((r >> 1) & 1) << 2);
     }
+    // One layout for both patterns: ux gives 16 distinct chunk slots to the
+    // 16 rows of a row-read pass (d = 128: its low two bits take r >> 2, its
+    // high two bits r & 3; d = 64: 8 distinct slots to each row parity) and
+    // sends the 4 rows of a transpose-read pass to 4 distinct 64-byte
+    // quarters (its bit 2, and at d = 128 bit 3, follow the row within its
+    // aligned quad). Rows 8 apart differ by ux ^ 2 (r >> 2 moves by 2).
+    static __device__ __forceinline__ int ux(int r) {
+        return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+    }
+    static __device__ __forceinline__ int kxs(int r) { return UNI ? ux(r) : kx(r); }
+    static __device__ __forceinline__ int vxs(int r) { return UNI ? ux(r) : vx(r); }
 
     // Per-lane constants, computed once.
     struct Lane {
         int krd[KS];       // K operand: byte offset in a K tile for (mb=0, ks)
         int vrd[DB];       // V operand: byte offset in a V tile for (st=0, db)
+        int vrdh[UNI ? DB : 1];   // UNI: the same for the second read, 8 key rows on
         int ldrow[SPW];    // tile row this lane fetches in load i
         int ldkcol[SPW];   // element offset of its K chunk within that row
         int ldvcol[SPW];   // element offset of its V chunk within that row
@@ -129,7 +144,7 @@ struct Bf16Path {
         const int ln = lane & 31, h = lane >> 5;
         // K row ln, logical chunk 2ks + h
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) L.krd[ks] = ln * ROWB + 16 * ((2 * ks + h) ^ kx(ln));
+        for (int ks = 0; ks < KS; ++ks) L.krd[ks] = ln * ROWB + 16 * ((2 * ks + h) ^ kxs(ln));
         // transpose read: lane j of 16-lane group g loads 4 elements of key
         // row 4h + j/4 at d = 32db + 16(g&1) + 4(j&3); lane i of the group then
         // holds d = 32db + 16(g&1) + i for the keys 4h + e, e = 0..3
@@ -137,14 +152,19 @@ struct Bf16Path {
         const int krow = 4 * h + (j >> 2);
         const int t = 2 * (g & 1) + ((j >> 1) & 1);
 #pragma unroll
-        for (int db = 0; db < DB; ++db) L.vrd[db] = krow * ROWB + 16 * ((4 * db + t) ^ vx(krow)) + 8 * (j & 1);
+        for (int db = 0; db < DB; ++db) L.vrd[db] = krow * ROWB + 16 * ((4 * db + t) ^ vxs(krow)) + 8 * (j & 1);
+        if constexpr (UNI) {
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+                L.vrdh[db] = (krow + 8) * ROWB + 16 * ((4 * db + t) ^ ux(krow + 8)) + 8 * (j & 1);
+        }
 #pragma unroll
         for (int i = 0; i < SPW; ++i) {
             const int o = (wave * SPW + i) * 1024 + lane * 16;
             const int row = o / ROWB, phys = (o % ROWB) / 16;
             L.ldrow[i] = row;
-            L.ldkcol[i] = (phys ^ kx(row)) * 8;
-            L.ldvcol[i] = (phys ^ vx(row)) * 8;
+            L.ldkcol[i] = (phys ^ kxs(row)) * 8;
+            L.ldvcol[i] = (phys ^ vxs(row)) * 8;
             L.ldlds[i] = (wave * SPW + i) * 1024;
             L.ldk[i] = row * dil * ROWB + 2 * L.ldkcol[i];
             L.ldv[i] = row * dil * ROWB + 2 * L.ldvcol[i];
@@ -186,6 +206,19 @@ struct Bf16Path {
                                                      off + 2 * L.ldvcol[i], 0, 0, 0);
         }
     }
+    // UNI: the one copy of a gathered tile that serves both read patterns.
+    static __device__ __forceinline__ void issue_one(const Lane &L, const elem_t *h, char *buf, const TileSrc &src,
+                                                     int fallback) {
+        static_assert(UNI, "one copy serves both patterns only in the unified layout");
+        const __amdgpu_buffer_rsrc_t r = head_rsrc(h, src.N);
+#pragma unroll
+        for (int i = 0; i < SPW; ++i) {
+            int key = src.key(L.ldrow[i]);
+            key = key < 0 ? fallback : key;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (EEA_LDS void *)(buf + L.ldlds[i]), 16,
+                                                     (unsigned)key * ROWB + 2 * L.ldkcol[i], 0, 0, 0);
+        }
+    }
 
     // Band tiles: the copy of the K (or V) tile whose first key is k0. Rows
     // past the end of the sequence lie past the buffer's last record, so the
@@ -194,15 +227,16 @@ struct Bf16Path {
     // (k0 + r) * dil of the tensor at kh, and N counts the rows of that
     // strided sequence; rows past it still read as zeros.
     // At d = 64 a wave's loads are 8 tile rows apart, and kx(r + 8) =
-    // kx(r) ^ 4 while vx(r + 8) = vx(r): load i's offsets follow from load
-    // 0's (the row part is a multiple of ROWB, the chunk part below it), so
-    // only load 0's stay live.
+    // kx(r) ^ 4 while vx(r + 8) = vx(r) (ux(r + 8) = ux(r) ^ 2): load i's
+    // offsets follow from load 0's (the row part is a multiple of ROWB, the
+    // chunk part below it), so only load 0's stay live.
     static __device__ __forceinline__ int k_off(const Lane &L, int i, int dil) {
-        if constexpr (D == 64) return ((L.ldk[0] ^ (64 * (i & 1))) + 8 * i * dil * ROWB);
+        if constexpr (D == 64) return ((L.ldk[0] ^ ((UNI ? 32 : 64) * (i & 1))) + 8 * i * dil * ROWB);
         else return L.ldk[i];
     }
     static __device__ __forceinline__ int v_off(const Lane &L, int i, int dil) {
-        if constexpr (D == 64) return L.ldv[0] + 8 * i * dil * ROWB;
+        if constexpr (D == 64 && UNI) return k_off(L, i, dil);
+        else if constexpr (D == 64) return L.ldv[0] + 8 * i * dil * ROWB;
         else return L.ldv[i];
     }
     static __device__ __forceinline__ void issue_k(const Lane &L, const elem_t *kh, int N, char *kbuf, int k0,
@@ -289,8 +323,9 @@ struct Bf16Path {
 
     static __device__ __forceinline__ bf16x8 v_operand(const Lane &L, const char *vbuf, int db, int st) {
         const char *p = vbuf + L.vrd[db] + 16 * st * ROWB;
+        const char *q = UNI ? vbuf + L.vrdh[db] + 16 * st * ROWB : p + 8 * ROWB;
         s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((EEA_LDS s16x4 *)(p));
-        s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((EEA_LDS s16x4 *)(p + 8 * ROWB));
+        s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((EEA_LDS s16x4 *)(q));
         s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         return __builtin_bit_cast(bf16x8, v);
     }
