@@ -837,18 +837,25 @@ struct DqPipe {
 // log-spaced strided or the random-block rule, as extra key tiles.
 template <int D, bool DIL, int MODE, bool XT = false>
 __global__ void __launch_bounds__((dq_threads<D, MODE, XT>()), dq_waves<D>()) bwd_dq(const BwdParams prm) {
-    typedef Bf16Path<D, dq_threads<D, MODE, XT>()> P;
+    // K tiles are read both ways (row reads for S^T, transpose reads for
+    // dQ): the unified LDS layout serves both from one copy.
+    typedef Bf16Path<D, dq_threads<D, MODE, XT>(), true> P;
     constexpr int BN = P::BN;                 // keys per streamed tile
     constexpr int BM = 32 * P::NW;            // query rows per workgroup
     constexpr int MB = P::MB, DB = P::DB;
     static_assert(!(DIL && MODE != BWD_BAND), "dilation is not combined with global tokens");
+    // the software-pipelined band loop (below) reads a K tile's rows in one
+    // iteration and its transposed operands in the next: three buffer sets
+    constexpr bool PIPE = !(MODE == BWD_GSET || XT || dq_threads<D, MODE, XT>() == 512);
 
-    __shared__ __attribute__((aligned(1024))) char kk0[P::TILE_BYTES];   // K, row-read layout
-    __shared__ __attribute__((aligned(1024))) char kv0[P::TILE_BYTES];   // K, transpose-read layout
-    __shared__ __attribute__((aligned(1024))) char vk0[P::TILE_BYTES];   // V, row-read layout
-    __shared__ __attribute__((aligned(1024))) char kk1[P::TILE_BYTES];
-    __shared__ __attribute__((aligned(1024))) char kv1[P::TILE_BYTES];
-    __shared__ __attribute__((aligned(1024))) char vk1[P::TILE_BYTES];
+    // K and V of one key tile, one copy each; two sets (three for the
+    // pipelined loop), distinct objects, the loops unrolled to match
+    __shared__ __attribute__((aligned(1024))) char kb0[P::TILE_BYTES];
+    __shared__ __attribute__((aligned(1024))) char vb0[P::TILE_BYTES];
+    __shared__ __attribute__((aligned(1024))) char kb1[P::TILE_BYTES];
+    __shared__ __attribute__((aligned(1024))) char vb1[P::TILE_BYTES];
+    __shared__ __attribute__((aligned(1024))) char kb2[PIPE ? P::TILE_BYTES : 16];
+    __shared__ __attribute__((aligned(1024))) char vb2[PIPE ? P::TILE_BYTES : 16];
     __shared__ int s_g[kMaxGlobal];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -926,11 +933,11 @@ __global__ void __launch_bounds__((dq_threads<D, MODE, XT>()), dq_waves<D>()) bw
 
     // dS^T of one staged key tile into dQ^T; col(r) gives the key of tile
     // slot r (or -1), vis(j) the extra test of an edge tile
-    auto tile_products = [&](const char *kk, const char *kv, const char *vk, int cl, auto col, auto vis)
+    auto tile_products = [&](const char *kb, const char *vb, int cl, auto col, auto vis)
         __attribute__((always_inline)) {
         f32x16 s[MB], dp[MB];
-        P::scores(s, qf, L, kk);    // S^T  = K Q^T  : lane = query row, registers = keys
-        P::scores(dp, gf, L, vk);   // dP^T = V dO^T
+        P::scores(s, qf, L, kb);    // S^T  = K Q^T  : lane = query row, registers = keys
+        P::scores(dp, gf, L, vb);   // dP^T = V dO^T
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -941,98 +948,97 @@ __global__ void __launch_bounds__((dq_threads<D, MODE, XT>()), dq_waves<D>()) bw
             }
         typename P::PFrag pd;
         P::pack_p(pd, dp);
-        P::pv(dq, pd, L, kv);       // dQ^T += K^T dS^T
+        P::pv(dq, pd, L, kb);       // dQ^T += K^T dS^T
     };
 
-    auto issue = [&](int kt, char *kk, char *kv, char *vk) __attribute__((always_inline)) {
-        P::issue_k(L, kh, N, kk, kt * BN, dil);
-        P::issue_v(L, kh, N, kv, kt * BN, dil);
-        P::issue_k(L, vh, N, vk, kt * BN, dil);
+    auto issue = [&](int kt, char *kb, char *vb) __attribute__((always_inline)) {
+        P::issue_k(L, kh, N, kb, kt * BN, dil);
+        P::issue_k(L, vh, N, vb, kt * BN, dil);
     };
-    auto step = [&](int kt, const char *kk, const char *kv, const char *vk, char *nkk, char *nkv, char *nvk)
-        __attribute__((always_inline)) {
+    auto step = [&](int kt, const char *kb, const char *vb, char *nkb, char *nvb) __attribute__((always_inline)) {
         debug_sync();
-        if (kt < kt_hi) issue(kt + 1, nkk, nkv, nvk);
+        if (kt < kt_hi) issue(kt + 1, nkb, nvb);
         debug_sync();
         const int k0 = kt * BN;
         if constexpr (MODE == BWD_GSET) {
             // set S3: keys outside the global row's band, causal cut
             if (wave_active)
-                tile_products(kk, kv, vk, TILE_EDGE, [&](int r) { return k0 + r; }, [&](int j) {
+                tile_products(kb, vb, TILE_EDGE, [&](int r) { return k0 + r; }, [&](int j) {
                     return valid & (j < N) & ((j < lo) | (j > hi)) & ((prm.causal == 0) | (j <= row));
                 });
         } else {
             const int cl = wave_active ? classify(band, wr0, wr1, k0, k0 + BN - 1) : TILE_SKIP;
             if (cl != TILE_SKIP)
-                tile_products(kk, kv, vk, cl, [&](int r) { return k0 + r; },
+                tile_products(kb, vb, cl, [&](int r) { return k0 + r; },
                               [&](int j) { return (j >= lo) & (j <= hi); });
         }
         wait_vmem();
         __syncthreads();
     };
 
-    if constexpr (MODE == BWD_GSET || XT || dq_threads<D, MODE, XT>() == 512) {
+    if constexpr (!PIPE) {
         if (kt_lo <= kt_hi) {
-            issue(kt_lo, kk0, kv0, vk0);
+            issue(kt_lo, kb0, vb0);
             wait_vmem();
             __syncthreads();
             for (int kt = kt_lo; kt <= kt_hi; kt += 2) {
-                step(kt, kk0, kv0, vk0, kk1, kv1, vk1);
+                step(kt, kb0, vb0, kb1, vb1);
                 if (kt + 1 > kt_hi) break;
-                step(kt + 1, kk1, kv1, vk1, kk0, kv0, vk0);
+                step(kt + 1, kb1, vb1, kb0, vb0);
             }
         }
     } else if (kt_lo <= kt_hi) {
-        // band tiles, software-pipelined (DqPipe): the row layouts of K and V
-        // for tile t are copied one iteration ahead, the transposed layout of
-        // K (read by the dQ MFMAs one iteration later) during iteration t
+        // band tiles, software-pipelined (DqPipe). Iteration t copies tile
+        // t+1, reads tile t's K and V rows (S^T, dP^T) and tile t-1's K
+        // transposed (dQ of tile t-1): three buffer sets in rotation, the
+        // loop unrolled by three so every buffer is a named object.
         typedef DqPipe<P> QP;
         typename P::PFrag pd;   // dS of the previous active tile
         bool act_prev = false;
-        auto issue_rows = [&](int kt, char *kk, char *vk) __attribute__((always_inline)) {
-            P::issue_k(L, kh, N, kk, kt * BN, dil);
-            P::issue_k(L, vh, N, vk, kt * BN, dil);
-        };
-        auto pstep = [&](int kt, const char *kk, const char *vk, char *nkk, char *nvk, char *kv_t, const char *kv_p)
+        auto pstep = [&](int kt, const char *kb, const char *vb, char *nkb, char *nvb, const char *kb_p)
             __attribute__((always_inline)) {
             debug_sync();
-            if (kt < kt_hi) issue_rows(kt + 1, nkk, nvk);
-            P::issue_v(L, kh, N, kv_t, kt * BN, dil);
+            if (kt < kt_hi) issue(kt + 1, nkb, nvb);
             debug_sync();
             const int k0 = kt * BN;
             const int cl = wave_active ? classify(band, wr0, wr1, k0, k0 + BN - 1) : TILE_SKIP;
             const bool act = cl != TILE_SKIP;
             f32x16 s[MB], dp[MB];
             // S^T = K Q^T and dP^T = V dO^T (lane = query row, registers = keys)
-            if (act) ScorePair<P>::scores(s, dp, qf, gf, L, kk, vk);
+            if (act) ScorePair<P>::scores(s, dp, qf, gf, L, kb, vb);
             if (act_prev) {
                 if (act) {
-                    if (cl == TILE_EDGE) QP::template region<true, true, true>(dq, pd, s, dp, L, kv_p, c, l2, dl, h, k0, lo, hi);
-                    else QP::template region<true, true, false>(dq, pd, s, dp, L, kv_p, c, l2, dl, h, k0, lo, hi);
+                    if (cl == TILE_EDGE) QP::template region<true, true, true>(dq, pd, s, dp, L, kb_p, c, l2, dl, h, k0, lo, hi);
+                    else QP::template region<true, true, false>(dq, pd, s, dp, L, kb_p, c, l2, dl, h, k0, lo, hi);
                 } else {
-                    QP::template region<true, false, false>(dq, pd, s, dp, L, kv_p, c, l2, dl, h, k0, lo, hi);
+                    QP::template region<true, false, false>(dq, pd, s, dp, L, kb_p, c, l2, dl, h, k0, lo, hi);
                 }
             } else if (act) {
-                if (cl == TILE_EDGE) QP::template region<false, true, true>(dq, pd, s, dp, L, kv_p, c, l2, dl, h, k0, lo, hi);
-                else QP::template region<false, true, false>(dq, pd, s, dp, L, kv_p, c, l2, dl, h, k0, lo, hi);
+                if (cl == TILE_EDGE) QP::template region<false, true, true>(dq, pd, s, dp, L, kb_p, c, l2, dl, h, k0, lo, hi);
+                else QP::template region<false, true, false>(dq, pd, s, dp, L, kb_p, c, l2, dl, h, k0, lo, hi);
             }
             if (act) P::pack_p(pd, dp);
             act_prev = act;
             wait_vmem();
             __syncthreads();
         };
-        issue_rows(kt_lo, kk0, vk0);
+        issue(kt_lo, kb0, vb0);
         wait_vmem();
         __syncthreads();
-        for (int kt = kt_lo; kt <= kt_hi; kt += 2) {
-            pstep(kt, kk0, vk0, kk1, vk1, kv0, kv1);
+        // tile kt_lo + x sits in set x % 3
+        for (int kt = kt_lo; kt <= kt_hi; kt += 3) {
+            pstep(kt, kb0, vb0, kb1, vb1, kb2);
             if (kt + 1 > kt_hi) break;
-            pstep(kt + 1, kk1, vk1, kk0, vk0, kv1, kv0);
+            pstep(kt + 1, kb1, vb1, kb2, vb2, kb0);
+            if (kt + 2 > kt_hi) break;
+            pstep(kt + 2, kb2, vb2, kb0, vb0, kb1);
         }
         if (act_prev) {   // the last active tile's dQ products
             f32x16 s[MB], dp[MB];
-            if ((kt_hi - kt_lo) & 1) QP::template region<true, false, false>(dq, pd, s, dp, L, kv1, c, l2, dl, h, 0, 0, 0);
-            else QP::template region<true, false, false>(dq, pd, s, dp, L, kv0, c, l2, dl, h, 0, 0, 0);
+            const int r = (kt_hi - kt_lo) % 3;
+            if (r == 0) QP::template region<true, false, false>(dq, pd, s, dp, L, kb0, c, l2, dl, h, 0, 0, 0);
+            else if (r == 1) QP::template region<true, false, false>(dq, pd, s, dp, L, kb1, c, l2, dl, h, 0, 0, 0);
+            else QP::template region<true, false, false>(dq, pd, s, dp, L, kb2, c, l2, dl, h, 0, 0, 0);
         }
         __syncthreads();   // every wave is done with the tile buffers
     }
@@ -1044,13 +1050,12 @@ __global__ void __launch_bounds__((dq_threads<D, MODE, XT>()), dq_waves<D>()) bw
         // set S2: the gathered tile of the global columns; a global column
         // counts here for non-global rows outside whose band it lies
         const TileSrc src{0, 1, N, ng, s_g};
-        typename P::Stage st;
-        P::issue(st, L, kh, kh, kk0, kv0, src, s_g[0]);
-        P::issue(st, L, vh, vh, vk0, kv1, src, s_g[0]);
+        P::issue_one(L, kh, kb0, src, s_g[0]);
+        P::issue_one(L, vh, vb0, src, s_g[0]);
         wait_vmem();
         __syncthreads();
         if (wave_active)
-            tile_products(kk0, kv0, vk0, TILE_EDGE, [&](int r) { return r < ng ? s_g[r] : -1; }, [&](int j) {
+            tile_products(kb0, vb0, TILE_EDGE, [&](int r) { return r < ng ? s_g[r] : -1; }, [&](int j) {
                 return valid & !row_is_g & (j >= 0) & ((prm.causal == 0) | (j <= row)) & ((j < lo) | (j > hi));
             });
         __syncthreads();
@@ -1062,14 +1067,13 @@ __global__ void __launch_bounds__((dq_threads<D, MODE, XT>()), dq_waves<D>()) bw
         // and columns and within the causal limit
         const int q1 = imin(N - 1, q0 + BM - 1);
         auto extra_ktile = [&](int k0, bool take, auto vis) __attribute__((always_inline)) {
-            P::issue_k(L, kh, N, kk0, k0);
-            P::issue_v(L, kh, N, kv0, k0);
-            P::issue_k(L, vh, N, vk0, k0);
+            P::issue_k(L, kh, N, kb0, k0);
+            P::issue_k(L, vh, N, vb0, k0);
             wait_vmem();
             __syncthreads();
             if (take) {
                 const unsigned long long gm = global_rows_in(s_g, ng, k0);   // global columns of the tile
-                tile_products(kk0, kv0, vk0, TILE_EDGE, [&](int r) { return k0 + r; }, [&](int j) {
+                tile_products(kb0, vb0, TILE_EDGE, [&](int r) { return k0 + r; }, [&](int j) {
                     return valid & !row_is_g & (j < N) & ((j < lo) | (j > hi)) & ((prm.causal == 0) | (j <= row)) &
                            !((gm >> (j - k0)) & 1ull) && vis(j);
                 });
