@@ -21,8 +21,9 @@
 //    walks the visible 64-key tiles, accumulating dQ^T += K^T dS^T.
 // All products use v_mfma_f32_32x32x16_bf16 in the transposed forms of the
 // forward pass, so each of them is one of the bf16 tile path's two operand
-// patterns (row reads with the K swizzle, transpose reads with the V
-// swizzle); a tile needed in both forms is copied into LDS in both layouts.
+// patterns (row reads, transpose reads); the tiles read both ways (Q and dO
+// in dK/dV, K in dQ) are copied into LDS once, in the tile path's unified
+// layout, which serves both patterns without bank conflicts.
 // Band masks (causal, windows, block-sparse), dilated masks (one band per
 // residue class of rows) and global tokens (below) are handled.
 #include <hip/hip_runtime.h>
