@@ -104,13 +104,15 @@ struct Bf16Path {
     // ds_read_b128 serves 16 lanes per pass and the 16 lanes of a pass read
     // the same logical chunk of 16 consecutive rows, so kx must map those
     // rows onto 16 distinct 16-byte slots of the 256-byte bank window.
-    static __device__ __forceinline__ int kx(int r) {
+    // (the swizzles and the per-lane offsets are host-callable too, so a CPU
+    // test can replay the copies and reads of a tile)
+    static __host__ __device__ __forceinline__ int kx(int r) {
         return D == 128 ? (r & 15) : ((r >> 1) & 7);   // d=64: two rows per window
     }
     // V rows: the transpose read of a half-wave touches 4 consecutive key
     // rows over one 64-byte d-block, so vx moves those 4 rows onto the 4
     // distinct 64-byte quarters of the bank window.
-    static __device__ __forceinline__ int vx(int r) {
+    static __host__ __device__ __forceinline__ int vx(int r) {
         return D == 128 ? ((r & 3) << 2) : (((r >> 1) & 1) << 2);
     }
     // One layout for both patterns: ux gives 16 distinct chunk slots to the
@@ -119,11 +121,11 @@ struct Bf16Path {
     // sends the 4 rows of a transpose-read pass to 4 distinct 64-byte
     // quarters (its bit 2, and at d = 128 bit 3, follow the row within its
     // aligned quad). Rows 8 apart differ by ux ^ 2 (r >> 2 moves by 2).
-    static __device__ __forceinline__ int ux(int r) {
+    static __host__ __device__ __forceinline__ int ux(int r) {
         return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
     }
-    static __device__ __forceinline__ int kxs(int r) { return UNI ? ux(r) : kx(r); }
-    static __device__ __forceinline__ int vxs(int r) { return UNI ? ux(r) : vx(r); }
+    static __host__ __device__ __forceinline__ int kxs(int r) { return UNI ? ux(r) : kx(r); }
+    static __host__ __device__ __forceinline__ int vxs(int r) { return UNI ? ux(r) : vx(r); }
 
     // Per-lane constants, computed once.
     struct Lane {
@@ -140,7 +142,7 @@ struct Bf16Path {
 
     // dil: distance in rows of the stored tensor between consecutive tile
     // rows (1 for contiguous rows; k for one residue class of a dilated mask).
-    static __device__ __forceinline__ void init_lane(Lane &L, int lane, int wave, int dil = 1) {
+    static __host__ __device__ __forceinline__ void init_lane(Lane &L, int lane, int wave, int dil = 1) {
         const int ln = lane & 31, h = lane >> 5;
         // K row ln, logical chunk 2ks + h
 #pragma unroll
