@@ -518,18 +518,19 @@ int fwd_impl(const void *q, const void *k, const void *v, void *out, float *lse,
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Backward workspace: the row terms rowsum(dO * O) [B*H][N], then, with
-// global tokens, the split passes' partials (dQ of the global rows per key
-// chunk, dK and dV of the global columns per row chunk).
+// Backward workspace: the row terms rowsum(dO * O) and LSE * log2(e), each
+// [B*H][N], then, with global tokens, the split passes' partials (dQ of the
+// global rows per key chunk, dK and dV of the global columns per row chunk).
 struct BwdLayout {
-    size_t delta = 0, part_q = 0, part_k = 0, total = 0;
+    size_t delta = 0, lse2 = 0, part_q = 0, part_k = 0, total = 0;
     int gchunks_q = 0, gct_q = 0, gchunks_k = 0, gct_k = 0;
 };
 
 BwdLayout bwd_layout(long long BH, long long BKV, int N, int d, int ng) {
     BwdLayout w;
     w.delta = 0;
-    w.total = align256((size_t)BH * N * sizeof(float));
+    w.lse2 = align256((size_t)BH * N * sizeof(float));
+    w.total = 2 * w.lse2;
     if (ng > 0) {
         eea::bwd_global_chunks((int)BH, N, &w.gchunks_q, &w.gct_q);
         eea::bwd_global_chunks((int)BKV, N, &w.gchunks_k, &w.gct_k);
@@ -652,6 +653,7 @@ int bwd_impl(const void *q, const void *k, const void *v, const void *out, const
     hipStream_t stream = opts ? static_cast<hipStream_t>(opts->stream) : nullptr;
     return run_on_device(SCR_BWD, need, ws, stream, [&](void *buf) {
         p.delta = static_cast<float *>(buf);
+        p.lse2 = reinterpret_cast<float *>(static_cast<char *>(buf) + lay.lse2);
         if (m.ng > 0) {
             p.part_q = reinterpret_cast<float *>(static_cast<char *>(buf) + lay.part_q);
             p.part_k = reinterpret_cast<float *>(static_cast<char *>(buf) + lay.part_k);

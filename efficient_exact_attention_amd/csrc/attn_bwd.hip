@@ -39,7 +39,9 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
-// rowsum(dO * O) per query row: 8 lanes per row, 32 rows per workgroup.
+// Row terms per query row: rowsum(dO * O), and LSE * log2(e) (so the
+// score loops form P = exp2(S c - LSE log2 e) with one FMA per element);
+// 8 lanes per row, 32 rows per workgroup.
 template <int D>
 __global__ void __launch_bounds__(kBwdThreads) bwd_delta(const BwdParams prm) {
     constexpr int PER = D / 8;   // elements per lane
@@ -64,7 +66,10 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_delta(const BwdParams prm) {
     acc += __shfl_xor(acc, 1);
     acc += __shfl_xor(acc, 2);
     acc += __shfl_xor(acc, 4);
-    if (sub == 0 && r < rows) prm.delta[r] = acc;
+    if (sub == 0 && r < rows) {
+        prm.delta[r] = acc;
+        prm.lse2[r] = prm.lse[r] * kLog2e;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -243,7 +248,7 @@ struct BwdPipe {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int r = 4 * g + e;
-                        float p = fast_exp2(__builtin_fmaf(s[mb][r], c, -(l4[j][e] * kLog2e)));
+                        float p = fast_exp2(__builtin_fmaf(s[mb][r], c, -l4[j][e]));
                         if constexpr (EDGE) {
                             const int i = q0 + 32 * mb + acc_row(r, h);
                             p = ((i >= qlo) & (i <= qhi)) ? p : 0.f;
@@ -326,7 +331,7 @@ __global__ void __launch_bounds__(kBwdThreads, (dkdv_waves<D, MODE, XT>())) bwd_
     __shared__ __attribute__((aligned(1024))) char ob1[P::TILE_BYTES];
     __shared__ __attribute__((aligned(1024))) char qb2[PIPE ? P::TILE_BYTES : 16];
     __shared__ __attribute__((aligned(1024))) char ob2[PIPE ? P::TILE_BYTES : 16];
-    __shared__ __attribute__((aligned(16))) float s_lse[2][BQ];   // LSE (natural log; scaled at use)
+    __shared__ __attribute__((aligned(16))) float s_lse[2][BQ];   // LSE * log2(e)
     __shared__ __attribute__((aligned(16))) float s_dl[2][BQ];    // rowsum(dO * O)
     __shared__ int s_g[kMaxGlobal];                               // sorted global positions
     __shared__ int s_hit[XT ? kBwdThreads : 1];                    // random-block list hits of one scan chunk
@@ -429,7 +434,7 @@ __global__ void __launch_bounds__(kBwdThreads, (dkdv_waves<D, MODE, XT>())) bwd_
             const int i = tile_of(t) * BQ + lane;
             const unsigned off = (unsigned)(rcls + i * dil) * 4u;   // row in the stored sequence
             const __amdgpu_buffer_rsrc_t lr =
-                __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(prm.lse + bh * prm.N), 0, prm.N * 4, 0x00020000);
+                __builtin_amdgcn_make_buffer_rsrc(prm.lse2 + bh * prm.N, 0, prm.N * 4, 0x00020000);
             const __amdgpu_buffer_rsrc_t dr =
                 __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(prm.delta + bh * prm.N), 0, prm.N * 4, 0x00020000);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(lr, (EEA_LDS void *)lse_dst, 4, off, 0, 0, 0);
@@ -453,7 +458,7 @@ __global__ void __launch_bounds__(kBwdThreads, (dkdv_waves<D, MODE, XT>())) bwd_
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int r = 4 * g + e;
-                    float p = fast_exp2(__builtin_fmaf(s[mb][r], c, -(l4[e] * kLog2e)));
+                    float p = fast_exp2(__builtin_fmaf(s[mb][r], c, -l4[e]));
                     if (cl == TILE_EDGE) p = vis(row(32 * mb + acc_row(r, h))) ? p : 0.f;
                     s[mb][r] = p;
                     dp[mb][r] = p * (dp[mb][r] - d4[e]);
@@ -611,7 +616,7 @@ __global__ void __launch_bounds__(kBwdThreads, (dkdv_waves<D, MODE, XT>())) bwd_
             P::issue_one(L, gh, ob0, src, s_g[0]);
             if (tid < BQ) {
                 const bool gv = tid < ng;
-                s_lse[0][tid] = gv ? prm.lse[bh * N + s_g[tid]] : 0.f;
+                s_lse[0][tid] = gv ? prm.lse2[bh * N + s_g[tid]] : 0.f;
                 s_dl[0][tid] = gv ? prm.delta[bh * N + s_g[tid]] : 0.f;
             }
             wait_vmem();
@@ -641,7 +646,7 @@ __global__ void __launch_bounds__(kBwdThreads, (dkdv_waves<D, MODE, XT>())) bwd_
                 P::issue_k(L, gh, N, ob0, q0);
                 if (tid < BQ) {
                     const int i = q0 + tid;
-                    s_lse[0][tid] = i < N ? prm.lse[bh * N + i] : 0.f;
+                    s_lse[0][tid] = i < N ? prm.lse2[bh * N + i] : 0.f;
                     s_dl[0][tid] = i < N ? prm.delta[bh * N + i] : 0.f;
                 }
                 wait_vmem();
@@ -924,7 +929,7 @@ __global__ void __launch_bounds__((dq_threads<D, MODE, XT>()), dq_waves<D>()) bw
     P::load_q(qf, qh, row * dil, valid, h);
     P::load_q(gf, gh, row * dil, valid, h);
     const long long grow = (long long)bh * prm.N + rcls + (long long)row * dil;   // row in the stored sequence
-    const float l2 = valid ? prm.lse[grow] * kLog2e : 0.f;
+    const float l2 = valid ? prm.lse2[grow] : 0.f;
     const float dl = valid ? prm.delta[grow] : 0.f;
     const float c = prm.scale_log2;
 

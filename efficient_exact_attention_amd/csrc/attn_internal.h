@@ -72,6 +72,7 @@ struct BwdParams {
     const float *lse;       // forward LSE, natural log, [B*H][N]
     void *dq, *dk, *dv;
     float *delta;           // workspace: rowsum(dO * O), [B*H][N]
+    float *lse2;            // workspace: LSE * log2(e) (the exponent offset of P), [B*H][N]
     long long head_stride;  // N * d elements
     int BH;                 // B * H
     int H, group;           // query heads per batch entry; per K/V head

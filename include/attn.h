@@ -257,8 +257,9 @@ int attn_bwd_masked(const void *q, const void *k, const void *v, const void *out
                     int B, int H, int H_kv, int N, int d, const attn_mask *mask, const attn_opts *opts);
 
 /*
- * attn_bwd_workspace_bytes - device scratch attn_bwd needs: one fp32 row term
- * per query row (B*H*N*4 bytes, rounded up to 256), plus, when n_global > 0,
+ * attn_bwd_workspace_bytes - device scratch attn_bwd needs: two fp32 row terms
+ * per query row (rowsum(dO * O) and the LSE in base 2; 2 * B*H*N*4 bytes, each
+ * half rounded up to 256), plus, when n_global > 0,
  * the split passes' fp32 partials (O(n_global * d * N / 64) per head, never
  * O(N^2)). 0 for invalid sizes.
  */

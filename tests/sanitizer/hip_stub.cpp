@@ -199,6 +199,7 @@ hipError_t launch_backward(const BwdParams &p, int d, hipStream_t) {
     if (!globals_ok(p.gidx, p.n_global, p.N)) return hipErrorInvalidValue;
     if (!rand_lists_ok(p.rand_idx, p.N, p.rand_block, p.n_rand)) return hipErrorInvalidValue;
     write_all(p.delta, (size_t)p.BH * p.N * sizeof(float));
+    write_all(p.lse2, (size_t)p.BH * p.N * sizeof(float));
     if (p.n_global > 0) {
         if ((long long)p.gchunks_q * p.gct_q * 64 < p.N || (long long)p.gchunks_k * p.gct_k * 64 < p.N)
             return hipErrorInvalidValue;

@@ -176,7 +176,7 @@ def test_bwd_globals_covered_by_window_are_accepted():
 
 
 def test_bwd_workspace_bytes():
-    assert ea.attn_bwd_workspace_bytes(2, 8, 1000, 128) == (2 * 8 * 1000 * 4 + 255) // 256 * 256
+    assert ea.attn_bwd_workspace_bytes(2, 8, 1000, 128) == 2 * ((2 * 8 * 1000 * 4 + 255) // 256 * 256)
     assert ea.attn_bwd_workspace_bytes(0, 8, 1000, 128) == 0
     assert ea.attn_bwd_workspace_bytes(1, 1, 16, 96) == 0
     # global tokens add the split passes' partials: O(n_global d N / 64) per head
