@@ -443,7 +443,10 @@ __global__ void __launch_bounds__(kBwdThreads, (dkdv_waves<D, MODE, XT>())) bwd_
     };
 
     // the four products of one staged query tile; row(r) gives the sequence
-    // row of tile slot r (or -1), vis(i) the extra test of an edge tile
+    // row of tile slot r (or -1), vis(i) the extra test of an edge tile. The
+    // edge mask is a pass of its own under a wave-uniform branch: folded
+    // into the element loop, the compiler had turned it into selects that
+    // every tile executed (about as many vector instructions as the rest).
     auto tile_products = [&](const char *qb, const char *ob, int sb, int cl, auto row, auto vis)
         __attribute__((always_inline)) {
         f32x16 s[MB], dp[MB];
@@ -454,15 +457,23 @@ __global__ void __launch_bounds__(kBwdThreads, (dkdv_waves<D, MODE, XT>())) bwd_
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const f32x4 l4 = *reinterpret_cast<const f32x4 *>(&s_lse[sb][32 * mb + 8 * g + 4 * h]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) s[mb][4 * g + e] = fast_exp2(__builtin_fmaf(s[mb][4 * g + e], c, -l4[e]));
+            }
+        if (cl == TILE_EDGE) {
+            asm volatile("");   // keeps this a branch (no speculation into selects)
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) s[mb][r] = vis(row(32 * mb + acc_row(r, h))) ? s[mb][r] : 0.f;
+        }
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
                 const f32x4 d4 = *reinterpret_cast<const f32x4 *>(&s_dl[sb][32 * mb + 8 * g + 4 * h]);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = 4 * g + e;
-                    float p = fast_exp2(__builtin_fmaf(s[mb][r], c, -l4[e]));
-                    if (cl == TILE_EDGE) p = vis(row(32 * mb + acc_row(r, h))) ? p : 0.f;
-                    s[mb][r] = p;
-                    dp[mb][r] = p * (dp[mb][r] - d4[e]);
-                }
+                for (int e = 0; e < 4; ++e) dp[mb][4 * g + e] = s[mb][4 * g + e] * (dp[mb][4 * g + e] - d4[e]);
             }
         typename P::PFrag pp, pd;
         P::pack_p(pp, s);
@@ -944,14 +955,22 @@ __global__ void __launch_bounds__((dq_threads<D, MODE, XT>()), dq_waves<D>()) bw
         f32x16 s[MB], dp[MB];
         P::scores(s, qf, L, kb);    // S^T  = K Q^T  : lane = query row, registers = keys
         P::scores(dp, gf, L, vb);   // dP^T = V dO^T
+        // (the edge mask a pass of its own under a uniform branch, as in bwd_dkdv)
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float p = fast_exp2(__builtin_fmaf(s[mb][r], c, -l2));
-                if (cl == TILE_EDGE) p = vis(col(mb * 32 + acc_row(r, h))) ? p : 0.f;
-                dp[mb][r] = p * (dp[mb][r] - dl);
-            }
+            for (int r = 0; r < 16; ++r) s[mb][r] = fast_exp2(__builtin_fmaf(s[mb][r], c, -l2));
+        if (cl == TILE_EDGE) {
+            asm volatile("");   // keeps this a branch (no speculation into selects)
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) s[mb][r] = vis(col(mb * 32 + acc_row(r, h))) ? s[mb][r] : 0.f;
+        }
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) dp[mb][r] = s[mb][r] * (dp[mb][r] - dl);
         typename P::PFrag pd;
         P::pack_p(pd, dp);
         P::pv(dq, pd, L, kb);       // dQ^T += K^T dS^T
