@@ -91,12 +91,13 @@ enum { BWD_BAND = 0, BWD_BAND_GL = 1, BWD_GSET = 2 };
 // registers run two per SIMD (two workgroups per CU), so one workgroup's
 // copies and barriers overlap the other's products: every dQ instance, and
 // the dK/dV band loop (in its unpipelined form: the pipelined one needs more
-// registers) and split pass. Measured on d = 64: 36-40 % less time for a
-// causal or banded backward than at one wave per SIMD with the pipelined
-// loops. d = 128 and the dK/dV instances with gathered global rows or extra
-// tiles keep one wave per SIMD.
+// registers), with or without the gathered tile of global rows, and split
+// pass. Measured on d = 64: 36-40 % less time for a causal or banded
+// backward than at one wave per SIMD with the pipelined loops, 20 % less for
+// band 256 + 9 global tokens. d = 128 and the dK/dV extra-tile instances keep
+// one wave per SIMD.
 template <int D, int MODE, bool XT>
-constexpr int dkdv_waves() { return (D == 64 && MODE != BWD_BAND_GL && !XT) ? 2 : 1; }
+constexpr int dkdv_waves() { return (D == 64 && !XT) ? 2 : 1; }
 template <int D>
 constexpr int dq_waves() { return D == 64 ? 2 : 1; }
 // Threads of a dQ instance. At d = 128 the band instance (no global tokens,
